@@ -1,0 +1,36 @@
+"""CPU oracle for DuoAttention's mixed retrieval/streaming attention.
+
+TEST INFRASTRUCTURE ONLY.  This package is the slow, plainly written fp64
+definition that the GPU library is checked against.  Only the test suite,
+the smoke check and the benchmark's CPU-baseline leg may import it; the
+library itself (``kv_cache_duo_amd``) never does, and this package imports
+nothing from the library.  The two share no code.
+
+Sources (the DuoAttention paper, arXiv 2410.10819, as described on the web
+pages this project was built from):
+
+* Abstract, as reproduced on the pith.science review page ("read the original
+  abstract"): retrieval heads attend to every token; streaming heads attend
+  to recent tokens and attention sinks and keep a constant-length cache.
+* sourcepulse.org project card, "How It Works": full KV cache only for
+  retrieval heads, a lightweight constant-length cache for streaming heads.
+* pith.science referee report, minor comment 3: the pages give no equation
+  for the cache size or for sink handling, so those steps follow the readings
+  listed in ``mixed_attention`` and ``cache_state``.
+
+Every function here is pinned by ``tests/test_oracle.py`` against closed
+forms, a library routine (torch fp64 scaled-dot-product attention), brute
+force on tiny inputs and hand-derived fixtures under ``tests/golden/``.
+"""
+
+from .mixed_attention import (  # noqa: F401
+    allowed_positions,
+    attention_weights_row,
+    attend_rows,
+    mixed_attention,
+)
+from .cache_state import (  # noqa: F401
+    CacheSimulator,
+    streaming_slot_of_position,
+    streaming_slot_positions,
+)
