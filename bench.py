@@ -1,0 +1,257 @@
+"""Benchmark of the DuoAttention hot path on one MI355X.
+
+One step = the whole path over one batch of synthetic input, for each of
+`--layers` independently seeded layer caches (a model's layer loop; it also
+keeps the decode working set far above the 256 MB Infinity Cache, so decode
+bandwidth is HBM bandwidth):
+  cache init -> one-shot prefill of the context -> `decode_steps` decode
+  steps (each step visits every layer).
+Inputs are resident in HBM before the timed region.  Reported:
+  value      decode attention, algorithmic HBM bytes / decode-phase wall time
+  prefill    algorithmic flops / prefill-phase wall time
+  roofline   decode kernel: algorithmic bytes per launch / mean launch time
+             (HIP events on the launch stream), against 8 TB/s
+  cpu_baseline  the fp64 oracle on a bounded sample of the same decode work
+Algorithmic counts: each K/V byte once per (sequence, KV head) plus q, out
+and the appended token; flops = 4*D per allowed (query, key) pair per query
+head.  Prints one JSON line.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=1)
+    p.add_argument("--workload", default="llama2_7b_mha_32k")
+    p.add_argument("--layers", type=int, default=8)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-steps", type=int, default=4)
+    return p.parse_args()
+
+
+def allowed_count(t: int, retrieval: bool, sink: int, recent: int) -> int:
+    """Number of positions a query at t attends to (for the flop count)."""
+    return t + 1 if retrieval else min(t + 1, sink + recent)
+
+
+def prefill_flops(w, mask) -> float:
+    g = w.group
+    nr = int(sum(mask))
+    ns = w.num_kv_heads - nr
+    n = w.prefill
+    retr = n * (n + 1) // 2
+    cap = w.sink + w.recent
+    stream = (min(n, cap) * (min(n, cap) + 1)) // 2 + max(n - cap, 0) * cap
+    return 4.0 * w.head_dim * w.batch * g * (nr * retr + ns * stream)
+
+
+def decode_bytes(w, mask, ctx: int) -> float:
+    """Algorithmic bytes of one decode call when each sequence holds ctx tokens."""
+    nr = int(sum(mask))
+    ns = w.num_kv_heads - nr
+    row = 2 * w.head_dim  # bf16 row
+    kv = 2 * row * w.batch * (nr * (ctx + 1) + ns * min(ctx + 1, w.sink + w.recent))
+    qo = 2 * row * w.batch * w.num_q_heads
+    append = 2 * row * w.batch * w.num_kv_heads
+    return float(kv + qo + append)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import kv_cache_duo_amd as duo
+    from workloads import WORKLOADS, qkv, workload_mask
+
+    w = WORKLOADS[args.workload]
+    if w.length_range is not None or w.layers > 1:
+        print(f"workload {w.name} is a parity case, not a bench line", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    lib = duo.load_library()
+    nl = args.layers
+    t_all = w.prefill + w.decode_steps
+    masks = [workload_mask(w, layer) for layer in range(nl)]
+    cfgs = [duo.Config(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, t_all, w.sink, w.recent,
+                       [int(x) for x in m]) for m in masks]
+    bufs = [torch.empty(duo.required_bytes(c), dtype=torch.uint8, device=dev) for c in cfgs]
+    ins = [qkv(w.batch, t_all, w.num_q_heads, w.num_kv_heads, w.head_dim, w.seed * 100 + layer, dev)
+           for layer in range(nl)]
+    outp = torch.empty(w.batch, w.prefill, w.num_q_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    outd = torch.empty(w.batch, w.num_q_heads, w.head_dim, dtype=torch.bfloat16, device=dev)
+    # decode inputs per (layer, step), contiguous [B,H,D]
+    dq = [[ins[l][0][:, w.prefill + s].contiguous() for s in range(w.decode_steps)] for l in range(nl)]
+    dk = [[ins[l][1][:, w.prefill + s].contiguous() for s in range(w.decode_steps)] for l in range(nl)]
+    dv = [[ins[l][2][:, w.prefill + s].contiguous() for s in range(w.decode_steps)] for l in range(nl)]
+    pq = [ins[l][0][:, :w.prefill].contiguous() for l in range(nl)]
+    pk = [ins[l][1][:, :w.prefill].contiguous() for l in range(nl)]
+    pv = [ins[l][2][:, :w.prefill].contiguous() for l in range(nl)]
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    n_new = (ctypes.c_int32 * w.batch)(*([w.prefill] * w.batch))
+    ptr = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    dq_p = [[ptr(x) for x in row] for row in dq]
+    dk_p = [[ptr(x) for x in row] for row in dk]
+    dv_p = [[ptr(x) for x in row] for row in dv]
+    od_p = ptr(outd)
+    op_p = ptr(outp)
+    n_dec = w.decode_steps * nl
+    ev_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dec)]
+    ev_p = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nl)]
+    ph = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+    def check(st, where):
+        if st != 0:
+            raise RuntimeError(f"{where}: {duo.status_string(st)}")
+
+    def one_step():
+        caches = [duo.duo_cache_init(cfgs[l], bufs[l]) for l in range(nl)]
+        hs = [c.handle for c in caches]
+        ph[0].record(stream)
+        for l in range(nl):
+            ev_p[l][0].record(stream)
+            check(lib.duo_prefill(hs[l], ptr(pq[l]), ptr(pk[l]), ptr(pv[l]), n_new, w.prefill, op_p, sp),
+                  "prefill")
+            ev_p[l][1].record(stream)
+        ph[1].record(stream)
+        i = 0
+        for s in range(w.decode_steps):
+            for l in range(nl):
+                ev_d[i][0].record(stream)
+                check(lib.duo_decode(hs[l], dq_p[l][s], dk_p[l][s], dv_p[l][s], od_p, sp), "decode")
+                ev_d[i][1].record(stream)
+                i += 1
+        ph[2].record(stream)
+        return caches
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    pre_ms = dec_ms = 0.0
+    dec_launch_ms = []
+    pre_launch_ms = []
+    t0.record(stream)
+    wall0 = time.perf_counter()
+    for _ in range(args.steps):
+        caches = one_step()
+        torch.cuda.synchronize()
+        pre_ms += ph[0].elapsed_time(ph[1])
+        dec_ms += ph[1].elapsed_time(ph[2])
+        dec_launch_ms += [a.elapsed_time(b) for a, b in ev_d]
+        pre_launch_ms += [a.elapsed_time(b) for a, b in ev_p]
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / args.steps
+    del caches
+
+    # algorithmic work
+    flops_step = sum(prefill_flops(w, m) for m in masks)
+    bytes_step = sum(decode_bytes(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
+    dec_gbs = bytes_step * args.steps / (dec_ms * 1e-3) / 1e9
+    pre_tflops = flops_step * args.steps / (pre_ms * 1e-3) / 1e12
+    mean_dec_launch = sum(dec_launch_ms) / len(dec_launch_ms)
+    bytes_per_launch = bytes_step / n_dec
+    achieved = bytes_per_launch / (mean_dec_launch * 1e-3) / 1e9
+    mean_pre_launch = sum(pre_launch_ms) / len(pre_launch_ms)
+    pre_achieved = (flops_step / nl) / (mean_pre_launch * 1e-3) / 1e12
+
+    result = {
+        "metric": "decode attn HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak), 1 MI355X",
+        "value": round(dec_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+            "head_dim": w.head_dim, "retrieval_kv_heads": w.n_retrieval, "prefill_tokens": w.prefill,
+            "decode_steps": w.decode_steps, "sink": w.sink, "recent": w.recent, "layers_rotated": nl,
+        },
+        "decode": {"gbs": round(dec_gbs, 1), "frac_of_hbm_peak": round(dec_gbs / HBM_PEAK_GBS, 4),
+                   "phase_ms_per_step": round(dec_ms / args.steps, 3),
+                   "calls_per_step": n_dec},
+        "prefill": {"tflops": round(pre_tflops, 1),
+                    "frac_of_mfma_peak": round(pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                    "phase_ms_per_step": round(pre_ms / args.steps, 3),
+                    "flops_per_step": flops_step},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel", "mean_launch_us": round(mean_dec_launch * 1e3, 3),
+                     "bytes_per_launch": bytes_per_launch},
+        "roofline_prefill": {"bound": "mfma", "achieved": round(pre_achieved, 1),
+                             "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(pre_achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                             "kernel": "prefill_kernel (+append)",
+                             "mean_launch_ms": round(mean_pre_launch, 4)},
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, masks[0], ins[0], args.cpu_sample_steps)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(w, mask, qkv_l0, sample_steps):
+    """Oracle timed on a bounded sample: the first `sample_steps` decode steps
+    of layer 0 (every query head), in the decode metric's unit."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import attend_rows
+    q, k, v = (x.float().cpu().numpy() for x in qkv_l0)
+    g = w.group
+    scale = 1.0 / math.sqrt(w.head_dim)
+    b = 0
+    # fp64 copies per KV head, outside the timed region
+    ks = [np.ascontiguousarray(k[b, :, h, :], dtype=np.float64) for h in range(w.num_kv_heads)]
+    vs = [np.ascontiguousarray(v[b, :, h, :], dtype=np.float64) for h in range(w.num_kv_heads)]
+    t0 = time.perf_counter()
+    done_bytes = 0.0
+    steps = 0
+    for s in range(sample_steps):
+        t = w.prefill + s
+        for h in range(w.num_q_heads):
+            kvh = h // g
+            attend_rows(q[b, [t], h, :], [t], ks[kvh], vs[kvh], bool(mask[kvh]), w.sink, w.recent, scale)
+        done_bytes += decode_bytes(w, mask, t) / w.batch
+        steps += 1
+        if time.perf_counter() - t0 > 30.0:
+            break
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{steps} decode steps of layer 0, sequence 0, all {w.num_q_heads} query heads, "
+                      f"context {w.prefill}+ ({dt:.2f} s)",
+            "seconds": round(dt, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,162 @@
+/*
+ * duo.h -- C ABI of a gfx950 (AMD MI355X) library for DuoAttention's
+ * per-head mixed attention over a head-split KV cache.
+ *
+ * The method (DuoAttention, arXiv 2410.10819; abstract as reproduced on the
+ * pith.science review page, and the sourcepulse.org project card, "How It
+ * Works"): attention heads are of two kinds.  Retrieval heads keep the full
+ * KV cache and attend to every earlier token.  Streaming heads keep a
+ * constant-length cache and attend only to the attention sinks and the most
+ * recent tokens.  Both prefill (many new tokens at once) and decoding (one
+ * new token per sequence) use the split.  Which heads are retrieval heads is
+ * decided offline (the pages' optimisation on synthetic data) and is an
+ * INPUT here: one flag per KV head.
+ *
+ * Readings of points the pages leave open (the pith.science referee report,
+ * minor comment 3, notes that the cache size and sink handling have no
+ * equation):
+ *   - sinks are the first `sink` positions of each sequence;
+ *   - a streaming query at position t sees positions t-recent+1 .. t (the
+ *     window includes the query) and the sinks, i.e. min(t+1, sink+recent)
+ *     positions -- exactly what sink+recent cache slots hold after the new
+ *     token is stored;
+ *   - query head h uses KV head h / (num_q_heads / num_kv_heads) (grouped
+ *     query attention) and inherits that KV head's kind;
+ *   - no positional encoding is applied here: q and k arrive positioned;
+ *   - retrieval heads never evict: running out of `max_len` is an error.
+ *
+ * Conventions for every call:
+ *   - Tensors are bf16 (IEEE binary16 "brain" format, 2 bytes), dense,
+ *     row-major, in DEVICE memory, 16-byte aligned.  The caller owns every
+ *     buffer; the library never allocates or frees device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls only enqueue work on it and never synchronise; DUO_OK means the
+ *     work was enqueued.  Results are visible after the caller synchronises.
+ *   - All arguments are validated before anything is enqueued; a call that
+ *     returns an error leaves the device buffer and the handle unchanged.
+ *   - A handle is not thread-safe; use one stream per handle, calls in order.
+ *   - No exception crosses the ABI and nothing aborts.
+ */
+#ifndef DUO_H
+#define DUO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUO_MAX_BATCH 128
+
+typedef enum duo_status {
+  DUO_OK = 0,
+  DUO_ERR_INVALID_ARG = 1,      /* null/misaligned pointer, bad size or shape */
+  DUO_ERR_UNSUPPORTED = 2,      /* head_dim not 64 or 128, batch > DUO_MAX_BATCH */
+  DUO_ERR_BUFFER_TOO_SMALL = 3, /* buf_bytes < required bytes */
+  DUO_ERR_CAPACITY = 4,         /* a sequence would exceed max_len tokens */
+  DUO_ERR_HIP = 5               /* a HIP launch failed (hipGetLastError) */
+} duo_status;
+
+/* Configuration of one attention layer's cache. */
+typedef struct duo_config {
+  int32_t batch;        /* B, 1..DUO_MAX_BATCH sequences */
+  int32_t num_q_heads;  /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads; /* Hkv >= 1 */
+  int32_t head_dim;     /* D: 64 or 128 */
+  int64_t max_len;      /* token capacity per sequence of the retrieval cache */
+  int32_t sink;         /* S >= 0 attention-sink positions kept by streaming heads */
+  int32_t recent;       /* W >= 1 recent positions kept by streaming heads */
+  float scale;          /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  const uint8_t* kv_head_is_retrieval; /* HOST [Hkv]: nonzero = retrieval; copied */
+} duo_config;
+
+/* Opaque host-side handle: configuration, head maps, region offsets and the
+ * host mirror of every sequence's length. */
+typedef struct duo_cache duo_cache;
+
+/* Byte offsets of the regions inside the caller's device buffer (all 256-byte
+ * aligned).  nR / nS = number of retrieval / streaming KV heads; retrieval
+ * KV head k is stored at index head_index[k] among the retrieval heads
+ * (in increasing k), likewise for streaming heads.
+ *   lengths  int32 [B]                     tokens stored per sequence
+ *   rk, rv   bf16  [B][nR][max_len][D]     retrieval cache, row = position
+ *   sk, sv   bf16  [B][nS][sink+recent][D] streaming cache, slot map:
+ *            slot(p) = p for p < sink, else sink + (p - sink) mod recent
+ *   work     fp32 split-K partials and uint32 merge tickets (library-private) */
+typedef struct duo_layout {
+  int64_t lengths_offset;
+  int64_t rk_offset, rv_offset;
+  int64_t sk_offset, sv_offset;
+  int64_t work_offset, work_bytes;
+  int64_t total_bytes;
+  int32_t n_retrieval, n_streaming;
+  int32_t slots_per_streaming_head; /* sink + recent */
+  int32_t reserved;
+} duo_layout;
+
+/* Lay out a new, empty cache in `dev_buf`.
+ * dev_buf == NULL: only writes *required_bytes (no device work); *out untouched.
+ * Otherwise dev_buf (256-byte aligned, buf_bytes long, caller-owned, must
+ * outlive the handle) receives the layout above; the lengths and the merge
+ * tickets are zeroed on `stream` by a fill kernel; *out gets a new handle.
+ * Errors: INVALID_ARG (null cfg / mask / out, B < 1, Hkv < 1, Hq % Hkv != 0,
+ * sink < 0, recent < 1, max_len < 1, misaligned dev_buf, scale < 0 or not
+ * finite), UNSUPPORTED (head_dim, batch), BUFFER_TOO_SMALL, HIP. */
+duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
+                          size_t* required_bytes, duo_cache** out, void* stream);
+
+/* Wrap a buffer that already holds a cache laid out for `cfg` (for example a
+ * copy of another handle's buffer: checkpoint / resume), with the host
+ * lengths `lengths[B]` (each 0..max_len).  Enqueues nothing.  Same errors as
+ * duo_cache_init, plus INVALID_ARG for null or out-of-range lengths. */
+duo_status duo_cache_attach(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
+                            const int64_t* lengths, duo_cache** out);
+
+/* Free the host handle only (the device buffer stays the caller's). */
+void duo_cache_destroy(duo_cache* h);
+
+/* Append n_new[b] tokens to every sequence without attending.
+ * k, v: bf16 [B][chunk][Hkv][D]; rows i >= n_new[b] of sequence b are
+ * ignored.  Token i of sequence b gets position len_b + i.  Retrieval heads
+ * store it at row len_b + i; streaming heads store positions < sink in their
+ * sink slot and the last `recent` non-sink positions in their ring slot
+ * (older ones would be overwritten at once).  Lengths advance by n_new.
+ * n_new: HOST int32 [B], each in [0, chunk].
+ * Errors: INVALID_ARG (null handle/k/v/n_new, misaligned, chunk < 1,
+ * n_new out of range), CAPACITY (len_b + n_new[b] > max_len), HIP. */
+duo_status duo_cache_append(duo_cache* h, const void* k, const void* v,
+                            const int32_t* n_new, int32_t chunk, void* stream);
+
+/* Pre-filling: for every new token i < n_new[b] of sequence b at position
+ * p = len_b + i and every query head, out = softmax(scale * q k^T) v over
+ * the positions that head may see (retrieval: 0..p; streaming: sinks and
+ * p-recent+1..p), where earlier positions come from the cache and the rest
+ * from this chunk; then the chunk is appended as by duo_cache_append.  A
+ * sequence may be prefilled in several chunks; the result equals one call
+ * with the whole sequence.  n_new[b] = 0 skips sequence b.
+ * q, out: bf16 [B][chunk][Hq][D]; k, v: bf16 [B][chunk][Hkv][D]; output
+ * rows i >= n_new[b] are left untouched.  n_new: HOST int32 [B].
+ * Errors: as duo_cache_append, plus null/misaligned q or out. */
+duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v,
+                       const int32_t* n_new, int32_t chunk, void* out, void* stream);
+
+/* Decoding: append one token per sequence at p = len_b and attend from it
+ * (itself included), exactly as duo_prefill with n_new[b] = 1 for all b.
+ * q, out: bf16 [B][Hq][D]; k, v: bf16 [B][Hkv][D].
+ * Errors: INVALID_ARG (null/misaligned pointers), CAPACITY, HIP. */
+duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v,
+                      void* out, void* stream);
+
+/* Introspection (host only, no device work). */
+const char* duo_status_string(duo_status s);
+duo_status duo_cache_lengths(const duo_cache* h, int64_t* out /* [B] */);
+duo_status duo_cache_layout(const duo_cache* h, duo_layout* out);
+/* out[k] = index of KV head k among the heads of its own kind. */
+duo_status duo_cache_head_index(const duo_cache* h, int32_t* out /* [Hkv] */);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DUO_H */

@@ -1,0 +1,282 @@
+"""Python binding of libduo.so: DuoAttention mixed retrieval/streaming
+attention over a head-split KV cache on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step of prefill, decode and append runs in
+the HIP kernels behind the C ABI of ``include/duo.h``; torch provides device
+memory and the current stream.  There is no CPU fallback: if the library is
+not built, importing the functions that need it raises.
+
+    cfg = Config(batch=1, num_q_heads=32, num_kv_heads=32, head_dim=128,
+                 max_len=33024, sink=64, recent=256,
+                 kv_head_is_retrieval=mask)
+    buf = torch.empty(required_bytes(cfg), dtype=torch.uint8, device="cuda")
+    cache = duo_cache_init(cfg, buf)
+    duo_prefill(cache, q, k, v, n_new, out)   # q/out [B,C,Hq,D], k/v [B,C,Hkv,D]
+    duo_decode(cache, q1, k1, v1, out1)       # q1/out1 [B,Hq,D], k1/v1 [B,Hkv,D]
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+from typing import Sequence
+
+import torch  # noqa: F401  -- load torch's HIP runtime before libduo.so binds to it
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libduo.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "duo.h")
+
+DUO_OK = 0
+DUO_ERR_INVALID_ARG = 1
+DUO_ERR_UNSUPPORTED = 2
+DUO_ERR_BUFFER_TOO_SMALL = 3
+DUO_ERR_CAPACITY = 4
+DUO_ERR_HIP = 5
+DUO_MAX_BATCH = 128
+
+
+class DuoError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("max_len", ctypes.c_int64), ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
+        ("scale", ctypes.c_float), ("kv_head_is_retrieval", ctypes.POINTER(ctypes.c_uint8)),
+    ]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [
+        ("lengths_offset", ctypes.c_int64), ("rk_offset", ctypes.c_int64),
+        ("rv_offset", ctypes.c_int64), ("sk_offset", ctypes.c_int64),
+        ("sv_offset", ctypes.c_int64), ("work_offset", ctypes.c_int64),
+        ("work_bytes", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
+        ("n_retrieval", ctypes.c_int32), ("n_streaming", ctypes.c_int32),
+        ("slots_per_streaming_head", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32P = ctypes.POINTER(ctypes.c_int32)
+_I64P = ctypes.POINTER(ctypes.c_int64)
+
+_SIGNATURES = {
+    "duo_cache_init": (ctypes.c_int, [ctypes.POINTER(_Config), _P, ctypes.c_size_t,
+                                      ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(_P), _P]),
+    "duo_cache_attach": (ctypes.c_int, [ctypes.POINTER(_Config), _P, ctypes.c_size_t, _I64P,
+                                        ctypes.POINTER(_P)]),
+    "duo_cache_destroy": (None, [_P]),
+    "duo_cache_append": (ctypes.c_int, [_P, _P, _P, _I32P, ctypes.c_int32, _P]),
+    "duo_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I32P, ctypes.c_int32, _P, _P]),
+    "duo_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "duo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "duo_cache_lengths": (ctypes.c_int, [_P, _I64P]),
+    "duo_cache_layout": (ctypes.c_int, [_P, ctypes.POINTER(Layout)]),
+    "duo_cache_head_index": (ctypes.c_int, [_P, _I32P]),
+}
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libduo.so (built by ``kv_cache_duo_amd.build``); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m kv_cache_duo_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/duo.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(duo_[a-z_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return load_library().duo_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != DUO_OK:
+        raise DuoError(status, where)
+
+
+@dataclass
+class Config:
+    batch: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    max_len: int
+    sink: int
+    recent: int
+    kv_head_is_retrieval: Sequence[int]
+    scale: float = 0.0
+
+    def _c(self):
+        mask = (ctypes.c_uint8 * max(len(self.kv_head_is_retrieval), 1))(
+            *[1 if x else 0 for x in self.kv_head_is_retrieval])
+        c = _Config(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim, self.max_len,
+                    self.sink, self.recent, self.scale,
+                    ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)))
+        return c, mask  # keep the mask alive for the call
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(getattr(stream, "cuda_stream", stream) or 0)
+
+
+def _dev(t: torch.Tensor, shape, name: str) -> int:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous bfloat16 tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def required_bytes(cfg: Config) -> int:
+    c, _m = cfg._c()
+    req = ctypes.c_size_t(0)
+    _check(load_library().duo_cache_init(ctypes.byref(c), None, 0, ctypes.byref(req), None, None),
+           "duo_cache_init")
+    return int(req.value)
+
+
+class Cache:
+    """Host handle of one cache laid out in a caller-owned device buffer."""
+
+    def __init__(self, cfg: Config, handle: int, buf):
+        self.cfg = cfg
+        self._h = ctypes.c_void_p(handle)
+        self.buf = buf  # keeps the device buffer alive as long as the handle
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.duo_cache_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def lengths(self) -> list[int]:
+        out = (ctypes.c_int64 * self.cfg.batch)()
+        _check(load_library().duo_cache_lengths(self._h, out), "duo_cache_lengths")
+        return list(out)
+
+    def layout(self) -> Layout:
+        lay = Layout()
+        _check(load_library().duo_cache_layout(self._h, ctypes.byref(lay)), "duo_cache_layout")
+        return lay
+
+    def head_index(self) -> list[int]:
+        out = (ctypes.c_int32 * self.cfg.num_kv_heads)()
+        _check(load_library().duo_cache_head_index(self._h, out), "duo_cache_head_index")
+        return list(out)
+
+
+def duo_cache_init(cfg: Config, buf: torch.Tensor, stream=None) -> Cache:
+    if buf.device.type != "cuda" or buf.dtype != torch.uint8 or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous uint8 CUDA (HIP) tensor")
+    c, _m = cfg._c()
+    req = ctypes.c_size_t(0)
+    h = ctypes.c_void_p()
+    _check(load_library().duo_cache_init(ctypes.byref(c), ctypes.c_void_p(buf.data_ptr()), buf.numel(),
+                                         ctypes.byref(req), ctypes.byref(h), ctypes.c_void_p(_stream(stream))),
+           "duo_cache_init")
+    return Cache(cfg, h.value, buf)
+
+
+def duo_cache_attach(cfg: Config, buf_ptr: int, buf_bytes: int, lengths: Sequence[int], keep=None) -> Cache:
+    """Wrap an existing cache buffer (device address ``buf_ptr``); no device work."""
+    c, _m = cfg._c()
+    lens = (ctypes.c_int64 * max(cfg.batch, 1))(*[int(x) for x in lengths])
+    h = ctypes.c_void_p()
+    _check(load_library().duo_cache_attach(ctypes.byref(c), ctypes.c_void_p(buf_ptr), buf_bytes, lens,
+                                           ctypes.byref(h)), "duo_cache_attach")
+    return Cache(cfg, h.value, keep)
+
+
+def _n_array(n_new, batch):
+    arr = (ctypes.c_int32 * batch)(*[int(x) for x in n_new])
+    if len(n_new) != batch:
+        raise ValueError(f"n_new has {len(n_new)} entries, expected {batch}")
+    return arr
+
+
+def duo_cache_append(cache: Cache, k, v, n_new, stream=None) -> None:
+    cfg = cache.cfg
+    chunk = k.shape[1]
+    shape = (cfg.batch, chunk, cfg.num_kv_heads, cfg.head_dim)
+    pk, pv = _dev(k, shape, "k"), _dev(v, shape, "v")
+    _check(load_library().duo_cache_append(cache.handle, pk, pv, _n_array(n_new, cfg.batch), chunk,
+                                           _stream(stream)), "duo_cache_append")
+
+
+def duo_prefill(cache: Cache, q, k, v, n_new, out, stream=None) -> None:
+    cfg = cache.cfg
+    chunk = q.shape[1]
+    pq = _dev(q, (cfg.batch, chunk, cfg.num_q_heads, cfg.head_dim), "q")
+    po = _dev(out, (cfg.batch, chunk, cfg.num_q_heads, cfg.head_dim), "out")
+    kv_shape = (cfg.batch, chunk, cfg.num_kv_heads, cfg.head_dim)
+    pk, pv = _dev(k, kv_shape, "k"), _dev(v, kv_shape, "v")
+    _check(load_library().duo_prefill(cache.handle, pq, pk, pv, _n_array(n_new, cfg.batch), chunk, po,
+                                      _stream(stream)), "duo_prefill")
+
+
+def duo_decode(cache: Cache, q, k, v, out, stream=None) -> None:
+    cfg = cache.cfg
+    pq = _dev(q, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
+    po = _dev(out, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "out")
+    kv_shape = (cfg.batch, cfg.num_kv_heads, cfg.head_dim)
+    pk, pv = _dev(k, kv_shape, "k"), _dev(v, kv_shape, "v")
+    _check(load_library().duo_decode(cache.handle, pq, pk, pv, po, _stream(stream)), "duo_decode")
+
+
+def cache_views(cache: Cache):
+    """Typed views of the regions of a cache's device buffer (for tests and
+    checkpointing): lengths int32 [B], rk/rv [B,nR,max_len,D], sk/sv
+    [B,nS,sink+recent,D] as bf16."""
+    cfg, lay, buf = cache.cfg, cache.layout(), cache.buf
+    if buf is None:
+        raise ValueError("cache has no torch buffer attached")
+    d = cfg.head_dim
+
+    def region(off, shape, dtype):
+        nbytes = 1
+        for s in shape:
+            nbytes *= s
+        nbytes *= torch.tensor([], dtype=dtype).element_size()
+        return buf[off:off + nbytes].view(dtype).view(*shape)
+
+    return {
+        "lengths": region(lay.lengths_offset, (cfg.batch,), torch.int32),
+        "rk": region(lay.rk_offset, (cfg.batch, lay.n_retrieval, cfg.max_len, d), torch.bfloat16),
+        "rv": region(lay.rv_offset, (cfg.batch, lay.n_retrieval, cfg.max_len, d), torch.bfloat16),
+        "sk": region(lay.sk_offset, (cfg.batch, lay.n_streaming, lay.slots_per_streaming_head, d),
+                     torch.bfloat16),
+        "sv": region(lay.sv_offset, (cfg.batch, lay.n_streaming, lay.slots_per_streaming_head, d),
+                     torch.bfloat16),
+    }

@@ -1,0 +1,113 @@
+// Cache append / evict kernel.
+//
+// DuoAttention (abstract; sourcepulse card, "How It Works"): retrieval heads
+// keep every token, streaming heads keep a constant-length cache of the
+// attention sinks and the recent tokens.  Storing a token therefore means:
+//   retrieval KV head: row `position` of its contiguous cache;
+//   streaming KV head: slot(p) = p for p < sink, else sink + (p-sink) mod
+//   recent -- which overwrites (evicts) the token `recent` positions older.
+// Within one call only the last `recent` non-sink positions of a chunk are
+// written to the ring: older ones would be overwritten by the same call.
+#include "device_util.h"
+#include "duo_internal.h"
+
+namespace duo {
+namespace {
+
+constexpr int kAppendThreads = 256;
+constexpr int kRowsPerBlock = 64;
+
+__global__ __launch_bounds__(kAppendThreads) void zero_words_kernel(uint32_t* p, int64_t words) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (; i < words; i += stride) p[i] = 0u;
+}
+
+// One block copies up to 64 token rows of one (sequence, KV head).
+// Blocks [0, B*nR*xr) handle retrieval heads, the rest streaming heads.
+template <int D>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, const uint16_t* __restrict__ k,
+                                                                const uint16_t* __restrict__ v, int32_t chunk,
+                                                                int32_t xr, int32_t xs) {
+  constexpr int CH = D / 8;                  // 16-byte chunks per row
+  constexpr int ROWS_PER_PASS = kAppendThreads / CH;
+  int id = blockIdx.x;
+  const int retrieval_blocks = g.B * g.nR * xr;
+  bool retrieval = id < retrieval_blocks;
+  int b, idx, x;
+  if (retrieval) {
+    x = id % xr;
+    idx = (id / xr) % g.nR;
+    b = id / (xr * g.nR);
+  } else {
+    id -= retrieval_blocks;
+    x = id % xs;
+    idx = (id / xs) % g.nS;
+    b = id / (xs * g.nS);
+  }
+  const int len = q.len[b];
+  const int n = q.n[b];
+  const int kvh = g.kv_of_unit[retrieval ? idx : g.nR + idx];
+
+  // Lengths: written once per sequence, by the first block of its first head.
+  if (x == 0 && idx == 0 && threadIdx.x == 0 && (retrieval || g.nR == 0)) g.lengths[b] = len + n;
+
+  // Rows of this call that the head stores.
+  int count, first_ring, sinks_here = 0;
+  if (retrieval) {
+    count = n;
+    first_ring = 0;
+  } else {
+    sinks_here = min(max(g.S - len, 0), n);          // chunk rows that are sinks
+    first_ring = max(sinks_here, n - g.W);           // first row kept in the ring
+    count = sinks_here + (n - first_ring);
+  }
+  const int c = threadIdx.x % CH;
+  for (int j = x * kRowsPerBlock + threadIdx.x / CH; j < min(count, (x + 1) * kRowsPerBlock);
+       j += ROWS_PER_PASS) {
+    int i = retrieval ? j : (j < sinks_here ? j : first_ring + (j - sinks_here));
+    int64_t p = (int64_t)len + i;
+    uint16_t *dk, *dv;
+    if (retrieval) {
+      int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + p;
+      dk = g.rk + row * D;
+      dv = g.rv + row * D;
+    } else {
+      int64_t slot = p < g.S ? p : g.S + (p - g.S) % g.W;
+      int64_t row = ((int64_t)b * g.nS + idx) * g.slots + slot;
+      dk = g.sk + row * D;
+      dv = g.sv + row * D;
+    }
+    int64_t src = (((int64_t)b * chunk + i) * g.Hkv + kvh) * D;
+    reinterpret_cast<uint4*>(dk)[c] = reinterpret_cast<const uint4*>(k + src)[c];
+    reinterpret_cast<uint4*>(dv)[c] = reinterpret_cast<const uint4*>(v + src)[c];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s) {
+  if (words <= 0) return hipSuccess;
+  int64_t blocks = (words + kAppendThreads - 1) / kAppendThreads;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, p, words);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v, int32_t chunk,
+                         int32_t max_n, hipStream_t s) {
+  int32_t xr = (max_n + kRowsPerBlock - 1) / kRowsPerBlock;
+  int32_t xs = (min(max_n, g.slots) + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (xr < 1) xr = 1;  // still one block per head so that the lengths are written
+  if (xs < 1) xs = 1;
+  int64_t blocks = (int64_t)g.B * g.nR * xr + (int64_t)g.B * g.nS * xs;
+  if (g.D == 128)
+    hipLaunchKernelGGL(append_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, chunk,
+                       xr, xs);
+  else
+    hipLaunchKernelGGL(append_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, chunk,
+                       xr, xs);
+  return hipGetLastError();
+}
+
+}  // namespace duo

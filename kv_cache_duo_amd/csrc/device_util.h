@@ -1,0 +1,54 @@
+// Small device helpers for the gfx950 kernels: bf16 bit handling, wave64
+// lane reductions, base-2 exponent.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace duo {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// bf16 pair packed in a 32-bit word -> the two fp32 values (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Two bf16 products accumulated in fp32 (v_dot2_f32_bf16).
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane moves inside a 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over aligned groups of LANES (2, 4, 8 or 16) lanes; every lane of the
+// group receives the group sum.
+template <int LANES>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(LANES == 2 || LANES == 4 || LANES == 8 || LANES == 16, "group size");
+  x += dpp_mov<0xB1>(x);                              // quad_perm [1,0,3,2]: lane ^ 1
+  if (LANES >= 4) x += dpp_mov<0x4E>(x);              // quad_perm [2,3,0,1]: lane ^ 2
+  if (LANES >= 8) x += dpp_mov<0x141>(x);             // row_half_mirror: quads 0<->1
+  if (LANES >= 16) x += dpp_mov<0x140>(x);            // row_mirror: halves of 16
+  return x;
+}
+
+}  // namespace duo

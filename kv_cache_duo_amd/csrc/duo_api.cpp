@@ -1,0 +1,289 @@
+// Host side of the C ABI declared in include/duo.h: validation, head
+// partition, region layout, host length mirror and kernel launch ordering.
+//
+// Head kinds come from the offline identification that DuoAttention runs on
+// synthetic data (sourcepulse card, "How It Works"); here they are an input.
+// Retrieval KV heads get a full contiguous cache, streaming KV heads a
+// constant-length sink + ring cache (DuoAttention abstract).  Every check
+// runs before anything is enqueued, so a failing call changes nothing.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "duo.h"
+#include "duo_internal.h"
+
+struct duo_cache {
+  duo_config cfg;
+  std::vector<uint8_t> mask;
+  duo::Geom geom;
+  duo_layout layout;
+  std::vector<int64_t> len;  // host mirror of the stored tokens per sequence
+};
+
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kMaxLen = int64_t(1) << 30;
+
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int head_chunk_for(int G) {
+  for (int c : {8, 4, 2, 1})
+    if (G % c == 0) return c;
+  return 1;
+}
+
+duo_status check_config(const duo_config* c) {
+  if (c == nullptr) return DUO_ERR_INVALID_ARG;
+  if (c->batch < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1) return DUO_ERR_INVALID_ARG;
+  if (c->num_q_heads % c->num_kv_heads != 0) return DUO_ERR_INVALID_ARG;
+  if (c->sink < 0 || c->recent < 1 || c->max_len < 1) return DUO_ERR_INVALID_ARG;
+  if (!(c->scale >= 0.f) || !std::isfinite(c->scale)) return DUO_ERR_INVALID_ARG;
+  if (c->kv_head_is_retrieval == nullptr) return DUO_ERR_INVALID_ARG;
+  if (c->head_dim != 64 && c->head_dim != 128) return DUO_ERR_UNSUPPORTED;
+  if (c->batch > DUO_MAX_BATCH || c->num_kv_heads > duo::kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
+  if (c->max_len > kMaxLen || (int64_t)c->sink + c->recent > kMaxLen) return DUO_ERR_UNSUPPORTED;
+  return DUO_OK;
+}
+
+// Fill geometry and layout for a config (no device pointers yet).
+void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
+  std::memset(g, 0, sizeof(*g));
+  std::memset(L, 0, sizeof(*L));
+  g->B = c->batch;
+  g->Hq = c->num_q_heads;
+  g->Hkv = c->num_kv_heads;
+  g->G = c->num_q_heads / c->num_kv_heads;
+  g->D = c->head_dim;
+  g->S = c->sink;
+  g->W = c->recent;
+  g->slots = c->sink + c->recent;
+  g->max_len = c->max_len;
+  const float scale = c->scale > 0.f ? c->scale : 1.0f / std::sqrt((float)c->head_dim);
+  g->scale_log2 = scale * 1.4426950408889634f;
+  int nr = 0, ns = 0;
+  for (int k = 0; k < c->num_kv_heads; ++k)
+    if (c->kv_head_is_retrieval[k]) g->index_of_kv[k] = (uint8_t)nr++, g->is_retrieval[k] = 1;
+  for (int k = 0; k < c->num_kv_heads; ++k)
+    if (!c->kv_head_is_retrieval[k]) g->index_of_kv[k] = (uint8_t)ns++, g->is_retrieval[k] = 0;
+  for (int k = 0; k < c->num_kv_heads; ++k)
+    g->kv_of_unit[g->is_retrieval[k] ? g->index_of_kv[k] : nr + g->index_of_kv[k]] = (uint8_t)k;
+  g->nR = nr;
+  g->nS = ns;
+  g->max_splits = duo::max_splits_for(c->max_len, g->slots);
+
+  const int gc = head_chunk_for(g->G);
+  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / gc);
+  int64_t off = 0;
+  L->lengths_offset = off;
+  off = align_up(off + 4 * (int64_t)g->B);
+  L->work_offset = off;
+  const int64_t tickets_off = off;
+  off = align_up(off + 4 * units);
+  const int64_t partials_off = off;
+  off = align_up(off + 4 * units * g->max_splits * gc * (g->D + 2));
+  L->work_bytes = off - tickets_off;
+  (void)partials_off;
+  const int64_t row = 2 * (int64_t)g->D;
+  L->rk_offset = off;
+  off = align_up(off + (int64_t)g->B * nr * g->max_len * row);
+  L->rv_offset = off;
+  off = align_up(off + (int64_t)g->B * nr * g->max_len * row);
+  L->sk_offset = off;
+  off = align_up(off + (int64_t)g->B * ns * g->slots * row);
+  L->sv_offset = off;
+  off = align_up(off + (int64_t)g->B * ns * g->slots * row);
+  L->total_bytes = off;
+  L->n_retrieval = nr;
+  L->n_streaming = ns;
+  L->slots_per_streaming_head = g->slots;
+}
+
+void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
+  char* base = static_cast<char*>(buf);
+  const int gc = head_chunk_for(g->G);
+  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / gc);
+  g->lengths = reinterpret_cast<int32_t*>(base + L.lengths_offset);
+  g->tickets = reinterpret_cast<uint32_t*>(base + L.work_offset);
+  g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units));
+  g->rk = reinterpret_cast<uint16_t*>(base + L.rk_offset);
+  g->rv = reinterpret_cast<uint16_t*>(base + L.rv_offset);
+  g->sk = reinterpret_cast<uint16_t*>(base + L.sk_offset);
+  g->sv = reinterpret_cast<uint16_t*>(base + L.sv_offset);
+}
+
+duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int64_t* lengths, duo_cache** out,
+                      bool zero, void* stream) {
+  duo_status st = check_config(cfg);
+  if (st != DUO_OK) return st;
+  if (out == nullptr) return DUO_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(buf) % kAlign) != 0) return DUO_ERR_INVALID_ARG;
+  duo::Geom g;
+  duo_layout L;
+  plan_layout(cfg, &g, &L);
+  if ((int64_t)bytes < L.total_bytes) return DUO_ERR_BUFFER_TOO_SMALL;
+  if (lengths != nullptr)
+    for (int b = 0; b < cfg->batch; ++b)
+      if (lengths[b] < 0 || lengths[b] > cfg->max_len) return DUO_ERR_INVALID_ARG;
+  duo_cache* h = new (std::nothrow) duo_cache;
+  if (h == nullptr) return DUO_ERR_INVALID_ARG;
+  h->cfg = *cfg;
+  h->mask.assign(cfg->kv_head_is_retrieval, cfg->kv_head_is_retrieval + cfg->num_kv_heads);
+  h->cfg.kv_head_is_retrieval = h->mask.data();
+  h->geom = g;
+  h->layout = L;
+  bind_device(&h->geom, L, buf);
+  h->len.assign(cfg->batch, 0);
+  if (lengths != nullptr)
+    for (int b = 0; b < cfg->batch; ++b) h->len[b] = lengths[b];
+  if (zero) {
+    // lengths and merge tickets are contiguous: [0, partials)
+    const int gc = head_chunk_for(g.G);
+    const int64_t units = (int64_t)g.B * g.Hkv * (g.G / gc);
+    const int64_t words = (align_up(L.work_offset + 4 * units) - L.lengths_offset) / 4;
+    hipError_t e = duo::launch_zero_words(reinterpret_cast<uint32_t*>(h->geom.lengths), words,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      delete h;
+      return DUO_ERR_HIP;
+    }
+  }
+  *out = h;
+  return DUO_OK;
+}
+
+// Shared validation of a chunk call; fills the sequence table.
+duo_status check_chunk(const duo_cache* h, const int32_t* n_new, int32_t chunk, duo::Seqs* sq, int32_t* max_n) {
+  if (chunk < 1) return DUO_ERR_INVALID_ARG;
+  if (n_new == nullptr) return DUO_ERR_INVALID_ARG;
+  int32_t mx = 0;
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    if (n_new[b] < 0 || n_new[b] > chunk) return DUO_ERR_INVALID_ARG;
+    if (h->len[b] + n_new[b] > h->cfg.max_len) return DUO_ERR_CAPACITY;
+    mx = n_new[b] > mx ? n_new[b] : mx;
+  }
+  std::memset(sq, 0, sizeof(*sq));
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    sq->len[b] = (int32_t)h->len[b];
+    sq->n[b] = n_new[b];
+  }
+  *max_n = mx;
+  return DUO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* duo_status_string(duo_status s) {
+  switch (s) {
+    case DUO_OK: return "ok";
+    case DUO_ERR_INVALID_ARG: return "invalid argument";
+    case DUO_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DUO_ERR_BUFFER_TOO_SMALL: return "device buffer too small";
+    case DUO_ERR_CAPACITY: return "sequence would exceed max_len";
+    case DUO_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes, size_t* required_bytes,
+                          duo_cache** out, void* stream) {
+  duo_status st = check_config(cfg);
+  if (st != DUO_OK) return st;
+  duo::Geom g;
+  duo_layout L;
+  plan_layout(cfg, &g, &L);
+  if (required_bytes != nullptr) *required_bytes = (size_t)L.total_bytes;
+  if (dev_buf == nullptr) return required_bytes != nullptr ? DUO_OK : DUO_ERR_INVALID_ARG;
+  return new_handle(cfg, dev_buf, buf_bytes, nullptr, out, true, stream);
+}
+
+duo_status duo_cache_attach(const duo_config* cfg, void* dev_buf, size_t buf_bytes, const int64_t* lengths,
+                            duo_cache** out) {
+  if (dev_buf == nullptr || lengths == nullptr) return DUO_ERR_INVALID_ARG;
+  return new_handle(cfg, dev_buf, buf_bytes, lengths, out, false, nullptr);
+}
+
+void duo_cache_destroy(duo_cache* h) { delete h; }
+
+duo_status duo_cache_append(duo_cache* h, const void* k, const void* v, const int32_t* n_new, int32_t chunk,
+                            void* stream) {
+  if (h == nullptr || !aligned16(k) || !aligned16(v)) return DUO_ERR_INVALID_ARG;
+  duo::Seqs sq;
+  int32_t max_n = 0;
+  duo_status st = check_chunk(h, n_new, chunk, &sq, &max_n);
+  if (st != DUO_OK) return st;
+  hipError_t e = duo::launch_append(h->geom, sq, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                    chunk, max_n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += n_new[b];
+  return DUO_OK;
+}
+
+duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v, const int32_t* n_new,
+                       int32_t chunk, void* out, void* stream) {
+  if (h == nullptr || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return DUO_ERR_INVALID_ARG;
+  duo::Seqs sq;
+  int32_t max_n = 0;
+  duo_status st = check_chunk(h, n_new, chunk, &sq, &max_n);
+  if (st != DUO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Attention first: streaming heads read ring slots that this chunk's
+  // append will overwrite.  Then the append stores the chunk.
+  hipError_t e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                     static_cast<const uint16_t*>(v), chunk, max_n, static_cast<uint16_t*>(out), s);
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  e = duo::launch_append(h->geom, sq, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk,
+                         max_n, s);
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += n_new[b];
+  return DUO_OK;
+}
+
+duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v, void* out, void* stream) {
+  if (h == nullptr || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return DUO_ERR_INVALID_ARG;
+  for (int b = 0; b < h->cfg.batch; ++b)
+    if (h->len[b] + 1 > h->cfg.max_len) return DUO_ERR_CAPACITY;
+  duo::Seqs sq;
+  std::memset(&sq, 0, sizeof(sq));
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    sq.len[b] = (int32_t)h->len[b];
+    sq.n[b] = 1;
+  }
+  const duo::DecodePlan p = duo::plan_decode(h->geom, sq);
+  hipError_t e = duo::launch_decode(h->geom, sq, p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                                    static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out),
+                                    static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += 1;
+  return DUO_OK;
+}
+
+duo_status duo_cache_lengths(const duo_cache* h, int64_t* out) {
+  if (h == nullptr || out == nullptr) return DUO_ERR_INVALID_ARG;
+  for (int b = 0; b < h->cfg.batch; ++b) out[b] = h->len[b];
+  return DUO_OK;
+}
+
+duo_status duo_cache_layout(const duo_cache* h, duo_layout* out) {
+  if (h == nullptr || out == nullptr) return DUO_ERR_INVALID_ARG;
+  *out = h->layout;
+  return DUO_OK;
+}
+
+duo_status duo_cache_head_index(const duo_cache* h, int32_t* out) {
+  if (h == nullptr || out == nullptr) return DUO_ERR_INVALID_ARG;
+  for (int k = 0; k < h->cfg.num_kv_heads; ++k) out[k] = h->geom.index_of_kv[k];
+  return DUO_OK;
+}
+
+}  // extern "C"

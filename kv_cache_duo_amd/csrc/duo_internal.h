@@ -1,0 +1,67 @@
+// Internal definitions shared by the host library (duo_api.cpp) and the
+// gfx950 kernels (*.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "duo.h"
+
+namespace duo {
+
+constexpr int kMaxKvHeads = 256;  // kv head ids are stored as uint8
+
+// Geometry of one cache, passed by value to every kernel.
+struct Geom {
+  int32_t B, Hq, Hkv, G, D;
+  int32_t S, W, slots;        // sink, recent, sink+recent
+  int32_t nR, nS;             // retrieval / streaming KV heads
+  int64_t max_len;
+  float scale_log2;           // softmax scale * log2(e): scores in base-2 units
+  uint16_t* rk;               // bf16 bits [B][nR][max_len][D]
+  uint16_t* rv;
+  uint16_t* sk;               // bf16 bits [B][nS][slots][D]
+  uint16_t* sv;
+  int32_t* lengths;           // [B]
+  float* partials;            // split-K records, see decode.hip
+  uint32_t* tickets;          // [B][Hkv][head chunks] merge counters
+  int32_t max_splits;         // capacity of the partial records per unit
+  // unit u < nR is retrieval KV head kv_of_unit[u]; unit nR+s is streaming
+  // KV head kv_of_unit[nR+s]; index_of_kv[k] is k's index within its kind.
+  uint8_t kv_of_unit[kMaxKvHeads];
+  uint8_t index_of_kv[kMaxKvHeads];
+  uint8_t is_retrieval[kMaxKvHeads];
+};
+
+// Per-call sequence table: tokens already stored and tokens added.
+struct Seqs {
+  int32_t len[DUO_MAX_BATCH];
+  int32_t n[DUO_MAX_BATCH];
+};
+
+// Launchers (each returns hipGetLastError() after the launch).
+hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s);
+
+hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v,
+                         int32_t chunk, int32_t max_n, hipStream_t s);
+
+struct DecodePlan {
+  int32_t split_tokens;      // rows per work-group (multiple of 64)
+  int32_t splits_r;          // max splits over retrieval units
+  int32_t splits_s;          // max splits over streaming units
+  int32_t head_chunk;        // query heads handled per work-group (divides G)
+};
+DecodePlan plan_decode(const Geom& g, const Seqs& q);
+hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p,
+                         const uint16_t* qin, const uint16_t* kin, const uint16_t* vin,
+                         uint16_t* out, hipStream_t s);
+
+hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, const uint16_t* kin,
+                          const uint16_t* vin, int32_t chunk, int32_t max_n, uint16_t* out,
+                          hipStream_t s);
+
+// Size of the split-K partial area for a geometry (bytes) and the per-unit
+// split capacity it is sized for.
+int32_t max_splits_for(int64_t max_len, int32_t slots);
+
+}  // namespace duo

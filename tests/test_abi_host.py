@@ -1,0 +1,177 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+Every call here fails validation (or needs no device work), so nothing is
+ever enqueued: handles come from duo_cache_attach over a fake, aligned
+device address that is never dereferenced.
+"""
+
+import ctypes
+
+import pytest
+
+import kv_cache_duo_amd as duo
+from workloads import WORKLOADS, workload_mask
+
+FAKE = 0x7f0000000000  # 256-byte aligned, never dereferenced
+
+
+def _cfg(**kw):
+    base = dict(batch=2, num_q_heads=8, num_kv_heads=4, head_dim=128, max_len=1000,
+                sink=4, recent=16, kv_head_is_retrieval=[1, 0, 1, 0])
+    base.update(kw)
+    return duo.Config(**base)
+
+
+def _attach(cfg, lengths=None):
+    req = duo.required_bytes(cfg)
+    return duo.duo_cache_attach(cfg, FAKE, req, lengths or [0] * cfg.batch)
+
+
+def test_library_exports_every_header_function():
+    lib = duo.load_library()
+    names = duo.header_functions()
+    assert {"duo_cache_init", "duo_prefill", "duo_decode", "duo_cache_append"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(duo._SIGNATURES), "binding and header disagree"
+
+
+def test_status_strings():
+    for s in range(6):
+        assert duo.status_string(s)
+    assert duo.status_string(0) == "ok"
+
+
+@pytest.mark.parametrize("name", sorted(WORKLOADS))
+def test_required_bytes_for_workloads(name):
+    w = WORKLOADS[name]
+    mask = workload_mask(w)
+    cfg = duo.Config(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                     w.prefill + w.decode_steps, w.sink, w.recent, list(mask))
+    req = duo.required_bytes(cfg)
+    nr = int(mask.sum())
+    ns = w.num_kv_heads - nr
+    kv_bytes = 2 * 2 * w.batch * w.head_dim * (nr * cfg.max_len + ns * (w.sink + w.recent))
+    assert req >= kv_bytes
+    # the rest (lengths, tickets, split-K partials, alignment) stays small
+    assert req - kv_bytes <= max(64 << 20, kv_bytes // 4)
+    bigger = duo.Config(**{**cfg.__dict__, "max_len": cfg.max_len + 1})
+    assert duo.required_bytes(bigger) >= req + 2 * 2 * w.batch * nr * w.head_dim - 4096
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_q_heads=6), duo.DUO_ERR_INVALID_ARG),       # Hq % Hkv != 0
+    (dict(head_dim=96), duo.DUO_ERR_UNSUPPORTED),
+    (dict(head_dim=256), duo.DUO_ERR_UNSUPPORTED),
+    (dict(sink=-1), duo.DUO_ERR_INVALID_ARG),
+    (dict(recent=0), duo.DUO_ERR_INVALID_ARG),
+    (dict(batch=0), duo.DUO_ERR_INVALID_ARG),
+    (dict(batch=129, kv_head_is_retrieval=[1, 0, 1, 0]), duo.DUO_ERR_UNSUPPORTED),
+    (dict(max_len=0), duo.DUO_ERR_INVALID_ARG),
+    (dict(scale=-1.0), duo.DUO_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), duo.DUO_ERR_INVALID_ARG),
+    (dict(max_len=1 << 31), duo.DUO_ERR_UNSUPPORTED),
+])
+def test_invalid_configs(kw, status):
+    with pytest.raises(duo.DuoError) as e:
+        duo.required_bytes(_cfg(**kw))
+    assert e.value.status == status
+
+
+def test_null_mask_and_null_outputs():
+    lib = duo.load_library()
+    c, _m = _cfg()._c()
+    c.kv_head_is_retrieval = None
+    req = ctypes.c_size_t(0)
+    assert lib.duo_cache_init(ctypes.byref(c), None, 0, ctypes.byref(req), None, None) == duo.DUO_ERR_INVALID_ARG
+    c2, _m2 = _cfg()._c()
+    # no buffer and nowhere to write the size
+    assert lib.duo_cache_init(ctypes.byref(c2), None, 0, None, None, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_cache_init(None, None, 0, ctypes.byref(req), None, None) == duo.DUO_ERR_INVALID_ARG
+
+
+def test_attach_checks_buffer_and_lengths():
+    cfg = _cfg()
+    req = duo.required_bytes(cfg)
+    with pytest.raises(duo.DuoError) as e:
+        duo.duo_cache_attach(cfg, FAKE, req - 1, [0, 0])
+    assert e.value.status == duo.DUO_ERR_BUFFER_TOO_SMALL
+    with pytest.raises(duo.DuoError) as e:
+        duo.duo_cache_attach(cfg, FAKE + 16, req, [0, 0])
+    assert e.value.status == duo.DUO_ERR_INVALID_ARG
+    with pytest.raises(duo.DuoError) as e:
+        duo.duo_cache_attach(cfg, FAKE, req, [0, cfg.max_len + 1])
+    assert e.value.status == duo.DUO_ERR_INVALID_ARG
+    with pytest.raises(duo.DuoError) as e:
+        duo.duo_cache_attach(cfg, 0, req, [0, 0])
+    assert e.value.status == duo.DUO_ERR_INVALID_ARG
+
+
+def test_layout_and_head_index():
+    cfg = _cfg(kv_head_is_retrieval=[0, 1, 1, 0])
+    c = _attach(cfg, [5, 7])
+    assert c.lengths() == [5, 7]
+    lay = c.layout()
+    assert (lay.n_retrieval, lay.n_streaming) == (2, 2)
+    assert lay.slots_per_streaming_head == cfg.sink + cfg.recent
+    offs = [lay.lengths_offset, lay.work_offset, lay.rk_offset, lay.rv_offset, lay.sk_offset, lay.sv_offset]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    row = 2 * cfg.head_dim
+    assert lay.rv_offset - lay.rk_offset >= cfg.batch * 2 * cfg.max_len * row
+    assert lay.sv_offset - lay.sk_offset >= cfg.batch * 2 * (cfg.sink + cfg.recent) * row
+    assert lay.total_bytes == duo.required_bytes(cfg)
+    # retrieval heads 1,2 -> indices 0,1; streaming heads 0,3 -> indices 0,1
+    assert c.head_index() == [0, 0, 1, 1]
+
+
+def _raw(c):
+    return duo.load_library(), c.handle
+
+
+def test_call_validation_leaves_state_unchanged():
+    cfg = _cfg()
+    c = _attach(cfg, [3, 990])
+    lib, h = _raw(c)
+    A = FAKE + 4096  # aligned fake device pointers
+    n_ok = (ctypes.c_int32 * 2)(1, 1)
+    # null / misaligned pointers
+    assert lib.duo_decode(h, None, A, A, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_decode(h, A + 2, A, A, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_decode(None, A, A, A, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_prefill(h, A, A, A, n_ok, 4, None, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_prefill(h, A, A + 8, A, n_ok, 4, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_prefill(h, A, A, A, None, 4, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_cache_append(h, None, A, n_ok, 4, None) == duo.DUO_ERR_INVALID_ARG
+    # chunk and n_new ranges
+    assert lib.duo_prefill(h, A, A, A, n_ok, 0, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_prefill(h, A, A, A, (ctypes.c_int32 * 2)(5, 1), 4, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_cache_append(h, A, A, (ctypes.c_int32 * 2)(-1, 0), 4, None) == duo.DUO_ERR_INVALID_ARG
+    # capacity: sequence 1 holds 990 of 1000 tokens
+    assert lib.duo_prefill(h, A, A, A, (ctypes.c_int32 * 2)(0, 11), 16, A, None) == duo.DUO_ERR_CAPACITY
+    assert lib.duo_cache_append(h, A, A, (ctypes.c_int32 * 2)(0, 11), 16, None) == duo.DUO_ERR_CAPACITY
+    assert c.lengths() == [3, 990]
+    full = _attach(cfg, [10, cfg.max_len])
+    lib, h2 = _raw(full)
+    assert lib.duo_decode(h2, A, A, A, A, None) == duo.DUO_ERR_CAPACITY
+    assert full.lengths() == [10, cfg.max_len]
+
+
+def test_introspection_null_arguments():
+    lib = duo.load_library()
+    lay = duo.Layout()
+    assert lib.duo_cache_layout(None, ctypes.byref(lay)) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_cache_lengths(None, None) == duo.DUO_ERR_INVALID_ARG
+    c = _attach(_cfg())
+    assert lib.duo_cache_head_index(c.handle, None) == duo.DUO_ERR_INVALID_ARG
+    lib.duo_cache_destroy(None)  # no-op
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    cfg = _cfg()
+    with pytest.raises(ValueError):
+        duo.duo_cache_init(cfg, torch.empty(16, dtype=torch.uint8))
+    c = _attach(cfg)
+    q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        duo.duo_decode(c, q, q[:, :4], q[:, :4], q)
