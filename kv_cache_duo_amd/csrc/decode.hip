@@ -5,19 +5,23 @@
 // constant-length cache of sinks + recent tokens.  Decoding is memory-bound:
 // every cached K/V byte of a retrieval head is read once per step.
 //
-// One launch does everything for a step:
-//   * work item = (sequence b, KV head, query-head chunk, split).  A split is
-//     a contiguous range of cache rows (retrieval: rows = positions 0..L;
-//     streaming: the min(L+1, sink+recent) occupied slots).  The new token's
-//     row is read from the input and written to the cache by its owner, so
-//     no work item ever reads a row that is being written;
-//   * each work-group streams its rows with coalesced 16-byte loads (a row of
-//     D bf16 is read by D/8 lanes), scores all query heads of the KV group
-//     from the same K bytes with bf16 dot2 + DPP group sums, and keeps an
-//     online softmax (running max m, sum l, unnormalised o) per head;
-//   * splits of one unit are merged by the last work-group to finish (agent
-//     -scope atomic ticket): M = max m_k, L = sum l_k 2^(m_k-M),
-//     O = sum o_k 2^(m_k-M) / L.  A unit with one split writes directly.
+// Two launches per step:
+//   decode_kernel -- work item = (sequence b, KV head, query-head chunk,
+//     split).  A split is a contiguous range of cache rows (retrieval: rows =
+//     positions 0..L; streaming: the min(L+1, sink+recent) occupied slots).
+//     The new token's row is read from the input and stored to the cache by
+//     its owner, so no work item reads a row that is being written.  Each
+//     work-group streams its rows with coalesced 16-byte loads (a row of D
+//     bf16 is read by D/8 lanes; one wave instruction reads 1 KB of
+//     consecutive rows), scores every query head of the KV group from the
+//     same K bytes with bf16 dot2 + DPP group sums, and keeps an online
+//     softmax (running max m, sum l, unnormalised o) per head.  A unit with
+//     one split writes the output; otherwise each split writes a record.
+//   merge_kernel -- one work-group per unit with several splits:
+//     M = max m_k, L = sum l_k 2^(m_k-M), O = sum o_k 2^(m_k-M) / L.
+// The kernel boundary makes the records visible across XCDs; an in-kernel
+// "last work-group merges" scheme would need an agent-scope release/acquire
+// per work-group, which on gfx950 writes back and invalidates the XCD's L2.
 // Scores are kept in base-2 units (scale * log2 e folded in), so exp2 is the
 // only transcendental.
 #include <cfloat>
@@ -31,7 +35,7 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = kThreads / 64;
-constexpr int kInFlight = 4;   // K rows and V rows loaded per lane before use
+constexpr int kMaxMergeRecords = 1024;  // (m, l) pairs the merge stages in LDS
 
 struct DecodeArgs {
   const uint16_t* q;  // [B][Hq][D]
@@ -43,15 +47,24 @@ struct DecodeArgs {
 
 __device__ __forceinline__ float max_or_zero(float m) { return m == -INFINITY ? 0.f : m; }
 
+// Records of one unit (b, kv head, head chunk): o [max_splits][GC][D] fp32,
+// then (m, l) [max_splits][GC].
+template <int D, int GC>
+__device__ __forceinline__ float* unit_records(const Geom& g, int64_t pu) {
+  return g.partials + pu * g.max_splits * GC * (D + 2);
+}
+
 template <int D, int GC>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, DecodeArgs a) {
   constexpr int LPR = D / 8;                  // lanes per row (8 bf16 each)
   constexpr int RPW = 64 / LPR;               // rows per wave per load
+  // K and V rows each lane loads per batch (two batches in flight); fewer
+  // when more query heads per work-group need registers.
+  constexpr int kInFlight = GC >= 4 ? 2 : 4;
   constexpr int ROWS_ITER = kWaves * RPW * kInFlight;
   __shared__ float sm_o[kWaves][GC][D];
   __shared__ float sm_m[kWaves][GC];
   __shared__ float sm_l[kWaves][GC];
-  __shared__ int sm_last;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -62,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   const int n_hc = g.G / GC;
   int id = blockIdx.x;
   const int items_r = g.B * g.nR * n_hc * a.splits_r;
-  bool retrieval = id < items_r;
+  const bool retrieval = id < items_r;
   int splits = a.splits_r;
   if (!retrieval) {
     id -= items_r;
@@ -109,26 +122,27 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     for (int e = 0; e < 8; ++e) o[gg][e] = 0.f;
   }
 
-  for (int base = r0; base < r1; base += ROWS_ITER) {
-    uint4 kr[kInFlight], vr[kInFlight];
-    bool valid[kInFlight];
+  // Row j of a batch starting at `base`: consecutive rows per load
+  // instruction of a wave, so each instruction reads RPW * D * 2 = 1 KB.
+  auto row_of = [&](int base, int j) { return base + (j * kWaves + wave) * RPW + grp; };
+  // Loads are unconditional (rows past the split re-read its last row and
+  // get a -inf score), so the compiler can count outstanding loads and wait
+  // only for the older batch.
+  auto load = [&](uint4 (&kr)[kInFlight], uint4 (&vr)[kInFlight], int base) {
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const int row = base + (j * kWaves + wave) * RPW + grp;
-      valid[j] = row < r1;
+      const int row = min(row_of(base, j), r1 - 1);
       const uint16_t* pk = row == new_row ? nk : ck + (int64_t)row * D;
       const uint16_t* pv = row == new_row ? nv : cv + (int64_t)row * D;
-      if (valid[j]) {
-        kr[j] = reinterpret_cast<const uint4*>(pk)[c];
-        vr[j] = reinterpret_cast<const uint4*>(pv)[c];
-      } else {
-        kr[j] = make_uint4(0, 0, 0, 0);
-        vr[j] = make_uint4(0, 0, 0, 0);
-      }
+      kr[j] = reinterpret_cast<const uint4*>(pk)[c];
+      vr[j] = reinterpret_cast<const uint4*>(pv)[c];
     }
+  };
+  auto process = [&](const uint4 (&kr)[kInFlight], const uint4 (&vr)[kInFlight], int base) {
     float s[kInFlight][GC];
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
+      const bool valid = row_of(base, j) < r1;
 #pragma unroll
       for (int gg = 0; gg < GC; ++gg) {
         float acc = dot2_bf16(kr[j].x, qw[gg][0], 0.f);
@@ -136,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
         acc = dot2_bf16(kr[j].z, qw[gg][2], acc);
         acc = dot2_bf16(kr[j].w, qw[gg][3], acc);
         acc = group_sum<LPR>(acc);
-        s[j][gg] = valid[j] ? acc * g.scale_log2 : -INFINITY;
+        s[j][gg] = valid ? acc * g.scale_log2 : -INFINITY;
       }
     }
 #pragma unroll
@@ -162,6 +176,23 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
         }
       }
       m[gg] = mn;
+    }
+  };
+
+  // ---- stream the rows, the next batch's loads in flight during each batch
+  {
+    uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
+    load(ka, va, r0);
+    for (int base = r0;;) {
+      const int nb = base + ROWS_ITER;
+      load(kb, vb, nb);  // past the end: clamped rows, served by the cache
+      process(ka, va, base);
+      if (nb >= r1) break;
+      const int nb2 = nb + ROWS_ITER;
+      load(ka, va, nb2);
+      process(kb, vb, nb);
+      if (nb2 >= r1) break;
+      base = nb2;
     }
   }
 
@@ -206,9 +237,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   }
   __syncthreads();
 
-  // ---- merge the waves; write the output or this split's partial record
+  // ---- merge the waves; write the output or this split's record
   const int64_t pu = ((int64_t)b * g.Hkv + kvh) * n_hc + hc;
-  float* recs = g.partials + pu * g.max_splits * GC * (D + 2);
+  float* rec_o = unit_records<D, GC>(g, pu);
+  float2* rec_ml = reinterpret_cast<float2*>(rec_o + (int64_t)g.max_splits * GC * D);
   for (int t = threadIdx.x; t < GC * D; t += kThreads) {
     const int gg = t / D, d = t % D;
     float mw = sm_m[0][gg];
@@ -225,60 +257,115 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     if (ns == 1) {
       a.out[((int64_t)b * g.Hq + h0 + gg) * D + d] = (uint16_t)f32_to_bf16_bits(osum / lsum);
     } else {
-      float* rec = recs + ((int64_t)split * GC + gg) * (D + 2);
-      rec[d] = osum;
-      if (d == 0) {
-        rec[D] = mw;
-        rec[D + 1] = lsum;
+      rec_o[((int64_t)split * GC + gg) * D + d] = osum;
+      if (d == 0) rec_ml[split * GC + gg] = make_float2(mw, lsum);
+    }
+  }
+}
+
+// One work-group per (b, kv head, head chunk) whose rows were split.
+template <int D, int GC>
+__global__ __launch_bounds__(kThreads) void merge_kernel(Geom g, Seqs sq, DecodeArgs a) {
+  constexpr int CPR = GC * D / 4;             // float4 chunks of one record's o
+  constexpr int KL = kThreads / CPR;          // records summed in parallel
+  static_assert(CPR <= kThreads && kThreads % CPR == 0, "merge mapping");
+  __shared__ float2 st_ml[kMaxMergeRecords];  // (m, then f = 2^(m-M); l)
+  __shared__ float4 st_acc[kThreads];
+  __shared__ float st_L[GC];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n_hc = g.G / GC;
+  const int pu = blockIdx.x;
+  const int hc = pu % n_hc;
+  const int kvh = (pu / n_hc) % g.Hkv;
+  const int b = pu / (n_hc * g.Hkv);
+  const int L = sq.len[b];
+  const int T = g.is_retrieval[kvh] ? L + 1 : min(L + 1, g.slots);
+  const int ns = (T + a.split_tokens - 1) / a.split_tokens;
+  if (ns <= 1) return;
+  const int h0 = kvh * g.G + hc * GC;
+  const float* rec_o = unit_records<D, GC>(g, pu);
+  const float2* rec_ml = reinterpret_cast<const float2*>(rec_o + (int64_t)g.max_splits * GC * D);
+  const int nrec = ns * GC;  // <= kMaxMergeRecords by the split planning
+
+  // 1. stage every (m, l) pair
+  for (int i = threadIdx.x; i < nrec; i += kThreads) st_ml[i] = rec_ml[i];
+  __syncthreads();
+  // 2. per head: M = max m_k, f_k = 2^(m_k - M), L = sum l_k f_k
+  for (int gg = wave; gg < GC; gg += kWaves) {
+    float mx = -INFINITY;
+    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, st_ml[k * GC + gg].x);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mu = max_or_zero(mx);
+    float ls = 0.f;
+    for (int k = lane; k < ns; k += 64) {
+      const float2 ml = st_ml[k * GC + gg];
+      const float f = exp2_fast(ml.x - mu);
+      st_ml[k * GC + gg].x = f;
+      ls += ml.y * f;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
+    if (lane == 0) st_L[gg] = ls;
+  }
+  __syncthreads();
+  // 3. O = sum_k f_k o_k: KL records at a time, 8 loads in flight per thread
+  {
+    const int cc = threadIdx.x % CPR;
+    const int kl = threadIdx.x / CPR;
+    const int gg = (cc * 4) / D;
+    const float4* src = reinterpret_cast<const float4*>(rec_o);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = kl; k0 < ns; k0 += KL * 8) {
+      float4 v[8];
+#pragma unroll
+      for (int u2 = 0; u2 < 8; ++u2) {
+        const int k = k0 + u2 * KL;
+        v[u2] = k < ns ? src[(int64_t)k * CPR + cc] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u2 = 0; u2 < 8; ++u2) {
+        const int k = k0 + u2 * KL;
+        const float f = k < ns ? st_ml[k * GC + gg].x : 0.f;
+        acc.x = fmaf(v[u2].x, f, acc.x);
+        acc.y = fmaf(v[u2].y, f, acc.y);
+        acc.z = fmaf(v[u2].z, f, acc.z);
+        acc.w = fmaf(v[u2].w, f, acc.w);
       }
     }
-  }
-  if (ns == 1) return;
-
-  // ---- last work-group of the unit merges all splits
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&g.tickets[pu], 1u);
-    sm_last = prev == (uint32_t)(ns - 1);
+    st_acc[threadIdx.x] = acc;
   }
   __syncthreads();
-  if (!sm_last) return;
-  __threadfence();
-  for (int t = threadIdx.x; t < GC * D; t += kThreads) {
-    const int gg = t / D, d = t % D;
-    float mx = -INFINITY;
-    for (int k = 0; k < ns; ++k) mx = fmaxf(mx, recs[((int64_t)k * GC + gg) * (D + 2) + D]);
-    const float mu = max_or_zero(mx);
-    float lsum = 0.f, osum = 0.f;
-    for (int k = 0; k < ns; ++k) {
-      const float* rec = recs + ((int64_t)k * GC + gg) * (D + 2);
-      const float f = exp2_fast(rec[D] - mu);
-      lsum += rec[D + 1] * f;
-      osum += rec[d] * f;
+  if (threadIdx.x < CPR) {
+    const int cc = threadIdx.x;
+    const int gg = (cc * 4) / D;
+    float4 s4 = st_acc[cc];
+    for (int kl = 1; kl < KL; ++kl) {
+      const float4 x = st_acc[kl * CPR + cc];
+      s4.x += x.x; s4.y += x.y; s4.z += x.z; s4.w += x.w;
     }
-    a.out[((int64_t)b * g.Hq + h0 + gg) * D + d] = (uint16_t)f32_to_bf16_bits(osum / lsum);
+    const float inv = 1.0f / st_L[gg];
+    const uint32_t w0 = pack_bf16x2(s4.x * inv, s4.y * inv);
+    const uint32_t w1 = pack_bf16x2(s4.z * inv, s4.w * inv);
+    const int d0 = (cc * 4) % D;
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)b * g.Hq + h0 + gg) * D + d0) = make_uint2(w0, w1);
   }
-  if (threadIdx.x == 0) g.tickets[pu] = 0u;  // ready for the next call
 }
 
 }  // namespace
 
-int32_t max_splits_for(int64_t max_len, int32_t slots) {
-  int64_t rows = max_len > slots ? max_len : slots;
-  int64_t s = (rows + 255) / 256;
-  return (int32_t)(s < 1024 ? s : 1024);
-}
-
-static int head_chunk_for(int G) {
-  for (int c : {8, 4, 2, 1})
-    if (G % c == 0) return c;
-  return 1;
+int32_t max_splits_for(int64_t max_len, int32_t slots, int head_chunk) {
+  const int64_t rows = max_len > slots ? max_len : slots;
+  const int64_t s = (rows + 255) / 256;
+  const int64_t cap = kMaxMergeRecords / head_chunk;
+  return (int32_t)(s < cap ? s : cap);
 }
 
 DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   DecodePlan p;
-  p.head_chunk = head_chunk_for(g.G);
+  p.head_chunk = decode_head_chunk(g.G);
   const int n_hc = g.G / p.head_chunk;
   int64_t total = 0;
   int32_t tmax = 1;
@@ -309,11 +396,13 @@ hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p, cons
   const int n_hc = g.G / p.head_chunk;
   const int64_t items = (int64_t)g.B * g.nR * n_hc * p.splits_r + (int64_t)g.B * g.nS * n_hc * p.splits_s;
   if (items <= 0) return hipSuccess;
-  const dim3 grid((unsigned)items), block(kThreads);
-#define DUO_DECODE_CASE(DD, GG)                                                   \
-  if (g.D == DD && p.head_chunk == GG) {                                          \
-    hipLaunchKernelGGL((decode_kernel<DD, GG>), grid, block, 0, s, g, q, a);      \
-    return hipGetLastError();                                                     \
+  const bool split = p.splits_r > 1 || p.splits_s > 1;
+  const dim3 grid((unsigned)items), block(kThreads), mgrid((unsigned)(g.B * g.Hkv * n_hc));
+#define DUO_DECODE_CASE(DD, GG)                                                        \
+  if (g.D == DD && p.head_chunk == GG) {                                               \
+    hipLaunchKernelGGL((decode_kernel<DD, GG>), grid, block, 0, s, g, q, a);           \
+    if (split) hipLaunchKernelGGL((merge_kernel<DD, GG>), mgrid, block, 0, s, g, q, a); \
+    return hipGetLastError();                                                          \
   }
   DUO_DECODE_CASE(128, 1)
   DUO_DECODE_CASE(128, 2)

@@ -33,12 +33,6 @@ int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int head_chunk_for(int G) {
-  for (int c : {8, 4, 2, 1})
-    if (G % c == 0) return c;
-  return 1;
-}
-
 duo_status check_config(const duo_config* c) {
   if (c == nullptr) return DUO_ERR_INVALID_ARG;
   if (c->batch < 1 || c->num_kv_heads < 1 || c->num_q_heads < 1) return DUO_ERR_INVALID_ARG;
@@ -76,20 +70,16 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
     g->kv_of_unit[g->is_retrieval[k] ? g->index_of_kv[k] : nr + g->index_of_kv[k]] = (uint8_t)k;
   g->nR = nr;
   g->nS = ns;
-  g->max_splits = duo::max_splits_for(c->max_len, g->slots);
+  g->max_splits = duo::max_splits_for(c->max_len, g->slots, duo::decode_head_chunk(g->G));
 
-  const int gc = head_chunk_for(g->G);
+  const int gc = duo::decode_head_chunk(g->G);
   const int64_t units = (int64_t)g->B * g->Hkv * (g->G / gc);
   int64_t off = 0;
   L->lengths_offset = off;
   off = align_up(off + 4 * (int64_t)g->B);
   L->work_offset = off;
-  const int64_t tickets_off = off;
-  off = align_up(off + 4 * units);
-  const int64_t partials_off = off;
   off = align_up(off + 4 * units * g->max_splits * gc * (g->D + 2));
-  L->work_bytes = off - tickets_off;
-  (void)partials_off;
+  L->work_bytes = off - L->work_offset;
   const int64_t row = 2 * (int64_t)g->D;
   L->rk_offset = off;
   off = align_up(off + (int64_t)g->B * nr * g->max_len * row);
@@ -107,11 +97,8 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
 
 void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   char* base = static_cast<char*>(buf);
-  const int gc = head_chunk_for(g->G);
-  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / gc);
   g->lengths = reinterpret_cast<int32_t*>(base + L.lengths_offset);
-  g->tickets = reinterpret_cast<uint32_t*>(base + L.work_offset);
-  g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units));
+  g->partials = reinterpret_cast<float*>(base + L.work_offset);
   g->rk = reinterpret_cast<uint16_t*>(base + L.rk_offset);
   g->rv = reinterpret_cast<uint16_t*>(base + L.rv_offset);
   g->sk = reinterpret_cast<uint16_t*>(base + L.sk_offset);
@@ -143,11 +130,7 @@ duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int6
   if (lengths != nullptr)
     for (int b = 0; b < cfg->batch; ++b) h->len[b] = lengths[b];
   if (zero) {
-    // lengths and merge tickets are contiguous: [0, partials)
-    const int gc = head_chunk_for(g.G);
-    const int64_t units = (int64_t)g.B * g.Hkv * (g.G / gc);
-    const int64_t words = (align_up(L.work_offset + 4 * units) - L.lengths_offset) / 4;
-    hipError_t e = duo::launch_zero_words(reinterpret_cast<uint32_t*>(h->geom.lengths), words,
+    hipError_t e = duo::launch_zero_words(reinterpret_cast<uint32_t*>(h->geom.lengths), cfg->batch,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
       delete h;

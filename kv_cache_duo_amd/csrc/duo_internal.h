@@ -24,7 +24,6 @@ struct Geom {
   uint16_t* sv;
   int32_t* lengths;           // [B]
   float* partials;            // split-K records, see decode.hip
-  uint32_t* tickets;          // [B][Hkv][head chunks] merge counters
   int32_t max_splits;         // capacity of the partial records per unit
   // unit u < nR is retrieval KV head kv_of_unit[u]; unit nR+s is streaming
   // KV head kv_of_unit[nR+s]; index_of_kv[k] is k's index within its kind.
@@ -60,8 +59,16 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
                           const uint16_t* vin, int32_t chunk, int32_t max_n, uint16_t* out,
                           hipStream_t s);
 
-// Size of the split-K partial area for a geometry (bytes) and the per-unit
-// split capacity it is sized for.
-int32_t max_splits_for(int64_t max_len, int32_t slots);
+// Query heads of one KV group handled together by a decode work-group.
+inline int decode_head_chunk(int G) {
+  for (int c : {8, 4, 2, 1})
+    if (G % c == 0) return c;
+  return 1;
+}
+
+// Split-K record capacity per (sequence, KV head, head chunk): enough for
+// splits of >= 256 rows, and at most 1024 / head_chunk records so that the
+// merging work-group can stage every (m, l) pair in LDS.
+int32_t max_splits_for(int64_t max_len, int32_t slots, int head_chunk);
 
 }  // namespace duo
