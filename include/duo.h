@@ -83,7 +83,8 @@ typedef struct duo_cache duo_cache;
  *   rk, rv   bf16  [B][nR][max_len][D]     retrieval cache, row = position
  *   sk, sv   bf16  [B][nS][sink+recent][D] streaming cache, slot map:
  *            slot(p) = p for p < sink, else sink + (p - sink) mod recent
- *   work     fp32 split-K partial results of decoding (library-private) */
+ *   work     uint32 split counters and fp32 split-K partial results of
+ *            decoding (library-private; the counters are zero between calls) */
 typedef struct duo_layout {
   int64_t lengths_offset;
   int64_t rk_offset, rv_offset;
@@ -98,8 +99,8 @@ typedef struct duo_layout {
 /* Lay out a new, empty cache in `dev_buf`.
  * dev_buf == NULL: only writes *required_bytes (no device work); *out untouched.
  * Otherwise dev_buf (256-byte aligned, buf_bytes long, caller-owned, must
- * outlive the handle) receives the layout above; the lengths are zeroed on
- * `stream` by a fill kernel; *out gets a new handle.
+ * outlive the handle) receives the layout above; the lengths and the split
+ * counters are zeroed on `stream` by a fill kernel; *out gets a new handle.
  * Errors: INVALID_ARG (null cfg / mask / out, B < 1, Hkv < 1, Hq % Hkv != 0,
  * sink < 0, recent < 1, max_len < 1, misaligned dev_buf, scale < 0 or not
  * finite), UNSUPPORTED (head_dim, batch), BUFFER_TOO_SMALL, HIP. */

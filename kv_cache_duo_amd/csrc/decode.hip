@@ -43,15 +43,101 @@ struct DecodeArgs {
   const uint16_t* v;
   uint16_t* out;      // [B][Hq][D]
   int32_t split_tokens, splits_r, splits_s;
+  int32_t inline_merge;  // 1: last work-group of a unit merges; 0: merge_kernel does
 };
 
+// Agent-coherent (cross-XCD) accesses without fences: on gfx950 relaxed
+// atomics at agent scope are plain loads/stores with the sc1 bit, which
+// bypass the non-coherent cache levels.  Only fences at agent scope write
+// back / invalidate a whole L2, which would cost far more than the merge.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float max_or_zero(float m) { return m == -INFINITY ? 0.f : m; }
+
+__device__ __forceinline__ uint4 load_nt(const uint4* p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
 
 // Records of one unit (b, kv head, head chunk): o [max_splits][GC][D] fp32,
 // then (m, l) [max_splits][GC].
 template <int D, int GC>
 __device__ __forceinline__ float* unit_records(const Geom& g, int64_t pu) {
   return g.partials + pu * g.max_splits * GC * (D + 2);
+}
+
+// Merge every split record of one unit into its outputs (used by the last
+// work-group of the unit).  Records are read with agent-coherent loads.
+// lds must hold kMaxMergeRecords * 8 + kThreads * 16 + GC * 4 bytes.
+template <int D, int GC>
+__device__ void merge_unit(const Geom& g, const DecodeArgs& a, int b, int h0, int64_t pu, int ns, const float* rec_o,
+                           const float* rec_ml, char* lds) {
+  constexpr int E = GC * D;                    // outputs of the unit
+  constexpr int KL = E >= kThreads ? 1 : kThreads / E;  // records summed in parallel
+  constexpr int BATCH = 16;                    // loads in flight per thread
+  float2* st_ml = reinterpret_cast<float2*>(lds);                            // [ns * GC]
+  float* st_acc = reinterpret_cast<float*>(lds + kMaxMergeRecords * 8);      // [kThreads]
+  float* st_L = reinterpret_cast<float*>(lds + kMaxMergeRecords * 8 + kThreads * 4);  // [GC]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int nrec = ns * GC;
+  for (int i = threadIdx.x; i < nrec; i += kThreads)
+    st_ml[i] = make_float2(load_agent(rec_ml + 2 * i), load_agent(rec_ml + 2 * i + 1));
+  __syncthreads();
+  for (int gg = wave; gg < GC; gg += kWaves) {
+    float mx = -INFINITY;
+    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, st_ml[k * GC + gg].x);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mu = max_or_zero(mx);
+    float ls = 0.f;
+    for (int k = lane; k < ns; k += 64) {
+      const float2 ml = st_ml[k * GC + gg];
+      const float f = exp2_fast(ml.x - mu);
+      st_ml[k * GC + gg].x = f;
+      ls += ml.y * f;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
+    if (lane == 0) st_L[gg] = ls;
+  }
+  __syncthreads();
+  for (int e0 = 0; e0 < E; e0 += kThreads / KL) {
+    const int e = e0 + threadIdx.x % (kThreads / KL);
+    const int kl = threadIdx.x / (kThreads / KL);
+    const int gg = e / D;
+    float acc = 0.f;
+    if (e < E) {
+      for (int k0 = kl; k0 < ns; k0 += KL * BATCH) {
+        float v[BATCH];
+#pragma unroll
+        for (int u2 = 0; u2 < BATCH; ++u2) {
+          const int k = min(k0 + u2 * KL, ns - 1);
+          v[u2] = load_agent(rec_o + (int64_t)k * E + e);
+        }
+#pragma unroll
+        for (int u2 = 0; u2 < BATCH; ++u2) {
+          const int k = k0 + u2 * KL;
+          acc = fmaf(v[u2], k < ns ? st_ml[k * GC + gg].x : 0.f, acc);
+        }
+      }
+    }
+    if (KL > 1) {
+      st_acc[threadIdx.x] = acc;
+      __syncthreads();
+      if (kl == 0 && e < E) {
+        for (int j = 1; j < KL; ++j) acc += st_acc[j * (kThreads / KL) + threadIdx.x];
+      }
+      __syncthreads();
+    }
+    if (kl == 0 && e < E) a.out[((int64_t)b * g.Hq + h0 + gg) * D + e % D] = (uint16_t)f32_to_bf16_bits(acc / st_L[gg]);
+  }
 }
 
 template <int D, int GC>
@@ -62,7 +148,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // when more query heads per work-group need registers.
   constexpr int kInFlight = GC >= 4 ? 2 : 4;
   constexpr int ROWS_ITER = kWaves * RPW * kInFlight;
-  __shared__ float sm_o[kWaves][GC][D];
+  // the cross-wave partials [kWaves][GC][D] share LDS with the merge staging
+  // area of the last work-group
+  constexpr int kCombineBytes = kWaves * GC * D * 4;
+  constexpr int kMergeLds = kMaxMergeRecords * 8 + kThreads * 4 + GC * 4;
+  __shared__ __attribute__((aligned(16))) char sm_raw[kCombineBytes > kMergeLds ? kCombineBytes : kMergeLds];
+  float(*sm_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(sm_raw);
   __shared__ float sm_m[kWaves][GC];
   __shared__ float sm_l[kWaves][GC];
 
@@ -134,8 +225,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       const int row = min(row_of(base, j), r1 - 1);
       const uint16_t* pk = row == new_row ? nk : ck + (int64_t)row * D;
       const uint16_t* pv = row == new_row ? nv : cv + (int64_t)row * D;
-      kr[j] = reinterpret_cast<const uint4*>(pk)[c];
-      vr[j] = reinterpret_cast<const uint4*>(pv)[c];
+      kr[j] = load_nt(reinterpret_cast<const uint4*>(pk) + c);  // streamed once: non-temporal
+      vr[j] = load_nt(reinterpret_cast<const uint4*>(pv) + c);
     }
   };
   auto process = [&](const uint4 (&kr)[kInFlight], const uint4 (&vr)[kInFlight], int base) {
@@ -256,27 +347,57 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     }
     if (ns == 1) {
       a.out[((int64_t)b * g.Hq + h0 + gg) * D + d] = (uint16_t)f32_to_bf16_bits(osum / lsum);
+    } else if (a.inline_merge) {
+      store_agent(&rec_o[((int64_t)split * GC + gg) * D + d], osum);
+      if (d == 0) {
+        store_agent(&rec_ml[split * GC + gg].x, mw);
+        store_agent(&rec_ml[split * GC + gg].y, lsum);
+      }
     } else {
       rec_o[((int64_t)split * GC + gg) * D + d] = osum;
       if (d == 0) rec_ml[split * GC + gg] = make_float2(mw, lsum);
     }
   }
+  if (ns == 1 || !a.inline_merge) return;
+
+  // ---- the last work-group of the unit to finish merges every split.
+  // Each thread's record stores are complete (at the agent-coherent level)
+  // before the barrier; then one ticket increment per work-group.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __shared__ int sm_last;
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(&g.tickets[pu], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_last = prev == (uint32_t)(ns - 1);
+  }
+  __syncthreads();
+  if (!sm_last) return;
+  merge_unit<D, GC>(g, a, b, h0, pu, ns, rec_o, reinterpret_cast<const float*>(rec_ml), sm_raw);
+  if (threadIdx.x == 0) __hip_atomic_store(&g.tickets[pu], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One work-group per (b, kv head, head chunk) whose rows were split.
+// Merge of the split records: one work-group per (b, kv head, head chunk,
+// query head of the chunk, 32-wide slice of D).  Every thread issues all its
+// record loads before using them, so the merge costs about one memory round
+// trip.
+constexpr int kMergeSlice = 32;
 template <int D, int GC>
 __global__ __launch_bounds__(kThreads) void merge_kernel(Geom g, Seqs sq, DecodeArgs a) {
-  constexpr int CPR = GC * D / 4;             // float4 chunks of one record's o
-  constexpr int KL = kThreads / CPR;          // records summed in parallel
-  static_assert(CPR <= kThreads && kThreads % CPR == 0, "merge mapping");
+  constexpr int SLICES = D / kMergeSlice;
+  constexpr int CPS = kMergeSlice / 4;        // float4 chunks per slice
+  constexpr int KL = kThreads / CPS;          // records summed in parallel
   __shared__ float2 st_ml[kMaxMergeRecords];  // (m, then f = 2^(m-M); l)
   __shared__ float4 st_acc[kThreads];
-  __shared__ float st_L[GC];
+  __shared__ float st_red[2][kWaves];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int n_hc = g.G / GC;
-  const int pu = blockIdx.x;
+  int id = blockIdx.x;
+  const int slice = id % SLICES;
+  id /= SLICES;
+  const int gg = id % GC;
+  const int pu = id / GC;
   const int hc = pu % n_hc;
   const int kvh = (pu / n_hc) % g.Hkv;
   const int b = pu / (n_hc * g.Hkv);
@@ -284,73 +405,71 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(Geom g, Seqs sq, Decode
   const int T = g.is_retrieval[kvh] ? L + 1 : min(L + 1, g.slots);
   const int ns = (T + a.split_tokens - 1) / a.split_tokens;
   if (ns <= 1) return;
-  const int h0 = kvh * g.G + hc * GC;
   const float* rec_o = unit_records<D, GC>(g, pu);
   const float2* rec_ml = reinterpret_cast<const float2*>(rec_o + (int64_t)g.max_splits * GC * D);
-  const int nrec = ns * GC;  // <= kMaxMergeRecords by the split planning
 
-  // 1. stage every (m, l) pair
-  for (int i = threadIdx.x; i < nrec; i += kThreads) st_ml[i] = rec_ml[i];
-  __syncthreads();
-  // 2. per head: M = max m_k, f_k = 2^(m_k - M), L = sum l_k f_k
-  for (int gg = wave; gg < GC; gg += kWaves) {
-    float mx = -INFINITY;
-    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, st_ml[k * GC + gg].x);
+  // 1. stage this head's (m, l) pairs; block max M
+  float mx = -INFINITY;
+  for (int k = threadIdx.x; k < ns; k += kThreads) {
+    const float2 ml = rec_ml[k * GC + gg];
+    st_ml[k] = ml;
+    mx = fmaxf(mx, ml.x);
+  }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    const float mu = max_or_zero(mx);
-    float ls = 0.f;
-    for (int k = lane; k < ns; k += 64) {
-      const float2 ml = st_ml[k * GC + gg];
-      const float f = exp2_fast(ml.x - mu);
-      st_ml[k * GC + gg].x = f;
-      ls += ml.y * f;
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) st_red[0][wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(st_red[0][0], st_red[0][1]), fmaxf(st_red[0][2], st_red[0][3]));
+  const float mu = max_or_zero(mx);
+  // 2. f_k = 2^(m_k - M), L = sum l_k f_k
+  float ls = 0.f;
+  for (int k = threadIdx.x; k < ns; k += kThreads) {
+    const float2 ml = st_ml[k];
+    const float f = exp2_fast(ml.x - mu);
+    st_ml[k].x = f;
+    ls += ml.y * f;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
+  if (lane == 0) st_red[1][wave] = ls;
+  __syncthreads();
+  // 3. O slice = sum_k f_k o_k, 8 record loads in flight per thread
+  const int cc = threadIdx.x % CPS;
+  const int kl = threadIdx.x / CPS;
+  const float4* src = reinterpret_cast<const float4*>(rec_o + (int64_t)gg * D + slice * kMergeSlice) + cc;
+  constexpr int REC4 = GC * D / 4;  // float4 stride between records
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k0 = kl; k0 < ns; k0 += KL * 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u2 = 0; u2 < 8; ++u2) {
+      const int k = min(k0 + u2 * KL, ns - 1);
+      v[u2] = src[(int64_t)k * REC4];
     }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
-    if (lane == 0) st_L[gg] = ls;
-  }
-  __syncthreads();
-  // 3. O = sum_k f_k o_k: KL records at a time, 8 loads in flight per thread
-  {
-    const int cc = threadIdx.x % CPR;
-    const int kl = threadIdx.x / CPR;
-    const int gg = (cc * 4) / D;
-    const float4* src = reinterpret_cast<const float4*>(rec_o);
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k0 = kl; k0 < ns; k0 += KL * 8) {
-      float4 v[8];
-#pragma unroll
-      for (int u2 = 0; u2 < 8; ++u2) {
-        const int k = k0 + u2 * KL;
-        v[u2] = k < ns ? src[(int64_t)k * CPR + cc] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int u2 = 0; u2 < 8; ++u2) {
-        const int k = k0 + u2 * KL;
-        const float f = k < ns ? st_ml[k * GC + gg].x : 0.f;
-        acc.x = fmaf(v[u2].x, f, acc.x);
-        acc.y = fmaf(v[u2].y, f, acc.y);
-        acc.z = fmaf(v[u2].z, f, acc.z);
-        acc.w = fmaf(v[u2].w, f, acc.w);
-      }
+    for (int u2 = 0; u2 < 8; ++u2) {
+      const int k = k0 + u2 * KL;
+      const float f = k < ns ? st_ml[k].x : 0.f;
+      acc.x = fmaf(v[u2].x, f, acc.x);
+      acc.y = fmaf(v[u2].y, f, acc.y);
+      acc.z = fmaf(v[u2].z, f, acc.z);
+      acc.w = fmaf(v[u2].w, f, acc.w);
     }
-    st_acc[threadIdx.x] = acc;
   }
+  st_acc[threadIdx.x] = acc;
   __syncthreads();
-  if (threadIdx.x < CPR) {
-    const int cc = threadIdx.x;
-    const int gg = (cc * 4) / D;
-    float4 s4 = st_acc[cc];
-    for (int kl = 1; kl < KL; ++kl) {
-      const float4 x = st_acc[kl * CPR + cc];
+  if (threadIdx.x < CPS) {
+    float4 s4 = st_acc[threadIdx.x];
+    for (int j = 1; j < KL; ++j) {
+      const float4 x = st_acc[j * CPS + threadIdx.x];
       s4.x += x.x; s4.y += x.y; s4.z += x.z; s4.w += x.w;
     }
-    const float inv = 1.0f / st_L[gg];
-    const uint32_t w0 = pack_bf16x2(s4.x * inv, s4.y * inv);
-    const uint32_t w1 = pack_bf16x2(s4.z * inv, s4.w * inv);
-    const int d0 = (cc * 4) % D;
-    *reinterpret_cast<uint2*>(a.out + ((int64_t)b * g.Hq + h0 + gg) * D + d0) = make_uint2(w0, w1);
+    const float lsum = st_red[1][0] + st_red[1][1] + st_red[1][2] + st_red[1][3];
+    const float inv = 1.0f / lsum;
+    const int h = kvh * g.G + hc * GC + gg;
+    const int d0 = slice * kMergeSlice + threadIdx.x * 4;
+    *reinterpret_cast<uint2*>(a.out + ((int64_t)b * g.Hq + h) * D + d0) =
+        make_uint2(pack_bf16x2(s4.x * inv, s4.y * inv), pack_bf16x2(s4.z * inv, s4.w * inv));
   }
 }
 
@@ -392,16 +511,23 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
 
 hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p, const uint16_t* qin,
                          const uint16_t* kin, const uint16_t* vin, uint16_t* out, hipStream_t s) {
-  DecodeArgs a{qin, kin, vin, out, p.split_tokens, p.splits_r, p.splits_s};
+  // Split merge: a separate launch by default (measured faster on the 32K
+  // MHA layer); DUO_DECODE_MERGE=inline lets the last work-group of each unit
+  // merge instead (one launch, a longer tail).
+  static const int inline_merge = [] {
+    const char* e = getenv("DUO_DECODE_MERGE");
+    return (e && e[0] == 'i') ? 1 : 0;
+  }();
+  DecodeArgs a{qin, kin, vin, out, p.split_tokens, p.splits_r, p.splits_s, inline_merge};
   const int n_hc = g.G / p.head_chunk;
   const int64_t items = (int64_t)g.B * g.nR * n_hc * p.splits_r + (int64_t)g.B * g.nS * n_hc * p.splits_s;
   if (items <= 0) return hipSuccess;
   const bool split = p.splits_r > 1 || p.splits_s > 1;
-  const dim3 grid((unsigned)items), block(kThreads), mgrid((unsigned)(g.B * g.Hkv * n_hc));
+  const dim3 grid((unsigned)items), block(kThreads), mgrid((unsigned)(g.B * g.Hkv * n_hc * p.head_chunk * (g.D / kMergeSlice)));
 #define DUO_DECODE_CASE(DD, GG)                                                        \
   if (g.D == DD && p.head_chunk == GG) {                                               \
     hipLaunchKernelGGL((decode_kernel<DD, GG>), grid, block, 0, s, g, q, a);           \
-    if (split) hipLaunchKernelGGL((merge_kernel<DD, GG>), mgrid, block, 0, s, g, q, a); \
+    if (split && !inline_merge) hipLaunchKernelGGL((merge_kernel<DD, GG>), mgrid, block, 0, s, g, q, a); \
     return hipGetLastError();                                                          \
   }
   DUO_DECODE_CASE(128, 1)

@@ -77,7 +77,8 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   int64_t off = 0;
   L->lengths_offset = off;
   off = align_up(off + 4 * (int64_t)g->B);
-  L->work_offset = off;
+  L->work_offset = off;  // merge tickets, then the split records
+  off = align_up(off + 4 * units);
   off = align_up(off + 4 * units * g->max_splits * gc * (g->D + 2));
   L->work_bytes = off - L->work_offset;
   const int64_t row = 2 * (int64_t)g->D;
@@ -97,8 +98,10 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
 
 void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   char* base = static_cast<char*>(buf);
+  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / duo::decode_head_chunk(g->G));
   g->lengths = reinterpret_cast<int32_t*>(base + L.lengths_offset);
-  g->partials = reinterpret_cast<float*>(base + L.work_offset);
+  g->tickets = reinterpret_cast<uint32_t*>(base + L.work_offset);
+  g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units));
   g->rk = reinterpret_cast<uint16_t*>(base + L.rk_offset);
   g->rv = reinterpret_cast<uint16_t*>(base + L.rv_offset);
   g->sk = reinterpret_cast<uint16_t*>(base + L.sk_offset);
@@ -130,7 +133,9 @@ duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int6
   if (lengths != nullptr)
     for (int b = 0; b < cfg->batch; ++b) h->len[b] = lengths[b];
   if (zero) {
-    hipError_t e = duo::launch_zero_words(reinterpret_cast<uint32_t*>(h->geom.lengths), cfg->batch,
+    // lengths, then the merge tickets (contiguous up to the split records)
+    const int64_t words = (reinterpret_cast<char*>(h->geom.partials) - reinterpret_cast<char*>(h->geom.lengths)) / 4;
+    hipError_t e = duo::launch_zero_words(reinterpret_cast<uint32_t*>(h->geom.lengths), words,
                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
       delete h;

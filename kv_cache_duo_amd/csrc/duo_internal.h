@@ -24,6 +24,7 @@ struct Geom {
   uint16_t* sv;
   int32_t* lengths;           // [B]
   float* partials;            // split-K records, see decode.hip
+  uint32_t* tickets;          // [B][Hkv][head chunks] split counters (zero between calls)
   int32_t max_splits;         // capacity of the partial records per unit
   // unit u < nR is retrieval KV head kv_of_unit[u]; unit nR+s is streaming
   // KV head kv_of_unit[nR+s]; index_of_kv[k] is k's index within its kind.

@@ -115,7 +115,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   char* const smem = prefill_smem;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int col = lane & 31;   // query row of a 32-row block held by this lane
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group
 
@@ -209,20 +209,50 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     if (!ok) off = in_base;  // chunk row 0 of this head: always readable
     return ok;
   };
+  // Per-lane element offsets of this lane's rows inside a tile, for a tile
+  // that lies wholly in the chunk input (row stride Hkv*D) or wholly in the
+  // retrieval cache (row stride D); such tiles need one uniform base each.
+  // K: the lane's j-th direct load covers row r0k + j*KROWS_J with the same
+  // swizzled chunk for every j; V: rows rgV*RPT + i.
+  constexpr int KROWS_J = kWaves * 64 / CH;  // tile rows between a lane's K loads
+  const int r0k = (wave * 64 + lane) / CH;
+  const int lck = ((wave * 64 + lane) % CH) ^ (r0k & (CH - 1));
+  const int koff_in = r0k * (int)in_stride + lck * 8, koff_c = r0k * D + lck * 8;
+  const int voff_in = rgV * RPT * (int)in_stride + chV * 8, voff_c = rgV * RPT * D + chV * 8;
   auto load_tile = [&](int tile, int buf) {
+    const int k0 = tile * kBN;
+    const bool all_in = k0 >= L && k0 + kBN - 1 <= qmax;           // every row in the chunk
+    const bool all_cache = retrieval && k0 + kBN - 1 < L;          // every row cached
+    if (all_in || all_cache) {
+      const int64_t stride = all_in ? in_stride : D;
+      const uint16_t* kbase = (all_in ? a.k + in_base + (int64_t)(k0 - L) * in_stride : ck + (int64_t)k0 * D) +
+                              (all_in ? koff_in : koff_c);
+      const uint16_t* vbase = (all_in ? a.v + in_base + (int64_t)(k0 - L) * in_stride : cv + (int64_t)k0 * D) +
+                              (all_in ? voff_in : voff_c);
+#pragma unroll
+      for (int j = 0; j < RPT; ++j)
+        global_to_lds16(kbase + j * KROWS_J * stride, buf * LD::BUF + (j * kWaves + wave) * 1024);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        vok[i] = true;
+        vbuf[i] = *reinterpret_cast<const uint4*>(vbase + i * stride);
+      }
+      return;
+    }
+    // general tile: any mix of cache rows, ring slots, chunk rows, unusable rows
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
       const int p = (j * kWaves + wave) * 64 + lane;  // 16-byte chunk index in the tile
       const int r = p / CH;
       const int lc = (p % CH) ^ (r & (CH - 1));
-      const int kp = tile * kBN + r;
+      const int kp = k0 + r;
       int64_t off;
       bool from_cache;
       row_src(kp, retrieval || kp < g.S ? 0 : ring_slot(kp), off, from_cache);
       const uint16_t* src = (from_cache ? ck : a.k) + off + lc * 8;
       global_to_lds16(src, buf * LD::BUF + (j * kWaves + wave) * 1024);
     }
-    const int kp0 = tile * kBN + rgV * RPT;
+    const int kp0 = k0 + rgV * RPT;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       const int kp = kp0 + i;
