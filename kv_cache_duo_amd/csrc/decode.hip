@@ -72,32 +72,52 @@ __device__ __forceinline__ float* unit_records(const Geom& g, int64_t pu) {
   return g.partials + pu * g.max_splits * GC * (D + 2);
 }
 
-// Merge every split record of one unit into its outputs (used by the last
-// work-group of the unit).  Records are read with agent-coherent loads.
-// lds must hold kMaxMergeRecords * 8 + kThreads * 16 + GC * 4 bytes.
+// Merge `cnt` records of one unit (slots first, first+step, ...) with
+// agent-coherent loads, into either the outputs or the record slot `first`
+// (o relative to the new max M, with m = M and l = sum).  All threads of the
+// work-group call it.  lds must hold kMergeLdsBytes.
+constexpr int kMergeBatch = 16;  // record loads in flight per thread
+template <int GC>
+constexpr int merge_lds_bytes() { return kMaxMergeRecords * 8 + kThreads * 4 + 2 * GC * 4; }
+
 template <int D, int GC>
-__device__ void merge_unit(const Geom& g, const DecodeArgs& a, int b, int h0, int64_t pu, int ns, const float* rec_o,
-                           const float* rec_ml, char* lds) {
-  constexpr int E = GC * D;                    // outputs of the unit
-  constexpr int KL = E >= kThreads ? 1 : kThreads / E;  // records summed in parallel
-  constexpr int BATCH = 16;                    // loads in flight per thread
-  float2* st_ml = reinterpret_cast<float2*>(lds);                            // [ns * GC]
-  float* st_acc = reinterpret_cast<float*>(lds + kMaxMergeRecords * 8);      // [kThreads]
-  float* st_L = reinterpret_cast<float*>(lds + kMaxMergeRecords * 8 + kThreads * 4);  // [GC]
+__device__ void merge_records(const Geom& g, const DecodeArgs& a, char* lds, float* rec_o, float* rec_ml, int first,
+                              int step, int cnt, bool to_output, int b, int h0) {
+  constexpr int E = GC * D;                               // outputs of the unit
+  constexpr int KL = E >= kThreads ? 1 : kThreads / E;    // records summed in parallel
+  constexpr int EB = kThreads / KL;                       // outputs per pass
+  float2* st_ml = reinterpret_cast<float2*>(lds);                              // [cnt * GC]
+  float* st_acc = reinterpret_cast<float*>(lds + kMaxMergeRecords * 8);        // [kThreads]
+  float* st_M = st_acc + kThreads;                                             // [GC]
+  float* st_L = st_M + GC;                                                     // [GC]
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int nrec = ns * GC;
-  for (int i = threadIdx.x; i < nrec; i += kThreads)
-    st_ml[i] = make_float2(load_agent(rec_ml + 2 * i), load_agent(rec_ml + 2 * i + 1));
+  // The first batch of o loads goes out together with the (m, l) loads, so
+  // a merge of up to KL * kMergeBatch records costs one memory round trip.
+  float v0[kMergeBatch];
+  {
+    const int e = threadIdx.x % EB;
+    const int kl = threadIdx.x / EB;
+#pragma unroll
+    for (int u2 = 0; u2 < kMergeBatch; ++u2) {
+      const int k = min(kl + u2 * KL, cnt - 1);
+      v0[u2] = load_agent(rec_o + (int64_t)(first + k * step) * E + e);
+    }
+  }
+  for (int i = threadIdx.x; i < cnt * GC; i += kThreads) {
+    const int s = first + (i / GC) * step;
+    const float* ml = rec_ml + 2 * ((int64_t)s * GC + i % GC);
+    st_ml[i] = make_float2(load_agent(ml), load_agent(ml + 1));
+  }
   __syncthreads();
   for (int gg = wave; gg < GC; gg += kWaves) {
     float mx = -INFINITY;
-    for (int k = lane; k < ns; k += 64) mx = fmaxf(mx, st_ml[k * GC + gg].x);
+    for (int k = lane; k < cnt; k += 64) mx = fmaxf(mx, st_ml[k * GC + gg].x);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
     const float mu = max_or_zero(mx);
     float ls = 0.f;
-    for (int k = lane; k < ns; k += 64) {
+    for (int k = lane; k < cnt; k += 64) {
       const float2 ml = st_ml[k * GC + gg];
       const float f = exp2_fast(ml.x - mu);
       st_ml[k * GC + gg].x = f;
@@ -105,38 +125,53 @@ __device__ void merge_unit(const Geom& g, const DecodeArgs& a, int b, int h0, in
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
-    if (lane == 0) st_L[gg] = ls;
+    if (lane == 0) {
+      st_M[gg] = mx;
+      st_L[gg] = ls;
+    }
   }
   __syncthreads();
-  for (int e0 = 0; e0 < E; e0 += kThreads / KL) {
-    const int e = e0 + threadIdx.x % (kThreads / KL);
-    const int kl = threadIdx.x / (kThreads / KL);
+  for (int e0 = 0; e0 < E; e0 += EB) {
+    const int e = e0 + threadIdx.x % EB;
+    const int kl = threadIdx.x / EB;
     const int gg = e / D;
     float acc = 0.f;
-    if (e < E) {
-      for (int k0 = kl; k0 < ns; k0 += KL * BATCH) {
-        float v[BATCH];
+    for (int k0 = kl; k0 < cnt; k0 += KL * kMergeBatch) {
+      float v[kMergeBatch];
+      if (e0 == 0 && k0 == kl) {
 #pragma unroll
-        for (int u2 = 0; u2 < BATCH; ++u2) {
-          const int k = min(k0 + u2 * KL, ns - 1);
-          v[u2] = load_agent(rec_o + (int64_t)k * E + e);
-        }
+        for (int u2 = 0; u2 < kMergeBatch; ++u2) v[u2] = v0[u2];
+      } else {
 #pragma unroll
-        for (int u2 = 0; u2 < BATCH; ++u2) {
-          const int k = k0 + u2 * KL;
-          acc = fmaf(v[u2], k < ns ? st_ml[k * GC + gg].x : 0.f, acc);
+        for (int u2 = 0; u2 < kMergeBatch; ++u2) {
+          const int k = min(k0 + u2 * KL, cnt - 1);
+          v[u2] = load_agent(rec_o + (int64_t)(first + k * step) * E + e);
         }
+      }
+#pragma unroll
+      for (int u2 = 0; u2 < kMergeBatch; ++u2) {
+        const int k = k0 + u2 * KL;
+        acc = fmaf(v[u2], k < cnt ? st_ml[k * GC + gg].x : 0.f, acc);
       }
     }
     if (KL > 1) {
       st_acc[threadIdx.x] = acc;
       __syncthreads();
-      if (kl == 0 && e < E) {
-        for (int j = 1; j < KL; ++j) acc += st_acc[j * (kThreads / KL) + threadIdx.x];
-      }
-      __syncthreads();
+      if (kl == 0)
+        for (int j = 1; j < KL; ++j) acc += st_acc[j * EB + threadIdx.x];
     }
-    if (kl == 0 && e < E) a.out[((int64_t)b * g.Hq + h0 + gg) * D + e % D] = (uint16_t)f32_to_bf16_bits(acc / st_L[gg]);
+    if (kl == 0) {
+      if (to_output) {
+        a.out[((int64_t)b * g.Hq + h0 + gg) * D + e % D] = (uint16_t)f32_to_bf16_bits(acc / st_L[gg]);
+      } else {
+        store_agent(rec_o + (int64_t)first * E + e, acc);
+        if (e % D == 0) {
+          store_agent(rec_ml + 2 * ((int64_t)first * GC + gg), st_M[gg]);
+          store_agent(rec_ml + 2 * ((int64_t)first * GC + gg) + 1, st_L[gg]);
+        }
+      }
+    }
+    if (KL > 1) __syncthreads();
   }
 }
 
@@ -151,7 +186,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // the cross-wave partials [kWaves][GC][D] share LDS with the merge staging
   // area of the last work-group
   constexpr int kCombineBytes = kWaves * GC * D * 4;
-  constexpr int kMergeLds = kMaxMergeRecords * 8 + kThreads * 4 + GC * 4;
+  constexpr int kMergeLds = merge_lds_bytes<GC>();
   __shared__ __attribute__((aligned(16))) char sm_raw[kCombineBytes > kMergeLds ? kCombineBytes : kMergeLds];
   float(*sm_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(sm_raw);
   __shared__ float sm_m[kWaves][GC];
@@ -360,20 +395,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   }
   if (ns == 1 || !a.inline_merge) return;
 
-  // ---- the last work-group of the unit to finish merges every split.
-  // Each thread's record stores are complete (at the agent-coherent level)
-  // before the barrier; then one ticket increment per work-group.
+  // ---- merge in two levels.  The last work-group to finish in a group of
+  // kMergeGroup splits merges the group into the group's first slot; the
+  // last group to finish merges the groups.  Each work-group's record stores
+  // are complete (at the agent-coherent level) before its ticket increment.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  __shared__ int sm_last;
+  __shared__ int sm_flag;
+  const int mgrp = split / kMergeGroup;
+  const int ng = (ns + kMergeGroup - 1) / kMergeGroup;
+  const int g0 = mgrp * kMergeGroup;
+  const int gsz = min(kMergeGroup, ns - g0);
+  uint32_t* t_unit = g.tickets + pu * g.tickets_per_unit;  // [0]: groups done, [1 + mgrp]: splits done
   if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(&g.tickets[pu], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_last = prev == (uint32_t)(ns - 1);
+    const uint32_t prev = __hip_atomic_fetch_add(t_unit + 1 + mgrp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_flag = prev == (uint32_t)(gsz - 1);
   }
   __syncthreads();
-  if (!sm_last) return;
-  merge_unit<D, GC>(g, a, b, h0, pu, ns, rec_o, reinterpret_cast<const float*>(rec_ml), sm_raw);
-  if (threadIdx.x == 0) __hip_atomic_store(&g.tickets[pu], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!sm_flag) return;
+  if (threadIdx.x == 0) __hip_atomic_store(t_unit + 1 + mgrp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float* rml = reinterpret_cast<float*>(rec_ml);
+  merge_records<D, GC>(g, a, sm_raw, rec_o, rml, g0, 1, gsz, ng == 1, b, h0);
+  if (ng == 1) return;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = __hip_atomic_fetch_add(t_unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sm_flag = prev == (uint32_t)(ng - 1);
+  }
+  __syncthreads();
+  if (!sm_flag) return;
+  if (threadIdx.x == 0) __hip_atomic_store(t_unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  merge_records<D, GC>(g, a, sm_raw, rec_o, rml, 0, kMergeGroup, ng, true, b, h0);
 }
 
 // Merge of the split records: one work-group per (b, kv head, head chunk,
@@ -511,12 +564,11 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
 
 hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p, const uint16_t* qin,
                          const uint16_t* kin, const uint16_t* vin, uint16_t* out, hipStream_t s) {
-  // Split merge: a separate launch by default (measured faster on the 32K
-  // MHA layer); DUO_DECODE_MERGE=inline lets the last work-group of each unit
-  // merge instead (one launch, a longer tail).
+  // Split merge inside the decode launch by default; DUO_DECODE_MERGE=kernel
+  // selects a separate merge launch instead.
   static const int inline_merge = [] {
     const char* e = getenv("DUO_DECODE_MERGE");
-    return (e && e[0] == 'i') ? 1 : 0;
+    return (e && e[0] == 'k') ? 0 : 1;
   }();
   DecodeArgs a{qin, kin, vin, out, p.split_tokens, p.splits_r, p.splits_s, inline_merge};
   const int n_hc = g.G / p.head_chunk;

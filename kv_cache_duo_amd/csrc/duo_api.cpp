@@ -78,7 +78,8 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   L->lengths_offset = off;
   off = align_up(off + 4 * (int64_t)g->B);
   L->work_offset = off;  // merge tickets, then the split records
-  off = align_up(off + 4 * units);
+  g->tickets_per_unit = duo::tickets_per_unit(g->max_splits);
+  off = align_up(off + 4 * units * g->tickets_per_unit);
   off = align_up(off + 4 * units * g->max_splits * gc * (g->D + 2));
   L->work_bytes = off - L->work_offset;
   const int64_t row = 2 * (int64_t)g->D;
@@ -101,7 +102,7 @@ void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   const int64_t units = (int64_t)g->B * g->Hkv * (g->G / duo::decode_head_chunk(g->G));
   g->lengths = reinterpret_cast<int32_t*>(base + L.lengths_offset);
   g->tickets = reinterpret_cast<uint32_t*>(base + L.work_offset);
-  g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units));
+  g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units * g->tickets_per_unit));
   g->rk = reinterpret_cast<uint16_t*>(base + L.rk_offset);
   g->rv = reinterpret_cast<uint16_t*>(base + L.rv_offset);
   g->sk = reinterpret_cast<uint16_t*>(base + L.sk_offset);

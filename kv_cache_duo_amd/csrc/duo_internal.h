@@ -24,7 +24,8 @@ struct Geom {
   uint16_t* sv;
   int32_t* lengths;           // [B]
   float* partials;            // split-K records, see decode.hip
-  uint32_t* tickets;          // [B][Hkv][head chunks] split counters (zero between calls)
+  uint32_t* tickets;          // [units][tickets_per_unit] split counters (zero between calls)
+  int32_t tickets_per_unit;   // 1 + groups of kMergeGroup splits
   int32_t max_splits;         // capacity of the partial records per unit
   // unit u < nR is retrieval KV head kv_of_unit[u]; unit nR+s is streaming
   // KV head kv_of_unit[nR+s]; index_of_kv[k] is k's index within its kind.
@@ -66,6 +67,10 @@ inline int decode_head_chunk(int G) {
     if (G % c == 0) return c;
   return 1;
 }
+
+// Decode splits are merged in groups of this many records, then the groups.
+constexpr int kMergeGroup = 16;
+inline int32_t tickets_per_unit(int32_t max_splits) { return 1 + (max_splits + kMergeGroup - 1) / kMergeGroup; }
 
 // Split-K record capacity per (sequence, KV head, head chunk): enough for
 // splits of >= 256 rows, and at most 1024 / head_chunk records so that the
