@@ -9,8 +9,10 @@ bandwidth is HBM bandwidth):
 Inputs are resident in HBM before the timed region.  Reported:
   value      decode attention, algorithmic HBM bytes / decode-phase wall time
   prefill    algorithmic flops / prefill-phase wall time
-  roofline   decode kernel: algorithmic bytes per launch / mean launch time
-             (HIP events on the launch stream), against 8 TB/s
+  roofline   decode kernel: algorithmic bytes per launch / mean launch time,
+             against 8 TB/s; one decode call is one kernel launch, and the
+             mean launch time is the decode phase (HIP events on the launch
+             stream) divided by the number of launches
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode work
 Algorithmic counts: each K/V byte once per (sequence, KV head) plus q, out
 and the appended token; flops = 4*D per allowed (query, key) pair per query
@@ -29,6 +31,44 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def source_digest(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode launch from the committed rocprofv3 counter
+    record, or None when the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    src = os.path.join(ROOT, "kv_cache_duo_amd", "csrc", "decode.hip")
+    if rec.get("decode_hip_sha256_16") != source_digest(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def measured_ceilings(decode_mib: int):
+    """Streaming-read (one launch of the decode call's size, and 4 GiB) and
+    bf16 MFMA-loop ceilings from kv_cache_duo_amd/ceiling, run as a child."""
+    import subprocess
+    exe = os.path.join(ROOT, "kv_cache_duo_amd", "ceiling")
+    out = {}
+    for args in (["stream_read", str(decode_mib)], ["stream_read", "4096"], ["mfma"]):
+        r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=120)
+        if r.returncode != 0:
+            raise RuntimeError(f"{exe} {' '.join(args)} failed: {r.stderr}")
+        rec = json.loads(r.stdout.strip().splitlines()[-1])
+        key = rec["ceiling"] + ("_%dMiB" % rec["mib"] if "mib" in rec else "")
+        out[key] = {k: v for k, v in rec.items() if k != "ceiling"}
+    return out
 
 
 def parse():
@@ -39,13 +79,9 @@ def parse():
     p.add_argument("--workload", default="llama2_7b_mha_32k")
     p.add_argument("--layers", type=int, default=8)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-steps", type=int, default=4)
+    p.add_argument("--cpu-sample-steps", type=int, default=128)
+    p.add_argument("--no-ceilings", action="store_true")
     return p.parse_args()
-
-
-def allowed_count(t: int, retrieval: bool, sink: int, recent: int) -> int:
-    """Number of positions a query at t attends to (for the flop count)."""
-    return t + 1 if retrieval else min(t + 1, sink + recent)
 
 
 def prefill_flops(w, mask) -> float:
@@ -76,7 +112,6 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    import numpy as np
     import torch
 
     import kv_cache_duo_amd as duo
@@ -116,8 +151,6 @@ def main():
     od_p = ptr(outd)
     op_p = ptr(outp)
     n_dec = w.decode_steps * nl
-    ev_d = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dec)]
-    ev_p = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nl)]
     ph = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
 
     def check(st, where):
@@ -129,18 +162,12 @@ def main():
         hs = [c.handle for c in caches]
         ph[0].record(stream)
         for l in range(nl):
-            ev_p[l][0].record(stream)
             check(lib.duo_prefill(hs[l], ptr(pq[l]), ptr(pk[l]), ptr(pv[l]), n_new, w.prefill, op_p, sp),
                   "prefill")
-            ev_p[l][1].record(stream)
         ph[1].record(stream)
-        i = 0
         for s in range(w.decode_steps):
             for l in range(nl):
-                ev_d[i][0].record(stream)
                 check(lib.duo_decode(hs[l], dq_p[l][s], dk_p[l][s], dv_p[l][s], od_p, sp), "decode")
-                ev_d[i][1].record(stream)
-                i += 1
         ph[2].record(stream)
         return caches
 
@@ -150,8 +177,6 @@ def main():
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     pre_ms = dec_ms = 0.0
-    dec_launch_ms = []
-    pre_launch_ms = []
     t0.record(stream)
     wall0 = time.perf_counter()
     for _ in range(args.steps):
@@ -159,8 +184,6 @@ def main():
         torch.cuda.synchronize()
         pre_ms += ph[0].elapsed_time(ph[1])
         dec_ms += ph[1].elapsed_time(ph[2])
-        dec_launch_ms += [a.elapsed_time(b) for a, b in ev_d]
-        pre_launch_ms += [a.elapsed_time(b) for a, b in ev_p]
     t1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -172,10 +195,10 @@ def main():
     bytes_step = sum(decode_bytes(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
     dec_gbs = bytes_step * args.steps / (dec_ms * 1e-3) / 1e9
     pre_tflops = flops_step * args.steps / (pre_ms * 1e-3) / 1e12
-    mean_dec_launch = sum(dec_launch_ms) / len(dec_launch_ms)
+    mean_dec_launch = dec_ms / (args.steps * n_dec)  # ms per decode launch
     bytes_per_launch = bytes_step / n_dec
     achieved = bytes_per_launch / (mean_dec_launch * 1e-3) / 1e9
-    mean_pre_launch = sum(pre_launch_ms) / len(pre_launch_ms)
+    mean_pre_launch = pre_ms / (args.steps * nl)     # ms per prefill call (prefill + append kernels)
     pre_achieved = (flops_step / nl) / (mean_pre_launch * 1e-3) / 1e12
 
     result = {
@@ -204,16 +227,19 @@ def main():
                     "phase_ms_per_step": round(pre_ms / args.steps, 3),
                     "flops_per_step": flops_step},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel", "mean_launch_us": round(mean_dec_launch * 1e3, 3),
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
+                     "kernel": "decode_kernel (one launch per decode call)",
+                     "mean_launch_us": round(mean_dec_launch * 1e3, 3),
                      "bytes_per_launch": bytes_per_launch},
         "roofline_prefill": {"bound": "mfma", "achieved": round(pre_achieved, 1),
                              "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                              "frac": round(pre_achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                             "kernel": "prefill_kernel (+append)",
+                             "kernel": "prefill_kernel + append_kernel (one prefill call)",
                              "mean_launch_ms": round(mean_pre_launch, 4)},
         "wall_s": round(wall, 3),
     }
+    if not args.no_ceilings:
+        result["measured_ceilings"] = measured_ceilings(max(1, int(round(bytes_per_launch / 2**20))))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, masks[0], ins[0], args.cpu_sample_steps)
     print(json.dumps(result), flush=True)

@@ -19,6 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libduo.so")
+CEILING = os.path.join(HERE, "ceiling")  # measured HBM / MFMA ceilings (standalone)
 
 SOURCES = ["duo_api.cpp", "append.hip", "decode.hip", "prefill.hip"]
 
@@ -63,8 +64,13 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    cmd = [hipcc(), *COMMON, "-x", "hip", os.path.join(CSRC, "ceiling.hip"), "-o", CEILING + ".tmp"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for ceiling.hip:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(CEILING + ".tmp", CEILING)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {CEILING}")
     return LIB
 
 

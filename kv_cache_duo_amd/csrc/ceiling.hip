@@ -1,0 +1,123 @@
+// Measured hardware ceilings used as a second reference next to the vendor
+// peaks when the kernels' roofline fractions are reported:
+//   ceiling stream_read <MiB>  -- 16-byte streaming reads of a buffer (HBM)
+//   ceiling mfma               -- back-to-back v_mfma_f32_32x32x16_bf16
+// Standalone executable (not part of the C ABI); prints one JSON line.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr size_t kSlab = 4096;  // 16-byte elements per block (64 KB)
+
+// Each block reads one contiguous 64 KB slab, 4 loads in flight per thread.
+template <bool NT>
+__global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ p, unsigned* out) {
+  const size_t base = (size_t)blockIdx.x * kSlab;
+  unsigned acc = 0;
+  for (size_t i = threadIdx.x; i < kSlab; i += 256 * 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const size_t idx = base + i + (size_t)u * 256;
+      v[u] = NT ? __builtin_nontemporal_load(p + idx) : p[idx];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;  // keeps the loads; practically never true
+}
+
+// 4 independent accumulators per wave, `iters` rounds of 4 MFMAs each.
+__global__ __launch_bounds__(256) void mfma_loop(float* out, int iters) {
+  bf16x8 a, b;
+  for (int j = 0; j < 8; ++j) {
+    a[j] = (__bf16)(0.001f * (threadIdx.x + j));
+    b[j] = (__bf16)(0.002f * (threadIdx.x - j));
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; ++i) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  if (s == 1234.5f) out[blockIdx.x] = s;
+}
+
+bool ok(hipError_t e, const char* what) {
+  if (e != hipSuccess) fprintf(stderr, "%s: %s\n", what, hipGetErrorString(e));
+  return e == hipSuccess;
+}
+
+int run_stream_read(size_t mib) {
+  const size_t bytes = mib << 20;
+  const unsigned blocks = (unsigned)(bytes / 16 / kSlab);
+  if (blocks == 0) return 2;
+  u32x4* p = nullptr;
+  unsigned* out = nullptr;
+  if (!ok(hipMalloc(&p, (size_t)blocks * kSlab * 16), "hipMalloc") || !ok(hipMalloc(&out, blocks * 4), "hipMalloc"))
+    return 1;
+  if (!ok(hipMemset(p, 1, (size_t)blocks * kSlab * 16), "hipMemset")) return 1;
+  hipEvent_t a, b;
+  if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return 1;
+  const int reps = bytes < ((size_t)1 << 30) ? 50 : 5;
+  double gbs[2];
+  for (int nt = 0; nt < 2; ++nt) {
+    auto k = nt ? stream_read<true> : stream_read<false>;
+    for (int w = 0; w < 2; ++w) hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, 0, p, out);
+    (void)hipEventRecord(a, 0);
+    for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(k, dim3(blocks), dim3(256), 0, 0, p, out);
+    (void)hipEventRecord(b, 0);
+    if (!ok(hipEventSynchronize(b), "sync")) return 1;
+    float ms = 0.f;
+    (void)hipEventElapsedTime(&ms, a, b);
+    gbs[nt] = (double)reps * blocks * kSlab * 16 / (ms * 1e-3) / 1e9;
+  }
+  printf("{\"ceiling\": \"stream_read\", \"mib\": %zu, \"plain_gbs\": %.1f, \"nontemporal_gbs\": %.1f}\n", mib, gbs[0],
+         gbs[1]);
+  return 0;
+}
+
+int run_mfma() {
+  int dev = 0, cus = 0;
+  if (!ok(hipGetDevice(&dev), "device") ||
+      !ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "attr"))
+    return 1;
+  const unsigned blocks = (unsigned)cus * 8;  // 8 work-groups of 4 waves per CU
+  const int iters = 4096;
+  float* out = nullptr;
+  if (!ok(hipMalloc(&out, blocks * 4), "hipMalloc")) return 1;
+  hipEvent_t a, b;
+  if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return 1;
+  hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(256), 0, 0, out, iters);
+  (void)hipEventRecord(a, 0);
+  const int reps = 5;
+  for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(256), 0, 0, out, iters);
+  (void)hipEventRecord(b, 0);
+  if (!ok(hipEventSynchronize(b), "sync")) return 1;
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, a, b);
+  const double flop = (double)reps * blocks * 4 /*waves*/ * iters * 4 /*mfma*/ * 32768.0;
+  printf("{\"ceiling\": \"mfma_bf16_32x32x16\", \"cus\": %d, \"tflops\": %.1f}\n", cus, flop / (ms * 1e-3) / 1e12);
+  return 0;
+}
+
+}  // namespace
+
+int main(int argc, char** argv) {
+  if (argc >= 2 && std::strcmp(argv[1], "stream_read") == 0)
+    return run_stream_read(argc >= 3 ? (size_t)std::atoll(argv[2]) : 4096);
+  if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma();
+  fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling mfma\n");
+  return 2;
+}
