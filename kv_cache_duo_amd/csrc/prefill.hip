@@ -11,23 +11,27 @@
 // this kernel (streaming ring slots read here may be overwritten by it).
 //
 // Tile engine (flash-style online softmax, fp32 accumulation):
-//   * work-group = 4 waves; each wave owns QB blocks of 32 query rows of one
-//     query head; the work-group covers gh query heads of one KV group, so
-//     every K/V tile staged in LDS serves all of them;
-//   * K/V tiles of 64 keys are gathered row by row (any mix of cache rows,
-//     ring slots and chunk rows) with 16-byte loads into registers while the
-//     previous tile is computed, then stored to a double-buffered LDS: K as
-//     rows (padded to 272 B), V transposed (rows of 144 B) so that both MFMA
-//     operands are 16-byte LDS reads.  The V tile is loaded with the row
-//     group varying fastest across lanes, which makes the transposed stores
-//     bank-conflict free;
+//   * work-group = 4 waves; each wave owns 32 query rows of one query head;
+//     the work-group covers gh query heads of one KV group, so every K/V tile
+//     staged in LDS serves all of them;
+//   * K and V tiles of 64 keys go from global memory straight into a
+//     double-buffered LDS (global_load_lds_dwordx4, 1 KB per wave
+//     instruction) while the previous tile is computed; rows may be any mix
+//     of cache rows, ring slots and chunk rows.  Both tiles keep the natural
+//     [key][d] layout with the 16-byte granules of a row XOR-swizzled (K by
+//     row mod D/8, V by 2 * (row mod 4)), which keeps the operand reads below
+//     free of bank conflicts;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q
-//     held in registers): each lane holds 32 scores of ONE query, so row max
-//     and sum need in-lane work plus one exchange with lane^32.  Each K
-//     fragment read from LDS feeds QB MFMAs;
-//   * P (bf16) feeds O^T += V^T P^T straight from the S^T registers: the key
-//     order inside a 16-key MFMA step is permuted identically in P and in the
-//     transposed V tile, which is legal because keys are the contracted axis;
+//     in registers, pre-multiplied by scale * log2 e): each lane holds 32
+//     scores of ONE query, so row max and sum need in-lane work plus one
+//     exchange with lane^32.  The accumulator starts at minus the running
+//     max, so the MFMA output is already the exponent of the softmax term;
+//   * P (bf16) feeds O^T += V^T P^T straight from the S^T registers.  The
+//     V^T operand comes from ds_read_b64_tr_b16, which transposes 4x4 blocks
+//     of 16-bit elements across each 16-lane group; the key order of P inside
+//     a 16-key MFMA step (groups of 4 keys interleaved by lane half) is
+//     reproduced by the read addresses, legal because keys are the
+//     contracted axis;
 //   * the running max is only moved (and O, l rescaled) when a tile's max
 //     exceeds it by more than 2^8; the result is exact because l and O always
 //     share the same reference;
@@ -35,7 +39,7 @@
 //   * work-groups run longest query tile first, t-major and unit-minor.
 #include <hip/hip_runtime.h>
 
-#include <cstdlib>
+#include <type_traits>
 
 #include "device_util.h"
 #include "duo_internal.h"
@@ -45,10 +49,11 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
-constexpr int kBN = 64;             // keys per tile
+constexpr int kBN = 64;               // keys per tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: rescale when the max grows by > 2^8
 
 struct PrefillArgs {
@@ -66,57 +71,51 @@ struct PrefillArgs {
 
 template <int D>
 struct Lds {
-  static constexpr int KSTRIDE = D * 2;             // bytes per K row (XOR-swizzled chunks)
-  static constexpr int VSTRIDE = kBN * 2 + 16;      // bytes per V^T row (padded)
-  static constexpr int KBYTES = kBN * KSTRIDE;
-  static constexpr int VBYTES = D * VSTRIDE;
-  static constexpr int BUF = KBYTES + VBYTES;
-  static constexpr int TOTAL = 2 * BUF;
+  static constexpr int ROW = D * 2;       // bytes per K or V row
+  static constexpr int TILE = kBN * ROW;  // one K or V tile
+  static constexpr int BUF = 2 * TILE;    // K tile, then V tile
+  static constexpr int TOTAL = 2 * BUF;   // double buffered
 };
-
-// Position inside a 16-key block of the transposed V tile where key `kk`
-// (0..15) is stored: 4-key groups 1 and 2 swap places, matching the order in
-// which the S^T accumulator registers hold keys.
-__device__ __forceinline__ int vt_pos(int kk) {
-  const int b16 = kk >> 4, g4 = (kk >> 2) & 3;
-  const int sw = g4 == 1 ? 2 : (g4 == 2 ? 1 : g4);
-  return b16 * 16 + sw * 4 + (kk & 3);
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4& x, int i) {
-  return i == 0 ? x.x : (i == 1 ? x.y : (i == 2 ? x.z : x.w));
-}
 
 // Dynamic LDS of the prefill kernel (two K/V tile buffers).
 extern __shared__ __attribute__((aligned(16))) char prefill_smem[];
 
+// The helpers below wrap target builtins that take LDS pointers; they stay
+// out of the kernel template, whose host-side stub is otherwise not emitted.
+
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave
 // writes bytes [lds_off + 16 l, lds_off + 16 l + 16); lds_off is wave-uniform.
-// (Kept out of the kernel template: the host pass must not see the builtin
-// in a template body, or the kernel's host stub is not emitted.)
 __device__ __forceinline__ void global_to_lds16(const void* src, int lds_off) {
   __builtin_amdgcn_global_load_lds(src, prefill_smem + lds_off, 16, 0, 0);
 }
 
-__device__ __forceinline__ uint4 select4(bool ok, const uint4& x) {
-  return make_uint4(ok ? x.x : 0u, ok ? x.y : 0u, ok ? x.z : 0u, ok ? x.w : 0u);
+// ds_read_b64_tr_b16: every lane names 8 bytes (four 16-bit elements) of
+// LDS; inside each group of 16 lanes, lane i receives as element j the
+// element (i mod 4) of the 8 bytes named by lane 4 j + i / 4 of its group.
+__device__ __forceinline__ uint2 lds_read_tr16(int lds_off) {
+  typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(prefill_smem + lds_off));
+  return __builtin_bit_cast(uint2, r);
 }
 
-template <int D, int QB>
-__global__ __launch_bounds__(kThreads, QB == 1 ? 2 : 1)
+__device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
+  return pack_bf16x2(bf16_lo(w) * s, bf16_hi(w) * s);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2)
 void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   using LD = Lds<D>;
-  constexpr int CH = D / 8;                 // 16-byte chunks per row
-  constexpr int RPT = kBN * CH / kThreads;  // tile rows loaded per thread (4 or 2)
-  constexpr int RG = kBN / RPT;             // row groups per tile
+  constexpr int CH = D / 8;                 // 16-byte granules per row
+  constexpr int RPC = 64 / CH;              // rows per 1 KB wave load (4 or 8)
+  constexpr int ROWS_J = RPC * kWaves;      // tile rows between a lane's loads
+  constexpr int NJ = kBN / ROWS_J;          // wave loads per tile and operand (4 or 2)
   constexpr int QC = D / 16;                // MFMA k-steps of Q K^T
   constexpr int DB = D / 32;                // 32-wide column blocks of O
-  constexpr int ROWS_WAVE = 32 * QB;
-  char* const smem = prefill_smem;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
-  const int col = lane & 31;   // query row of a 32-row block held by this lane
+  const int col = lane & 31;   // query row of the 32-row block held by this lane
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group
 
   // ---- work item: t-major (longest tiles first), unit-minor
@@ -140,24 +139,20 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const uint16_t* ck = (retrieval ? g.rk : g.sk) + cache_off;
   const uint16_t* cv = (retrieval ? g.rv : g.sv) + cache_off;
   const int64_t in_base = ((int64_t)b * a.chunk * g.Hkv + kvh) * D;  // chunk row 0
-  const int64_t in_stride = (int64_t)g.Hkv * D;
+  const int in_stride = g.Hkv * D;
 
-  // query positions of the work-group and of this wave's blocks
-  const int i_lo = t * a.tq;                          // first chunk row
-  const int i_hi = min(i_lo + a.tq, n) - 1;           // last chunk row
+  // query positions of the work-group and of this wave's block
+  const int i_lo = t * a.tq;                 // first chunk row
+  const int i_hi = min(i_lo + a.tq, n) - 1;  // last chunk row
   const int qmin = L + i_lo, qmax = L + i_hi;
   const int waves_per_head = kWaves / a.gh;
   const int gg = wave / waves_per_head;
-  const int wi0 = i_lo + (wave % waves_per_head) * ROWS_WAVE;  // wave's first chunk row
+  const int wi0 = i_lo + (wave % waves_per_head) * 32;  // wave's first chunk row
   const int h = kvh * g.G + hc * a.gh + gg;
-  int blo[QB], bhi[QB], my_i[QB], my_q[QB];  // block position range (wave-uniform), lane row
-#pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    blo[qb] = L + wi0 + 32 * qb;
-    bhi[qb] = L + min(wi0 + 32 * qb + 32, n) - 1;  // < blo: block has no rows
-    my_i[qb] = wi0 + 32 * qb + col;
-    my_q[qb] = L + my_i[qb];
-  }
+  const int blo = L + wi0;                   // block position range (wave-uniform)
+  const int bhi = L + min(wi0 + 32, n) - 1;  // < blo: the block has no rows
+  const int my_i = wi0 + col;
+  const int my_q = L + my_i;
 
   // ---- key tiles: retrieval 0..qmax; streaming sinks + window
   int tA = 0, tB0 = 0, tB1 = qmax / kBN;  // tiles [0,tA) then [tB0,tB1]
@@ -173,257 +168,203 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int ntiles = tA + (tB1 - tB0 + 1);
   auto tile_of = [&](int k) { return k < tA ? k : tB0 + (k - tA); };
 
-  // ---- Q operand (B of S^T = K Q^T): lane holds row `col`, k slice `half`
-  bf16x8_t qreg[QB][QC];
+  // ---- Q operand (B of S^T = K Q^T), scaled by scale * log2 e: lane holds
+  // row `col`, k slice `half`
+  const float c2 = g.scale_log2;
+  bf16x8_t qreg[QC];
+  {
+    const bool ok = my_i <= i_hi;
+    const uint4* src = reinterpret_cast<const uint4*>(a.q + (((int64_t)b * a.chunk + (ok ? my_i : i_lo)) * g.Hq + h) * D);
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const bool ok = my_i[qb] <= i_hi;
-    const uint4* src = reinterpret_cast<const uint4*>(a.q + (((int64_t)b * a.chunk + (ok ? my_i[qb] : i_lo)) * g.Hq + h) * D);
-#pragma unroll
-    for (int c = 0; c < QC; ++c) qreg[qb][c] = __builtin_bit_cast(bf16x8_t, select4(ok, src[2 * c + half]));
+    for (int c = 0; c < QC; ++c) {
+      const uint4 x = src[2 * c + half];
+      const float s = ok ? c2 : 0.f;
+      qreg[c] = __builtin_bit_cast(bf16x8_t, make_uint4(scaled_pair(x.x, s), scaled_pair(x.y, s),
+                                                        scaled_pair(x.z, s), scaled_pair(x.w, s)));
+    }
   }
 
-  // ---- tile loader.
-  // K goes straight from global memory to LDS (global_load_lds_dwordx4): each
-  // wave instruction fills 1 KB of the tile, lane l the 16-byte chunk l of
-  // it.  Chunk c of row r is stored at chunk c ^ (r mod CH) of the row, which
-  // keeps the MFMA operand reads (32 rows, same chunk) bank-conflict free.
-  // Rows that no query of this work-group may use load an arbitrary valid
-  // row: their scores are always masked.
-  // V goes through registers, is zeroed where unusable, and is stored
-  // transposed; it is loaded with the row group varying fastest across
-  // lanes, which makes the transposed stores bank-conflict free.
-  const int rgV = threadIdx.x % RG, chV = threadIdx.x / RG;
-  uint4 vbuf[RPT];
-  bool vok[RPT];
+  // ---- tile loader.  Wave load j of wave w fills 1 KB chunk j*4+w of the
+  // K (or V) tile: tile rows r0 + j*ROWS_J, lane l the physical granule l mod
+  // CH of its row, which holds logical granule gK (gV) of that row.  Rows no
+  // query of this work-group may use load chunk row 0 of this KV head
+  // instead: their scores are always masked, so P is exactly 0 there and the
+  // (finite) V row adds nothing.
+  const int r0 = wave * RPC + lane / CH;
+  const int pch = lane % CH;
+  const int gK = pch ^ (r0 & (CH - 1));
+  const int gV = pch ^ (2 * (r0 & 3));
   auto ring_slot = [&](int kp) {  // valid for kp >= S
     return g.S + (kp - g.S) % g.W;
   };
-  // Element offset of position kp's row and whether this work-group may use it.
-  auto row_src = [&](int kp, int slot, int64_t& off, bool& from_cache) -> bool {
+  // Element offset of position kp's row and whether it comes from the cache.
+  auto row_src = [&](int kp, int64_t& off, bool& from_cache) {
     const bool in_chunk = kp >= L;
     const bool ok = kp <= qmax && (in_chunk || retrieval || kp < g.S || kp >= L - g.W);
-    const int64_t cache_row = (retrieval || kp < g.S) ? (int64_t)kp : (int64_t)slot;
+    const int64_t cache_row = (retrieval || kp < g.S) ? (int64_t)kp : (int64_t)ring_slot(kp);
     off = in_chunk ? in_base + (int64_t)(kp - L) * in_stride : cache_row * D;
     from_cache = !in_chunk && ok;
     if (!ok) off = in_base;  // chunk row 0 of this head: always readable
-    return ok;
   };
-  // Per-lane element offsets of this lane's rows inside a tile, for a tile
-  // that lies wholly in the chunk input (row stride Hkv*D) or wholly in the
-  // retrieval cache (row stride D); such tiles need one uniform base each.
-  // K: the lane's j-th direct load covers row r0k + j*KROWS_J with the same
-  // swizzled chunk for every j; V: rows rgV*RPT + i.
-  constexpr int KROWS_J = kWaves * 64 / CH;  // tile rows between a lane's K loads
-  const int r0k = (wave * 64 + lane) / CH;
-  const int lck = ((wave * 64 + lane) % CH) ^ (r0k & (CH - 1));
-  const int koff_in = r0k * (int)in_stride + lck * 8, koff_c = r0k * D + lck * 8;
-  const int voff_in = rgV * RPT * (int)in_stride + chV * 8, voff_c = rgV * RPT * D + chV * 8;
-  auto load_tile = [&](int tile, int buf) {
+  const int koff_in = r0 * in_stride + gK * 8, koff_c = r0 * D + gK * 8;
+  const int voff_in = r0 * in_stride + gV * 8, voff_c = r0 * D + gV * 8;
+  auto load_tile = [&](int tile, int buf_off) {
     const int k0 = tile * kBN;
-    const bool all_in = k0 >= L && k0 + kBN - 1 <= qmax;           // every row in the chunk
-    const bool all_cache = retrieval && k0 + kBN - 1 < L;          // every row cached
+    const int dst = buf_off + wave * 1024;
+    const bool all_in = k0 >= L && k0 + kBN - 1 <= qmax;   // every row in the chunk
+    const bool all_cache = retrieval && k0 + kBN - 1 < L;  // every row cached
     if (all_in || all_cache) {
       const int64_t stride = all_in ? in_stride : D;
-      const uint16_t* kbase = (all_in ? a.k + in_base + (int64_t)(k0 - L) * in_stride : ck + (int64_t)k0 * D) +
-                              (all_in ? koff_in : koff_c);
-      const uint16_t* vbase = (all_in ? a.v + in_base + (int64_t)(k0 - L) * in_stride : cv + (int64_t)k0 * D) +
-                              (all_in ? voff_in : voff_c);
+      const uint16_t* kb = all_in ? a.k + in_base + (int64_t)(k0 - L) * in_stride + koff_in : ck + (int64_t)k0 * D + koff_c;
+      const uint16_t* vb = all_in ? a.v + in_base + (int64_t)(k0 - L) * in_stride + voff_in : cv + (int64_t)k0 * D + voff_c;
 #pragma unroll
-      for (int j = 0; j < RPT; ++j)
-        global_to_lds16(kbase + j * KROWS_J * stride, buf * LD::BUF + (j * kWaves + wave) * 1024);
+      for (int j = 0; j < NJ; ++j) global_to_lds16(kb + j * ROWS_J * stride, dst + j * kWaves * 1024);
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        vok[i] = true;
-        vbuf[i] = *reinterpret_cast<const uint4*>(vbase + i * stride);
-      }
+      for (int j = 0; j < NJ; ++j) global_to_lds16(vb + j * ROWS_J * stride, dst + LD::TILE + j * kWaves * 1024);
       return;
     }
-    // general tile: any mix of cache rows, ring slots, chunk rows, unusable rows
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int p = (j * kWaves + wave) * 64 + lane;  // 16-byte chunk index in the tile
-      const int r = p / CH;
-      const int lc = (p % CH) ^ (r & (CH - 1));
-      const int kp = k0 + r;
+    for (int j = 0; j < NJ; ++j) {
       int64_t off;
       bool from_cache;
-      row_src(kp, retrieval || kp < g.S ? 0 : ring_slot(kp), off, from_cache);
-      const uint16_t* src = (from_cache ? ck : a.k) + off + lc * 8;
-      global_to_lds16(src, buf * LD::BUF + (j * kWaves + wave) * 1024);
-    }
-    const int kp0 = k0 + rgV * RPT;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int kp = kp0 + i;
-      int64_t off;
-      bool from_cache;
-      vok[i] = row_src(kp, retrieval || kp < g.S ? 0 : ring_slot(kp), off, from_cache);
-      vbuf[i] = reinterpret_cast<const uint4*>((from_cache ? cv : a.v) + off)[chV];  // zeroed at the store
-    }
-  };
-  auto store_tile = [&](int buf) {
-    char* vb = smem + buf * LD::BUF + LD::KBYTES;
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) vbuf[i] = select4(vok[i], vbuf[i]);
-    const int pos = vt_pos(rgV * RPT);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      char* dst = vb + (chV * 8 + e) * LD::VSTRIDE + pos * 2;
-      const uint32_t lo = __builtin_amdgcn_perm(word_of(vbuf[1], e >> 1), word_of(vbuf[0], e >> 1), sel);
-      if constexpr (RPT == 4) {
-        const uint32_t hi = __builtin_amdgcn_perm(word_of(vbuf[3], e >> 1), word_of(vbuf[2], e >> 1), sel);
-        *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = lo;
-      }
+      row_src(k0 + r0 + j * ROWS_J, off, from_cache);
+      global_to_lds16((from_cache ? ck : a.k) + off + gK * 8, dst + j * kWaves * 1024);
+      global_to_lds16((from_cache ? cv : a.v) + off + gV * 8, dst + LD::TILE + j * kWaves * 1024);
     }
   };
 
-  // ---- softmax state per block: this lane's query (m, partial l), O^T
-  f32x16_t oacc[QB][DB];
-  float m_run[QB], l_run[QB];
+  // ---- LDS operand addresses (bytes inside a tile)
+  // K rows kb2*32 + col, logical granule 2c + half
+  auto k_addr = [&](int kb2, int c) { return (kb2 * 32 + col) * LD::ROW + (((2 * c + half) ^ (col & (CH - 1))) * 16); };
+  // V^T operand of the 16-key step starting at key s16, rows d = db*32 + col:
+  // lane l names key s16 + 8 t + 4 half + (l/4 mod 4), columns
+  // db*32 + 16 ((l/16) mod 2) + 4 (l mod 4) .. +3, for t = 0, 1.
+  const int vq = (lane >> 2) & 3;
+  const int vg = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
+  auto v_addr = [&](int s16, int tt, int db) {
+    return (s16 + 8 * tt + 4 * half + vq) * LD::ROW + (((4 * db + vg) ^ (2 * vq)) * 16) + 8 * (lane & 1);
+  };
+
+  // ---- softmax state: this lane's query (running max, partial l), O^T
+  f32x16_t oacc[DB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    m_run[qb] = -INFINITY;
-    l_run[qb] = 0.f;
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY;  // running max (log2 units), -inf before any key
+  float mu = 0.f;           // reference subtracted from the scores (m_run, or 0)
+  float thr = -INFINITY;    // move the reference when a tile max (relative to mu) exceeds this
+  float l_run = 0.f;
+  f32x16_t negm;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[qb][db][r] = 0.f;
-  }
-  const float c2 = g.scale_log2;
+  for (int r = 0; r < 16; ++r) negm[r] = 0.f;
   const uint32_t ones = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  load_tile(tile_of(0), 0);
-  store_tile(0);
-  __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of K
-  __syncthreads();
+  auto compute_tile = [&](int kt, auto cur_c) {
+    constexpr int cur = decltype(cur_c)::value;
+    const int k0 = tile_of(kt) * kBN;
+    if (kt + 1 < ntiles) load_tile(tile_of(kt + 1), (cur ^ 1) * LD::BUF);
 
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    const int tile = tile_of(kt);
-    const int k0 = tile * kBN;
-    if (kt + 1 < ntiles) load_tile(tile_of(kt + 1), cur ^ 1);
-
-    // wave-uniform: can any block of this wave see a key of this tile?
-    bool any_live = false, need_mask = !retrieval;
+    // wave-uniform: can the block see a key of this tile, and does any key
+    // need a mask (causal diagonal, or outside the streaming band)
+    bool live = bhi >= blo && k0 <= bhi;
+    if (!retrieval && k0 >= g.S && k0 + kBN - 1 < blo - g.W + 1) live = false;
+    const bool need_mask = k0 + kBN - 1 > blo || (!retrieval && k0 + kBN - 1 >= g.S && k0 < bhi - g.W + 1);
+    if (live) {
+      constexpr int kb = cur * LD::BUF, vb = kb + LD::TILE;
+      f32x16_t sacc[2];
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-      bool live = bhi[qb] >= blo[qb] && k0 <= bhi[qb];
-      if (!retrieval && k0 >= g.S && k0 + kBN - 1 < blo[qb] - g.W + 1) live = false;
-      any_live = any_live || live;
-      need_mask = need_mask || k0 + kBN - 1 > blo[qb];
-    }
-    if (any_live) {
-      const char* kb = smem + cur * LD::BUF;
-      const char* vb = kb + LD::KBYTES;
-      f32x16_t sacc[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[qb][kb2][r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < QC; ++c) {
+      for (int c = 0; c < QC; ++c)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const int kr = kb2 * 32 + col;
-          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kb + kr * LD::KSTRIDE + (((2 * c + half) ^ (kr & (CH - 1))) * 16));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            sacc[qb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[qb][c], sacc[qb][kb2], 0, 0, 0);
+          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(prefill_smem + kb + k_addr(kb2, c));
+          sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c], c == 0 ? negm : sacc[kb2], 0, 0, 0);
         }
-      }
       // masks: causal on the diagonal, band for streaming heads (branch-free)
       if (need_mask) {
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          const int lo_win = retrieval ? -1 : max(my_q[qb] - g.W, g.S - 1);  // keep kp > lo_win ...
-          const int sink_end = retrieval ? 0 : g.S;                        // ... or kp < sink_end
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int kp = k0 + kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              const bool ok = (kp <= my_q[qb]) & ((kp > lo_win) | (kp < sink_end));
-              sacc[qb][kb2][r] = ok ? sacc[qb][kb2][r] : -INFINITY;
-            }
-        }
-      }
-      float mu[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mt = fmaxf(sacc[qb][0][0], sacc[qb][1][0]);
+        const int lo_win = retrieval ? -1 : max(my_q - g.W, g.S - 1);  // keep kp > lo_win ...
+        const int sink_end = retrieval ? 0 : g.S;                       // ... or kp < sink_end
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[qb][kb2][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32)) * c2;
-        // move the reference only when some query's max grew by > 2^8
-        if (__any(mt > m_run[qb] + kRescaleSlack)) {
-          const float m_new = fmaxf(m_run[qb], mt);
-          const float alpha = exp2_fast(m_run[qb] - (m_new == -INFINITY ? 0.f : m_new));
-          m_run[qb] = m_new;
-          l_run[qb] *= alpha;
+          for (int r = 0; r < 16; ++r) {
+            const int kp = k0 + kb2 * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool ok = (kp <= my_q) & ((kp > lo_win) | (kp < sink_end));
+            sacc[kb2][r] = ok ? sacc[kb2][r] : -INFINITY;
+          }
+      }
+      float mt = fmaxf(sacc[0][0], sacc[1][0]);
 #pragma unroll
-          for (int db = 0; db < DB; ++db)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[qb][db][r] *= alpha;
-        }
-        mu[qb] = m_run[qb] == -INFINITY ? 0.f : m_run[qb];
+        for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32));  // tile max relative to mu
+      if (__any(mt > thr)) {
+        const float m_new = fmaxf(m_run, mu + mt);
+        const float mu_new = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2_fast(m_run - mu_new);  // 0 while m_run = -inf
+        const float delta = mu_new - mu;
+        m_run = m_new;
+        mu = mu_new;
+        thr = m_new == -INFINITY ? -INFINITY : kRescaleSlack;
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb2][r] -= delta;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) negm[r] = -mu;
       }
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
-          bf16x8_t pb[QB];
+          uint32_t w[4];
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            uint32_t w[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float p0 = exp2_fast(fmaf(sacc[qb][kb2][st * 8 + 2 * r], c2, -mu[qb]));
-              const float p1 = exp2_fast(fmaf(sacc[qb][kb2][st * 8 + 2 * r + 1], c2, -mu[qb]));
-              w[r] = pack_bf16x2(p0, p1);
-              l_run[qb] = dot2_bf16(w[r], ones, l_run[qb]);
-            }
-            pb[qb] = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+          for (int r = 0; r < 4; ++r) {
+            w[r] = pack_bf16x2(exp2_fast(sacc[kb2][st * 8 + 2 * r]), exp2_fast(sacc[kb2][st * 8 + 2 * r + 1]));
+            l_run = dot2_bf16(w[r], ones, l_run);
           }
+          const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const bf16x8_t va = *reinterpret_cast<const bf16x8_t*>(vb + (db * 32 + col) * LD::VSTRIDE +
-                                                                   (kb2 * 32 + st * 16 + 8 * half) * 2);
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb)
-              oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[qb], oacc[qb][db], 0, 0, 0);
+            const uint2 lo = lds_read_tr16(vb + v_addr(kb2 * 32 + st * 16, 0, db));
+            const uint2 hi = lds_read_tr16(vb + v_addr(kb2 * 32 + st * 16, 1, db));
+            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
           }
         }
     }
-    if (kt + 1 < ntiles) store_tile(cur ^ 1);
-    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of K
+    __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next tile
     __syncthreads();
+  };
+
+  load_tile(tile_of(0), 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    compute_tile(kt, std::integral_constant<int, 0>());
+    if (kt + 1 < ntiles) compute_tile(kt + 1, std::integral_constant<int, 1>());
   }
 
-  // ---- normalise and store this lane's query rows
+  // ---- normalise and store this lane's query row
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (my_i <= i_hi) {
+    const float inv = 1.0f / l_tot;
+    uint16_t* dst = a.out + (((int64_t)b * a.chunk + my_i) * g.Hq + h) * D;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    if (my_i[qb] <= i_hi) {
-      const float inv = 1.0f / l_tot;
-      uint16_t* dst = a.out + (((int64_t)b * a.chunk + my_i[qb]) * g.Hq + h) * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = db * 32 + 8 * r4 + 4 * half;
-          const uint32_t w0 = pack_bf16x2(oacc[qb][db][4 * r4] * inv, oacc[qb][db][4 * r4 + 1] * inv);
-          const uint32_t w1 = pack_bf16x2(oacc[qb][db][4 * r4 + 2] * inv, oacc[qb][db][4 * r4 + 3] * inv);
-          *reinterpret_cast<uint2*>(dst + d0) = make_uint2(w0, w1);
-        }
-    }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * half;
+        const uint32_t w0 = pack_bf16x2(oacc[db][4 * r4] * inv, oacc[db][4 * r4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(oacc[db][4 * r4 + 2] * inv, oacc[db][4 * r4 + 3] * inv);
+        *reinterpret_cast<uint2*>(dst + d0) = make_uint2(w0, w1);
+      }
   }
 }
 
@@ -433,21 +374,21 @@ int heads_per_group(int G) {
   return 1;
 }
 
-template <int D, int QB>
+template <int D>
 hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, QB>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Lds<D>::TOTAL);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  a.tq = kWaves * 32 * QB / a.gh;
+  a.tq = kWaves * 32 / a.gh;
   a.tiles_max = (max_n + a.tq - 1) / a.tq;
   a.items_r = a.tiles_max * g.B * g.nR * a.n_hc;
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * g.B * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<D, QB>), dim3((unsigned)blocks), dim3(kThreads), Lds<D>::TOTAL, s, g, q, a);
+  hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), Lds<D>::TOTAL, s, g, q, a);
   return hipGetLastError();
 }
 
@@ -464,12 +405,7 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   a.chunk = chunk;
   a.gh = heads_per_group(g.G);
   a.n_hc = g.G / a.gh;
-  static const int qb_env = [] {
-    const char* e = getenv("DUO_PREFILL_QB");
-    return e ? atoi(e) : 1;
-  }();
-  if (g.D == 128) return qb_env == 1 ? launch_t<128, 1>(g, q, a, max_n, s) : launch_t<128, 2>(g, q, a, max_n, s);
-  return qb_env == 1 ? launch_t<64, 1>(g, q, a, max_n, s) : launch_t<64, 2>(g, q, a, max_n, s);
+  return g.D == 128 ? launch_t<128>(g, q, a, max_n, s) : launch_t<64>(g, q, a, max_n, s);
 }
 
 }  // namespace duo
