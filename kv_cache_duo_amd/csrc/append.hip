@@ -47,7 +47,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
   }
   const int len = q.len[b];
   const int n = q.n[b];
-  const int kvh = g.kv_of_unit[retrieval ? idx : g.nR + idx];
+  const int kvh = kv_head_of_unit(g, retrieval ? idx : g.nR + idx);
 
   // Lengths: written once per sequence, by the first block of its first head.
   if (x == 0 && idx == 0 && threadIdx.x == 0 && (retrieval || g.nR == 0)) g.lengths[b] = len + n;

@@ -5,23 +5,23 @@
 // constant-length cache of sinks + recent tokens.  Decoding is memory-bound:
 // every cached K/V byte of a retrieval head is read once per step.
 //
-// Two launches per step:
-//   decode_kernel -- work item = (sequence b, KV head, query-head chunk,
-//     split).  A split is a contiguous range of cache rows (retrieval: rows =
-//     positions 0..L; streaming: the min(L+1, sink+recent) occupied slots).
-//     The new token's row is read from the input and stored to the cache by
-//     its owner, so no work item reads a row that is being written.  Each
-//     work-group streams its rows with coalesced 16-byte loads (a row of D
-//     bf16 is read by D/8 lanes; one wave instruction reads 1 KB of
-//     consecutive rows), scores every query head of the KV group from the
-//     same K bytes with bf16 dot2 + DPP group sums, and keeps an online
-//     softmax (running max m, sum l, unnormalised o) per head.  A unit with
-//     one split writes the output; otherwise each split writes a record.
-//   merge_kernel -- one work-group per unit with several splits:
-//     M = max m_k, L = sum l_k 2^(m_k-M), O = sum o_k 2^(m_k-M) / L.
-// The kernel boundary makes the records visible across XCDs; an in-kernel
-// "last work-group merges" scheme would need an agent-scope release/acquire
-// per work-group, which on gfx950 writes back and invalidates the XCD's L2.
+// One launch per step.  A unit is (sequence b, KV head, query-head chunk);
+// its rows are the cache rows (retrieval: positions 0..L; streaming: the
+// min(L+1, sink+recent) occupied slots), cut into pairs of batches.  Every
+// unit gets ns work-groups.  Work-group `split` of a unit takes pair `split`
+// first, then claims further pairs from the unit's counter (one claim
+// ahead of use), so work-groups that get less bandwidth take fewer rows.
+// The new token's row is read from the input and stored to the cache by the
+// work-group whose pair holds it; no other work-group reads that row.  Each
+// work-group streams its rows with coalesced 16-byte loads (a row of D bf16
+// is read by D/8 lanes; one wave instruction reads 1 KB of consecutive
+// rows), scores every query head of the KV group from the same K bytes with
+// bf16 dot2 + DPP group sums, and keeps an online softmax (running max m,
+// sum l, unnormalised o) per head.  A unit with one work-group writes the
+// output; otherwise each work-group writes a record and the last one to
+// arrive merges:  M = max m_k, L = sum l_k 2^(m_k-M), O = sum o_k 2^(m_k-M) / L.
+// Records and tickets use agent-coherent (sc1) accesses without fences: an
+// agent-scope fence on gfx950 writes back and invalidates the whole L2.
 // Scores are kept in base-2 units (scale * log2 e folded in), so exp2 is the
 // only transcendental.
 #include <cfloat>
@@ -36,6 +36,7 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxMergeRecords = 1024;  // (m, l) pairs the merge stages in LDS
+constexpr int kMinPairs = 4;            // pairs of batches per work-group, at least, on average
 
 struct DecodeArgs {
   const uint16_t* q;  // [B][Hq][D]
@@ -43,7 +44,6 @@ struct DecodeArgs {
   const uint16_t* v;
   uint16_t* out;      // [B][Hq][D]
   int32_t split_tokens, splits_r, splits_s;
-  int32_t inline_merge;  // 1: last work-group of a unit merges; 0: merge_kernel does
 };
 
 // Agent-coherent (cross-XCD) accesses without fences: on gfx950 relaxed
@@ -55,6 +55,11 @@ __device__ __forceinline__ void store_agent(float* p, float v) {
 }
 __device__ __forceinline__ float load_agent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent2(const float* p) {  // p 8-byte aligned
+  const uint64_t x = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(float2, x);
 }
 
 __device__ __forceinline__ float max_or_zero(float m) { return m == -INFINITY ? 0.f : m; }
@@ -78,7 +83,84 @@ __device__ __forceinline__ float* unit_records(const Geom& g, int64_t pu) {
 // work-group call it.  lds must hold kMergeLdsBytes.
 constexpr int kMergeBatch = 16;  // record loads in flight per thread
 template <int GC>
-constexpr int merge_lds_bytes() { return kMaxMergeRecords * 8 + kThreads * 4 + 2 * GC * 4; }
+constexpr int merge_lds_bytes() { return kMaxMergeRecords * 8 + kThreads * 8 + 2 * GC * 4; }
+
+// Single-pass merge: when a unit's records fit, the last work-group loads
+// every o value at once (kSingleLoads 64-bit loads per thread, issued together
+// with the (m, l) loads), so the merge costs one memory round trip after the
+// ticket.  Records of GC*D floats are read as GC*D/2 float2 chunks; KL
+// records are summed in parallel.
+constexpr int kSingleLoads = 36;
+template <int D, int GC>
+constexpr int single_merge_max() {
+  return GC * D / 2 > kThreads ? 0 : (kThreads / (GC * D / 2)) * kSingleLoads;
+}
+
+template <int D, int GC>
+__device__ void merge_single(const Geom& g, const DecodeArgs& a, char* lds, const float* rec_o, const float* rec_ml,
+                             int cnt, int b, int h0) {
+  constexpr int E = GC * D;
+  constexpr int C2 = E / 2;            // float2 chunks per record
+  constexpr int KL = kThreads / C2;    // records summed in parallel
+  static_assert(C2 <= kThreads && kThreads % C2 == 0, "single-pass merge layout");
+  float2* st_ml = reinterpret_cast<float2*>(lds);                           // [cnt * GC]
+  float2* st_acc = reinterpret_cast<float2*>(lds + kMaxMergeRecords * 8);   // [kThreads]
+  float* st_L = reinterpret_cast<float*>(st_acc + kThreads);                // [GC]
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int cc = threadIdx.x % C2;
+  const int kl = threadIdx.x / C2;
+  float2 v[kSingleLoads];
+#pragma unroll
+  for (int u = 0; u < kSingleLoads; ++u)
+    if (u * KL < cnt) v[u] = load_agent2(rec_o + (int64_t)min(kl + u * KL, cnt - 1) * E + 2 * cc);
+  for (int i = threadIdx.x; i < cnt * GC; i += kThreads) st_ml[i] = load_agent2(rec_ml + 2 * i);
+  __syncthreads();
+  for (int gg = wave; gg < GC; gg += kWaves) {
+    float mx = -INFINITY;
+    for (int k = lane; k < cnt; k += 64) mx = fmaxf(mx, st_ml[k * GC + gg].x);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mu = max_or_zero(mx);
+    float ls = 0.f;
+    for (int k = lane; k < cnt; k += 64) {
+      const float2 ml = st_ml[k * GC + gg];
+      const float f = exp2_fast(ml.x - mu);
+      st_ml[k * GC + gg].x = f;
+      ls += ml.y * f;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
+    if (lane == 0) st_L[gg] = ls;
+  }
+  __syncthreads();
+  const int gg = 2 * cc / D;
+  float2 acc = make_float2(0.f, 0.f);
+#pragma unroll
+  for (int u = 0; u < kSingleLoads; ++u) {
+    const int k = kl + u * KL;
+    if (u * KL < cnt && k < cnt) {
+      const float f = st_ml[k * GC + gg].x;
+      acc.x = fmaf(v[u].x, f, acc.x);
+      acc.y = fmaf(v[u].y, f, acc.y);
+    }
+  }
+  if (KL > 1) {
+    st_acc[threadIdx.x] = acc;
+    __syncthreads();
+    if (kl == 0)
+      for (int j = 1; j < KL; ++j) {
+        const float2 x = st_acc[j * C2 + cc];
+        acc.x += x.x;
+        acc.y += x.y;
+      }
+  }
+  if (kl == 0) {
+    const float inv = 1.0f / st_L[gg];
+    *reinterpret_cast<uint32_t*>(a.out + ((int64_t)b * g.Hq + h0 + gg) * D + (2 * cc) % D) =
+        pack_bf16x2(acc.x * inv, acc.y * inv);
+  }
+}
 
 template <int D, int GC>
 __device__ void merge_records(const Geom& g, const DecodeArgs& a, char* lds, float* rec_o, float* rec_ml, int first,
@@ -182,7 +264,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // K and V rows each lane loads per batch (two batches in flight); fewer
   // when more query heads per work-group need registers.
   constexpr int kInFlight = GC >= 4 ? 2 : 4;
-  constexpr int ROWS_ITER = kWaves * RPW * kInFlight;
+  constexpr int ROWS_ITER = kWaves * RPW * kInFlight;  // rows per batch
+  constexpr int PAIR = 2 * ROWS_ITER;                   // rows per claimed pair of batches
+  static_assert(PAIR == decode_pair_rows(D, GC), "host and kernel pair sizes");
   // the cross-wave partials [kWaves][GC][D] share LDS with the merge staging
   // area of the last work-group
   constexpr int kCombineBytes = kWaves * GC * D * 4;
@@ -191,6 +275,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   float(*sm_o)[GC][D] = reinterpret_cast<float(*)[GC][D]>(sm_raw);
   __shared__ float sm_m[kWaves][GC];
   __shared__ float sm_l[kWaves][GC];
+  __shared__ int sm_flag;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -218,11 +303,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   const int L = sq.len[b];
   const int T = retrieval ? L + 1 : min(L + 1, g.slots);
   const int new_row = retrieval ? L : (L < g.S ? L : g.S + (L - g.S) % g.W);
-  const int ns = (T + a.split_tokens - 1) / a.split_tokens;
+  const int ns = (T + a.split_tokens - 1) / a.split_tokens;  // work-groups of this unit
   if (split >= ns) return;
-  const int r0 = split * a.split_tokens;
-  const int r1 = min(r0 + a.split_tokens, T);
-  const int kvh = g.kv_of_unit[retrieval ? idx : g.nR + idx];
+  const int npairs = (T + PAIR - 1) / PAIR;
+  const int kvh = kv_head_of_unit(g, retrieval ? idx : g.nR + idx);
   const int64_t unit_rows = retrieval ? g.max_len : (int64_t)g.slots;
   const int64_t cache_off = ((int64_t)b * nkind + idx) * unit_rows * D;
   uint16_t* ck = (retrieval ? g.rk : g.sk) + cache_off;
@@ -230,6 +314,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   const uint16_t* nk = a.k + ((int64_t)b * g.Hkv + kvh) * D;
   const uint16_t* nv = a.v + ((int64_t)b * g.Hkv + kvh) * D;
   const int h0 = kvh * g.G + hc * GC;
+  const int64_t pu = ((int64_t)b * g.Hkv + kvh) * n_hc + hc;
+  uint32_t* t_unit = g.tickets + pu * g.tickets_per_unit;  // line 0: arrivals, line 1: pair claims
+  uint32_t* t_claim = t_unit + kTicketStride;
+  // Wave 0 claims for the work-group: lane 0 adds 1, the other lanes 0, so
+  // lane 0's value is the claim however the lanes' atomics are combined.
+  // The claim for the second pair goes out before anything else.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  auto claim = [&]() {
+    return __hip_atomic_fetch_add(t_claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  uint32_t claimed = 0;
+  if (threadIdx.x == 0) claimed = claim();
 
   // ---- queries of the GC heads: this lane's 8 dims of each
   uint32_t qw[GC][4];
@@ -251,13 +347,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // Row j of a batch starting at `base`: consecutive rows per load
   // instruction of a wave, so each instruction reads RPW * D * 2 = 1 KB.
   auto row_of = [&](int base, int j) { return base + (j * kWaves + wave) * RPW + grp; };
-  // Loads are unconditional (rows past the split re-read its last row and
-  // get a -inf score), so the compiler can count outstanding loads and wait
-  // only for the older batch.
+  // Loads are unconditional per lane (rows past the unit's end re-read its
+  // last row and get a -inf score), so the compiler can count outstanding
+  // loads and wait only for the older batch.
   auto load = [&](uint4 (&kr)[kInFlight], uint4 (&vr)[kInFlight], int base) {
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const int row = min(row_of(base, j), r1 - 1);
+      const int row = min(row_of(base, j), T - 1);
       const uint16_t* pk = row == new_row ? nk : ck + (int64_t)row * D;
       const uint16_t* pv = row == new_row ? nv : cv + (int64_t)row * D;
       kr[j] = load_nt(reinterpret_cast<const uint4*>(pk) + c);  // streamed once: non-temporal
@@ -268,7 +364,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     float s[kInFlight][GC];
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const bool valid = row_of(base, j) < r1;
+      const bool valid = row_of(base, j) < T;
 #pragma unroll
       for (int gg = 0; gg < GC; ++gg) {
         float acc = dot2_bf16(kr[j].x, qw[gg][0], 0.f);
@@ -305,20 +401,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     }
   };
 
-  // ---- stream the rows, the next batch's loads in flight during each batch
+  // ---- stream the pairs: pair `split`, then claimed pairs ns, ns+1, ...
+  // While a pair's two batches are processed, the next pair's loads go out
+  // batch by batch, and the claim for the pair after it is in flight.  The
+  // claim reaches the other waves through a double-buffered LDS slot (one
+  // barrier per pair).
+  __shared__ int sm_claim[2];
+  bool own_new = false;  // this work-group's rows hold the new token
   {
     uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
-    load(ka, va, r0);
-    for (int base = r0;;) {
-      const int nb = base + ROWS_ITER;
-      load(kb, vb, nb);  // past the end: clamped rows, served by the cache
+    int base = split * PAIR;
+    load(ka, va, base);
+    load(kb, vb, base + ROWS_ITER);
+    for (int it = 0;; it ^= 1) {
+      if (threadIdx.x == 0) {
+        sm_claim[it] = ns + (int)claimed;
+        claimed = claim();
+      }
+      __syncthreads();
+      const int p_next = __builtin_amdgcn_readfirstlane(sm_claim[it]);
+      const bool more = p_next < npairs;
+      // past the last pair the loads re-read the unit's last row (cached);
+      // unconditional loads keep the outstanding-load count static
+      const int nbase = more ? p_next * PAIR : T;
       process(ka, va, base);
-      if (nb >= r1) break;
-      const int nb2 = nb + ROWS_ITER;
-      load(ka, va, nb2);
-      process(kb, vb, nb);
-      if (nb2 >= r1) break;
-      base = nb2;
+      load(ka, va, nbase);
+      process(kb, vb, base + ROWS_ITER);
+      load(kb, vb, nbase + ROWS_ITER);
+      own_new = own_new || (new_row >= base && new_row < base + PAIR);
+      if (!more) break;
+      base = nbase;
     }
   }
 
@@ -355,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   }
 
   // ---- the owner of the new token stores it (one head chunk does it)
-  if (hc == 0 && new_row >= r0 && new_row < r1 && threadIdx.x < LPR) {
+  if (hc == 0 && own_new && threadIdx.x < LPR) {
     const int64_t off = (int64_t)new_row * D;
     reinterpret_cast<uint4*>(ck + off)[threadIdx.x] = reinterpret_cast<const uint4*>(nk)[threadIdx.x];
     reinterpret_cast<uint4*>(cv + off)[threadIdx.x] = reinterpret_cast<const uint4*>(nv)[threadIdx.x];
@@ -363,10 +475,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   }
   __syncthreads();
 
-  // ---- merge the waves; write the output or this split's record
-  const int64_t pu = ((int64_t)b * g.Hkv + kvh) * n_hc + hc;
+  // ---- merge the waves; write the output or this work-group's record
   float* rec_o = unit_records<D, GC>(g, pu);
-  float2* rec_ml = reinterpret_cast<float2*>(rec_o + (int64_t)g.max_splits * GC * D);
+  float* rec_ml = rec_o + (int64_t)g.max_splits * GC * D;  // (m, l) pairs
   for (int t = threadIdx.x; t < GC * D; t += kThreads) {
     const int gg = t / D, d = t % D;
     float mw = sm_m[0][gg];
@@ -382,148 +493,66 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     }
     if (ns == 1) {
       a.out[((int64_t)b * g.Hq + h0 + gg) * D + d] = (uint16_t)f32_to_bf16_bits(osum / lsum);
-    } else if (a.inline_merge) {
+    } else {
       store_agent(&rec_o[((int64_t)split * GC + gg) * D + d], osum);
       if (d == 0) {
-        store_agent(&rec_ml[split * GC + gg].x, mw);
-        store_agent(&rec_ml[split * GC + gg].y, lsum);
+        store_agent(&rec_ml[2 * (split * GC + gg)], mw);
+        store_agent(&rec_ml[2 * (split * GC + gg) + 1], lsum);
       }
-    } else {
-      rec_o[((int64_t)split * GC + gg) * D + d] = osum;
-      if (d == 0) rec_ml[split * GC + gg] = make_float2(mw, lsum);
     }
   }
-  if (ns == 1 || !a.inline_merge) return;
+  if (ns == 1) {  // the only claimer of this unit
+    if (threadIdx.x == 0) __hip_atomic_store(t_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
 
-  // ---- merge in two levels.  The last work-group to finish in a group of
-  // kMergeGroup splits merges the group into the group's first slot; the
-  // last group to finish merges the groups.  Each work-group's record stores
-  // are complete (at the agent-coherent level) before its ticket increment.
+  // ---- merge.  Each work-group's record stores are complete (at the
+  // agent-coherent level) before its ticket increment.  The work-groups of
+  // a unit arrive in groups of kMergeGroup; the last arrival of a group
+  // arrives at the unit's counter, and the last arrival there (after which
+  // no work-group of the unit claims any more) resets the claim counter and
+  // merges.  Up to single_merge_max records it merges them all in one pass;
+  // beyond that the last arrival of each group first merges its group into
+  // the group's first record slot.
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  __shared__ int sm_flag;
   const int mgrp = split / kMergeGroup;
   const int ng = (ns + kMergeGroup - 1) / kMergeGroup;
   const int g0 = mgrp * kMergeGroup;
   const int gsz = min(kMergeGroup, ns - g0);
-  uint32_t* t_unit = g.tickets + pu * g.tickets_per_unit;  // [0]: groups done, [1 + mgrp]: splits done
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(t_unit + 1 + mgrp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_flag = prev == (uint32_t)(gsz - 1);
+  uint32_t* t_group = t_unit + kTicketStride * (2 + mgrp);  // arrivals of this group
+  // True in the work-group that completes n arrivals at *t (which it resets).
+  auto last_arrival = [&](uint32_t* t, int n) {
+    __syncthreads();  // also: sm_flag of an earlier call has been read
+    if (threadIdx.x == 0) {
+      const uint32_t prev = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      sm_flag = prev == (uint32_t)(n - 1);
+      if (sm_flag) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    return sm_flag != 0;
+  };
+  auto reset_claims = [&]() {
+    if (threadIdx.x == 0) __hip_atomic_store(t_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if constexpr (single_merge_max<D, GC>() > 0) {
+    if (ns <= single_merge_max<D, GC>()) {
+      if (ng > 1 && !last_arrival(t_group, gsz)) return;
+      if (!last_arrival(t_unit, ng > 1 ? ng : ns)) return;
+      reset_claims();
+      merge_single<D, GC>(g, a, sm_raw, rec_o, rec_ml, ns, b, h0);
+      return;
+    }
   }
-  __syncthreads();
-  if (!sm_flag) return;
-  if (threadIdx.x == 0) __hip_atomic_store(t_unit + 1 + mgrp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float* rml = reinterpret_cast<float*>(rec_ml);
-  merge_records<D, GC>(g, a, sm_raw, rec_o, rml, g0, 1, gsz, ng == 1, b, h0);
-  if (ng == 1) return;
+  if (!last_arrival(t_group, gsz)) return;
+  merge_records<D, GC>(g, a, sm_raw, rec_o, rec_ml, g0, 1, gsz, ng == 1, b, h0);
+  if (ng == 1) {
+    reset_claims();
+    return;
+  }
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = __hip_atomic_fetch_add(t_unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sm_flag = prev == (uint32_t)(ng - 1);
-  }
-  __syncthreads();
-  if (!sm_flag) return;
-  if (threadIdx.x == 0) __hip_atomic_store(t_unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  merge_records<D, GC>(g, a, sm_raw, rec_o, rml, 0, kMergeGroup, ng, true, b, h0);
-}
-
-// Merge of the split records: one work-group per (b, kv head, head chunk,
-// query head of the chunk, 32-wide slice of D).  Every thread issues all its
-// record loads before using them, so the merge costs about one memory round
-// trip.
-constexpr int kMergeSlice = 32;
-template <int D, int GC>
-__global__ __launch_bounds__(kThreads) void merge_kernel(Geom g, Seqs sq, DecodeArgs a) {
-  constexpr int SLICES = D / kMergeSlice;
-  constexpr int CPS = kMergeSlice / 4;        // float4 chunks per slice
-  constexpr int KL = kThreads / CPS;          // records summed in parallel
-  __shared__ float2 st_ml[kMaxMergeRecords];  // (m, then f = 2^(m-M); l)
-  __shared__ float4 st_acc[kThreads];
-  __shared__ float st_red[2][kWaves];
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int n_hc = g.G / GC;
-  int id = blockIdx.x;
-  const int slice = id % SLICES;
-  id /= SLICES;
-  const int gg = id % GC;
-  const int pu = id / GC;
-  const int hc = pu % n_hc;
-  const int kvh = (pu / n_hc) % g.Hkv;
-  const int b = pu / (n_hc * g.Hkv);
-  const int L = sq.len[b];
-  const int T = g.is_retrieval[kvh] ? L + 1 : min(L + 1, g.slots);
-  const int ns = (T + a.split_tokens - 1) / a.split_tokens;
-  if (ns <= 1) return;
-  const float* rec_o = unit_records<D, GC>(g, pu);
-  const float2* rec_ml = reinterpret_cast<const float2*>(rec_o + (int64_t)g.max_splits * GC * D);
-
-  // 1. stage this head's (m, l) pairs; block max M
-  float mx = -INFINITY;
-  for (int k = threadIdx.x; k < ns; k += kThreads) {
-    const float2 ml = rec_ml[k * GC + gg];
-    st_ml[k] = ml;
-    mx = fmaxf(mx, ml.x);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if (lane == 0) st_red[0][wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(st_red[0][0], st_red[0][1]), fmaxf(st_red[0][2], st_red[0][3]));
-  const float mu = max_or_zero(mx);
-  // 2. f_k = 2^(m_k - M), L = sum l_k f_k
-  float ls = 0.f;
-  for (int k = threadIdx.x; k < ns; k += kThreads) {
-    const float2 ml = st_ml[k];
-    const float f = exp2_fast(ml.x - mu);
-    st_ml[k].x = f;
-    ls += ml.y * f;
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) ls += __shfl_xor(ls, off);
-  if (lane == 0) st_red[1][wave] = ls;
-  __syncthreads();
-  // 3. O slice = sum_k f_k o_k, 8 record loads in flight per thread
-  const int cc = threadIdx.x % CPS;
-  const int kl = threadIdx.x / CPS;
-  const float4* src = reinterpret_cast<const float4*>(rec_o + (int64_t)gg * D + slice * kMergeSlice) + cc;
-  constexpr int REC4 = GC * D / 4;  // float4 stride between records
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int k0 = kl; k0 < ns; k0 += KL * 8) {
-    float4 v[8];
-#pragma unroll
-    for (int u2 = 0; u2 < 8; ++u2) {
-      const int k = min(k0 + u2 * KL, ns - 1);
-      v[u2] = src[(int64_t)k * REC4];
-    }
-#pragma unroll
-    for (int u2 = 0; u2 < 8; ++u2) {
-      const int k = k0 + u2 * KL;
-      const float f = k < ns ? st_ml[k].x : 0.f;
-      acc.x = fmaf(v[u2].x, f, acc.x);
-      acc.y = fmaf(v[u2].y, f, acc.y);
-      acc.z = fmaf(v[u2].z, f, acc.z);
-      acc.w = fmaf(v[u2].w, f, acc.w);
-    }
-  }
-  st_acc[threadIdx.x] = acc;
-  __syncthreads();
-  if (threadIdx.x < CPS) {
-    float4 s4 = st_acc[threadIdx.x];
-    for (int j = 1; j < KL; ++j) {
-      const float4 x = st_acc[j * CPS + threadIdx.x];
-      s4.x += x.x; s4.y += x.y; s4.z += x.z; s4.w += x.w;
-    }
-    const float lsum = st_red[1][0] + st_red[1][1] + st_red[1][2] + st_red[1][3];
-    const float inv = 1.0f / lsum;
-    const int h = kvh * g.G + hc * GC + gg;
-    const int d0 = slice * kMergeSlice + threadIdx.x * 4;
-    *reinterpret_cast<uint2*>(a.out + ((int64_t)b * g.Hq + h) * D + d0) =
-        make_uint2(pack_bf16x2(s4.x * inv, s4.y * inv), pack_bf16x2(s4.z * inv, s4.w * inv));
-  }
+  if (!last_arrival(t_unit, ng)) return;
+  reset_claims();
+  merge_records<D, GC>(g, a, sm_raw, rec_o, rec_ml, 0, kMergeGroup, ng, true, b, h0);
 }
 
 }  // namespace
@@ -539,22 +568,26 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   DecodePlan p;
   p.head_chunk = decode_head_chunk(g.G);
   const int n_hc = g.G / p.head_chunk;
+  const int64_t pair = decode_pair_rows(g.D, p.head_chunk);
   int64_t total = 0;
   int32_t tmax = 1;
   for (int b = 0; b < g.B; ++b) {
     total += (int64_t)(q.len[b] + 1) * g.nR * n_hc;
     tmax = q.len[b] + 1 > tmax ? q.len[b] + 1 : tmax;
   }
-  auto round64 = [](int64_t x) { return (x + 63) / 64 * 64; };
-  int64_t ts = round64((total + 2047) / 2048);
-  if (ts < 256) ts = 256;
-  const int64_t ts_cap = round64(((int64_t)tmax + g.max_splits - 1) / g.max_splits);
+  // Rows per work-group on average (work-groups of a unit share its rows
+  // dynamically): about 2048 work-groups over the retrieval rows, at least
+  // kMinPairs pairs each, and few enough work-groups per unit for its records.
+  auto round_pair = [&](int64_t x) { return (x + pair - 1) / pair * pair; };
+  int64_t ts = round_pair((total + 2047) / 2048);
+  if (ts < kMinPairs * pair) ts = kMinPairs * pair;
+  const int64_t ts_cap = round_pair(((int64_t)tmax + g.max_splits - 1) / g.max_splits);
   if (ts < ts_cap) ts = ts_cap;
   static const int64_t env_ts = [] {
     const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
     return e ? (int64_t)atoll(e) : (int64_t)0;
   }();
-  if (env_ts >= 64 && env_ts % 64 == 0 && env_ts >= ts_cap) ts = env_ts;
+  if (env_ts > 0 && env_ts % pair == 0 && env_ts >= ts_cap) ts = env_ts;
   p.split_tokens = (int32_t)ts;
   p.splits_r = (int32_t)((tmax + ts - 1) / ts);
   const int32_t smax = tmax < g.slots ? tmax : g.slots;
@@ -564,23 +597,15 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
 
 hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p, const uint16_t* qin,
                          const uint16_t* kin, const uint16_t* vin, uint16_t* out, hipStream_t s) {
-  // Split merge inside the decode launch by default; DUO_DECODE_MERGE=kernel
-  // selects a separate merge launch instead.
-  static const int inline_merge = [] {
-    const char* e = getenv("DUO_DECODE_MERGE");
-    return (e && e[0] == 'k') ? 0 : 1;
-  }();
-  DecodeArgs a{qin, kin, vin, out, p.split_tokens, p.splits_r, p.splits_s, inline_merge};
+  DecodeArgs a{qin, kin, vin, out, p.split_tokens, p.splits_r, p.splits_s};
   const int n_hc = g.G / p.head_chunk;
   const int64_t items = (int64_t)g.B * g.nR * n_hc * p.splits_r + (int64_t)g.B * g.nS * n_hc * p.splits_s;
   if (items <= 0) return hipSuccess;
-  const bool split = p.splits_r > 1 || p.splits_s > 1;
-  const dim3 grid((unsigned)items), block(kThreads), mgrid((unsigned)(g.B * g.Hkv * n_hc * p.head_chunk * (g.D / kMergeSlice)));
-#define DUO_DECODE_CASE(DD, GG)                                                        \
-  if (g.D == DD && p.head_chunk == GG) {                                               \
-    hipLaunchKernelGGL((decode_kernel<DD, GG>), grid, block, 0, s, g, q, a);           \
-    if (split && !inline_merge) hipLaunchKernelGGL((merge_kernel<DD, GG>), mgrid, block, 0, s, g, q, a); \
-    return hipGetLastError();                                                          \
+  const dim3 grid((unsigned)items), block(kThreads);
+#define DUO_DECODE_CASE(DD, GG)                                              \
+  if (g.D == DD && p.head_chunk == GG) {                                     \
+    hipLaunchKernelGGL((decode_kernel<DD, GG>), grid, block, 0, s, g, q, a); \
+    return hipGetLastError();                                                \
   }
   DUO_DECODE_CASE(128, 1)
   DUO_DECODE_CASE(128, 2)

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include "duo.h"
@@ -25,7 +26,7 @@ struct Geom {
   int32_t* lengths;           // [B]
   float* partials;            // split-K records, see decode.hip
   uint32_t* tickets;          // [units][tickets_per_unit] split counters (zero between calls)
-  int32_t tickets_per_unit;   // 1 + groups of kMergeGroup splits
+  int32_t tickets_per_unit;   // words: arrivals, pair claims, then one line per group of kMergeGroup splits
   int32_t max_splits;         // capacity of the partial records per unit
   // unit u < nR is retrieval KV head kv_of_unit[u]; unit nR+s is streaming
   // KV head kv_of_unit[nR+s]; index_of_kv[k] is k's index within its kind.
@@ -33,6 +34,16 @@ struct Geom {
   uint8_t index_of_kv[kMaxKvHeads];
   uint8_t is_retrieval[kMaxKvHeads];
 };
+
+static_assert(offsetof(Geom, kv_of_unit) % 4 == 0, "kv_of_unit is read as 32-bit words");
+
+// KV head of unit u.  Read as a 32-bit word of the kernel argument: for a
+// work-group-uniform u that is a scalar load, where a byte load of the
+// argument would be a vector memory round trip.
+__device__ __forceinline__ int kv_head_of_unit(const Geom& g, int u) {
+  const uint32_t w = reinterpret_cast<const uint32_t*>(g.kv_of_unit)[u >> 2];
+  return (int)((w >> (8 * (u & 3))) & 0xffu);
+}
 
 // Per-call sequence table: tokens already stored and tokens added.
 struct Seqs {
@@ -47,7 +58,7 @@ hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const 
                          int32_t chunk, int32_t max_n, hipStream_t s);
 
 struct DecodePlan {
-  int32_t split_tokens;      // rows per work-group (multiple of 64)
+  int32_t split_tokens;      // rows per work-group on average (a multiple of the pair rows)
   int32_t splits_r;          // max splits over retrieval units
   int32_t splits_s;          // max splits over streaming units
   int32_t head_chunk;        // query heads handled per work-group (divides G)
@@ -68,9 +79,21 @@ inline int decode_head_chunk(int G) {
   return 1;
 }
 
-// Decode splits are merged in groups of this many records, then the groups.
+// Decode splits arrive in groups of this many; the last arrival of each
+// group moves on to the unit's counter.  Every counter sits on its own
+// 128-byte line (kTicketStride words): atomics to one line are serialised
+// where they are performed.
 constexpr int kMergeGroup = 16;
-inline int32_t tickets_per_unit(int32_t max_splits) { return 1 + (max_splits + kMergeGroup - 1) / kMergeGroup; }
+constexpr int kTicketStride = 32;
+// per unit: the arrivals counter, the pair-claim counter, a counter per group
+inline int32_t tickets_per_unit(int32_t max_splits) {
+  return kTicketStride * (2 + (max_splits + kMergeGroup - 1) / kMergeGroup);
+}
+
+// Rows of a decode pair of batches (the unit of dynamic claiming): 4 waves,
+// 64 / (D/8) rows per wave load, 4 loads in flight per lane (2 for chunks of
+// 4 or more query heads), two batches.
+constexpr int decode_pair_rows(int D, int head_chunk) { return 2 * 4 * (64 / (D / 8)) * (head_chunk >= 4 ? 2 : 4); }
 
 // Split-K record capacity per (sequence, KV head, head chunk): enough for
 // splits of >= 256 rows, and at most 1024 / head_chunk records so that the

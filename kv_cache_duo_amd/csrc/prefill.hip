@@ -133,7 +133,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int n = sq.n[b];
   if (t * a.tq >= n) return;
   const int L = sq.len[b];
-  const int kvh = g.kv_of_unit[retrieval ? idx : g.nR + idx];
+  const int kvh = kv_head_of_unit(g, retrieval ? idx : g.nR + idx);
   const int64_t unit_rows = retrieval ? g.max_len : (int64_t)g.slots;
   const int64_t cache_off = ((int64_t)b * nkind + idx) * unit_rows * D;
   const uint16_t* ck = (retrieval ? g.rk : g.sk) + cache_off;
