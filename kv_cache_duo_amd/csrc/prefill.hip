@@ -18,9 +18,8 @@
 //     double-buffered LDS (global_load_lds_dwordx4, 1 KB per wave
 //     instruction) while the previous tile is computed; rows may be any mix
 //     of cache rows, ring slots and chunk rows.  Both tiles keep the natural
-//     [key][d] layout with the 16-byte granules of a row XOR-swizzled (K by
-//     row mod D/8, V by 2 * (row mod 4)), which keeps the operand reads below
-//     free of bank conflicts;
+//     [key][d] layout with the 16-byte granules of a row XOR-swizzled so that
+//     the operand reads below are free of bank conflicts;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = Q
 //     in registers, pre-multiplied by scale * log2 e): each lane holds 32
 //     scores of ONE query, so row max and sum need in-lane work plus one
@@ -68,6 +67,18 @@ struct PrefillArgs {
   int32_t n_hc;       // G / gh
   int32_t items_r;    // work-groups of retrieval heads
 };
+
+// LDS has 64 banks of 4 bytes; a wave's 16-byte reads are served 16 lanes
+// at a time, 8-byte reads 32 lanes at a time.  Granule swizzles (granule =
+// 16 bytes of a row) that keep the operand reads below conflict-free:
+//   K row r: granule g stored at g ^ k_swizzle(r)  (the 16 rows one read
+//     serves fall on 16 distinct 16-byte bank groups);
+//   V row r: granule g stored at g ^ v_swizzle(r)  (the 4 rows x 4 granules
+//     of a transposing read's 32 lanes do likewise).
+template <int D>
+__device__ __forceinline__ int k_swizzle(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int v_swizzle(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 
 template <int D>
 struct Lds {
@@ -192,8 +203,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // (finite) V row adds nothing.
   const int r0 = wave * RPC + lane / CH;
   const int pch = lane % CH;
-  const int gK = pch ^ (r0 & (CH - 1));
-  const int gV = pch ^ (2 * (r0 & 3));
+  const int gK = pch ^ k_swizzle<D>(r0);  // the swizzles of rows r0 + j*ROWS_J equal r0's
+  const int gV = pch ^ v_swizzle<D>(r0);
   auto ring_slot = [&](int kp) {  // valid for kp >= S
     return g.S + (kp - g.S) % g.W;
   };
@@ -235,14 +246,14 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
 
   // ---- LDS operand addresses (bytes inside a tile)
   // K rows kb2*32 + col, logical granule 2c + half
-  auto k_addr = [&](int kb2, int c) { return (kb2 * 32 + col) * LD::ROW + (((2 * c + half) ^ (col & (CH - 1))) * 16); };
+  auto k_addr = [&](int kb2, int c) { return (kb2 * 32 + col) * LD::ROW + (((2 * c + half) ^ k_swizzle<D>(col)) * 16); };
   // V^T operand of the 16-key step starting at key s16, rows d = db*32 + col:
   // lane l names key s16 + 8 t + 4 half + (l/4 mod 4), columns
   // db*32 + 16 ((l/16) mod 2) + 4 (l mod 4) .. +3, for t = 0, 1.
   const int vq = (lane >> 2) & 3;
   const int vg = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
   auto v_addr = [&](int s16, int tt, int db) {
-    return (s16 + 8 * tt + 4 * half + vq) * LD::ROW + (((4 * db + vg) ^ (2 * vq)) * 16) + 8 * (lane & 1);
+    return (s16 + 8 * tt + 4 * half + vq) * LD::ROW + (((4 * db + vg) ^ v_swizzle<D>(vq)) * 16) + 8 * (lane & 1);
   };
 
   // ---- softmax state: this lane's query (running max, partial l), O^T
