@@ -1,6 +1,7 @@
 // Measured hardware ceilings used as a second reference next to the vendor
 // peaks when the kernels' roofline fractions are reported:
 //   ceiling stream_read <MiB>  -- 16-byte streaming reads of a buffer (HBM)
+//   ceiling stream_read_rotating <MiB> <n> -- the same over n buffers in turn
 //   ceiling mfma               -- back-to-back v_mfma_f32_32x32x16_bf16
 // Standalone executable (not part of the C ABI); prints one JSON line.
 #include <hip/hip_runtime.h>
@@ -88,6 +89,40 @@ int run_stream_read(size_t mib) {
   return 0;
 }
 
+// One launch per buffer of `nbuf` separate buffers of `mib` MiB each, in
+// turn, so no launch finds its data in the 256 MB Infinity Cache: the rate
+// one launch of that size gets from HBM, launch ramp and drain included.
+int run_stream_read_rotating(size_t mib, int nbuf) {
+  const size_t bytes = mib << 20;
+  const unsigned blocks = (unsigned)(bytes / 16 / kSlab);
+  if (blocks == 0 || nbuf < 1 || nbuf > 64) return 2;
+  u32x4* p[64] = {};
+  unsigned* out = nullptr;
+  for (int i = 0; i < nbuf; ++i) {
+    if (!ok(hipMalloc(&p[i], (size_t)blocks * kSlab * 16), "hipMalloc")) return 1;
+    if (!ok(hipMemset(p[i], 1, (size_t)blocks * kSlab * 16), "hipMemset")) return 1;
+  }
+  if (!ok(hipMalloc(&out, blocks * 4), "hipMalloc")) return 1;
+  hipEvent_t a, b;
+  if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return 1;
+  const int launches = 16 * nbuf;
+  for (int i = 0; i < nbuf; ++i) hipLaunchKernelGGL(stream_read<true>, dim3(blocks), dim3(256), 0, 0, p[i], out);
+  (void)hipEventRecord(a, 0);
+  for (int r = 0; r < launches; ++r)
+    hipLaunchKernelGGL(stream_read<true>, dim3(blocks), dim3(256), 0, 0, p[r % nbuf], out);
+  (void)hipEventRecord(b, 0);
+  if (!ok(hipEventSynchronize(b), "sync")) return 1;
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, a, b);
+  const double us = ms * 1e3 / launches;
+  printf("{\"ceiling\": \"stream_read_rotating\", \"mib\": %zu, \"buffers\": %d, \"us_per_launch\": %.2f, "
+         "\"nontemporal_gbs\": %.1f}\n",
+         mib, nbuf, us, (double)blocks * kSlab * 16 / us / 1e3);
+  for (int i = 0; i < nbuf; ++i) (void)hipFree(p[i]);
+  (void)hipFree(out);
+  return 0;
+}
+
 int run_mfma() {
   int dev = 0, cus = 0;
   if (!ok(hipGetDevice(&dev), "device") ||
@@ -117,7 +152,9 @@ int run_mfma() {
 int main(int argc, char** argv) {
   if (argc >= 2 && std::strcmp(argv[1], "stream_read") == 0)
     return run_stream_read(argc >= 3 ? (size_t)std::atoll(argv[2]) : 4096);
+  if (argc >= 2 && std::strcmp(argv[1], "stream_read_rotating") == 0)
+    return run_stream_read_rotating(argc >= 3 ? (size_t)std::atoll(argv[2]) : 132, argc >= 4 ? std::atoi(argv[3]) : 8);
   if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma();
-  fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling mfma\n");
+  fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling stream_read_rotating <MiB> <buffers> | ceiling mfma\n");
   return 2;
 }
