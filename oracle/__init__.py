@@ -18,9 +18,12 @@ pages this project was built from):
   for the cache size or for sink handling, so those steps follow the readings
   listed in ``mixed_attention`` and ``cache_state``.
 
-Every function here is pinned by ``tests/test_oracle.py`` against closed
-forms, a library routine (torch fp64 scaled-dot-product attention), brute
-force on tiny inputs and hand-derived fixtures under ``tests/golden/``.
+Every function here is pinned by ``tests/test_oracle.py`` and
+``tests/test_oracle_quant.py`` against closed forms, a library routine (torch
+fp64 scaled-dot-product attention), brute force on tiny inputs and
+hand-derived fixtures under ``tests/golden/``.  ``quantized_cache`` adds the
+int8 retrieval cache the pages allude to ("combined with quantization",
+abstract), with the scheme taken as a stated reading.
 """
 
 from .mixed_attention import (  # noqa: F401
@@ -33,4 +36,9 @@ from .cache_state import (  # noqa: F401
     CacheSimulator,
     streaming_slot_of_position,
     streaming_slot_positions,
+)
+from .quantized_cache import (  # noqa: F401
+    dequantize_rows,
+    quantize_rows,
+    seen_rows,
 )
