@@ -58,6 +58,20 @@ typedef enum duo_status {
   DUO_ERR_HIP = 5               /* a HIP launch failed (hipGetLastError) */
 } duo_status;
 
+/* Storage format of the retrieval heads' cached K and V rows.
+ *   DUO_KV_BF16: bf16 rows, as the inputs.
+ *   DUO_KV_INT8: one int8 code per element and one fp32 scale per row (a row
+ *     is the head_dim values of one sequence, KV head and position).  The
+ *     pages only say that DuoAttention reaches a 3.3M-token context combined
+ *     with quantization (abstract on the pith.science review page); the
+ *     scheme is this library's reading: scale = max|x| / 127 and code =
+ *     clamp(rint(x / scale), -127, 127), both in fp32 with round to nearest
+ *     even (a zero row: scale 0, codes 0); stored as the byte code + 128.
+ *     A call attends to rows stored by earlier calls through code * scale,
+ *     and to the rows of its own chunk (or decode token) as given.
+ * Streaming heads' caches are bf16 in both formats. */
+typedef enum duo_kv_format { DUO_KV_BF16 = 0, DUO_KV_INT8 = 1 } duo_kv_format;
+
 /* Configuration of one attention layer's cache. */
 typedef struct duo_config {
   int32_t batch;        /* B, 1..DUO_MAX_BATCH sequences */
@@ -69,6 +83,7 @@ typedef struct duo_config {
   int32_t recent;       /* W >= 1 recent positions kept by streaming heads */
   float scale;          /* softmax scale; 0 selects 1/sqrt(head_dim) */
   const uint8_t* kv_head_is_retrieval; /* HOST [Hkv]: nonzero = retrieval; copied */
+  int32_t kv_format;    /* duo_kv_format of the retrieval cache */
 } duo_config;
 
 /* Opaque host-side handle: configuration, head maps, region offsets and the
@@ -81,6 +96,9 @@ typedef struct duo_cache duo_cache;
  * (in increasing k), likewise for streaming heads.
  *   lengths  int32 [B]                     tokens stored per sequence
  *   rk, rv   bf16  [B][nR][max_len][D]     retrieval cache, row = position
+ *            (DUO_KV_INT8: uint8 codes, same shape)
+ *   rks, rvs fp32  [B][nR][max_len]        DUO_KV_INT8 only: row scales
+ *            (offset -1 for DUO_KV_BF16)
  *   sk, sv   bf16  [B][nS][sink+recent][D] streaming cache, slot map:
  *            slot(p) = p for p < sink, else sink + (p - sink) mod recent
  *   work     uint32 split counters and fp32 split-K partial results of
@@ -93,7 +111,8 @@ typedef struct duo_layout {
   int64_t total_bytes;
   int32_t n_retrieval, n_streaming;
   int32_t slots_per_streaming_head; /* sink + recent */
-  int32_t reserved;
+  int32_t kv_format;                /* duo_kv_format */
+  int64_t rks_offset, rvs_offset;
 } duo_layout;
 
 /* Lay out a new, empty cache in `dev_buf`.
@@ -103,7 +122,8 @@ typedef struct duo_layout {
  * counters are zeroed on `stream` by a fill kernel; *out gets a new handle.
  * Errors: INVALID_ARG (null cfg / mask / out, B < 1, Hkv < 1, Hq % Hkv != 0,
  * sink < 0, recent < 1, max_len < 1, misaligned dev_buf, scale < 0 or not
- * finite), UNSUPPORTED (head_dim, batch), BUFFER_TOO_SMALL, HIP. */
+ * finite, kv_format not a duo_kv_format), UNSUPPORTED (head_dim, batch),
+ * BUFFER_TOO_SMALL, HIP. */
 duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
                           size_t* required_bytes, duo_cache** out, void* stream);
 

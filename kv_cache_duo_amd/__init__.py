@@ -38,6 +38,9 @@ DUO_ERR_HIP = 5
 DUO_MAX_BATCH = 128
 
 
+DUO_KV_BF16, DUO_KV_INT8 = 0, 1
+
+
 class DuoError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -50,6 +53,7 @@ class _Config(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("max_len", ctypes.c_int64), ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
         ("scale", ctypes.c_float), ("kv_head_is_retrieval", ctypes.POINTER(ctypes.c_uint8)),
+        ("kv_format", ctypes.c_int32),
     ]
 
 
@@ -60,7 +64,8 @@ class Layout(ctypes.Structure):
         ("sv_offset", ctypes.c_int64), ("work_offset", ctypes.c_int64),
         ("work_bytes", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
         ("n_retrieval", ctypes.c_int32), ("n_streaming", ctypes.c_int32),
-        ("slots_per_streaming_head", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("slots_per_streaming_head", ctypes.c_int32), ("kv_format", ctypes.c_int32),
+        ("rks_offset", ctypes.c_int64), ("rvs_offset", ctypes.c_int64),
     ]
 
 
@@ -129,13 +134,14 @@ class Config:
     recent: int
     kv_head_is_retrieval: Sequence[int]
     scale: float = 0.0
+    kv_format: int = 0  # DUO_KV_BF16; DUO_KV_INT8 = 1 stores retrieval rows as int8 + fp32 row scales
 
     def _c(self):
         mask = (ctypes.c_uint8 * max(len(self.kv_head_is_retrieval), 1))(
             *[1 if x else 0 for x in self.kv_head_is_retrieval])
         c = _Config(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim, self.max_len,
                     self.sink, self.recent, self.scale,
-                    ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)))
+                    ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)), self.kv_format)
         return c, mask  # keep the mask alive for the call
 
 
@@ -257,7 +263,8 @@ def duo_decode(cache: Cache, q, k, v, out, stream=None) -> None:
 
 def cache_views(cache: Cache):
     """Typed views of the regions of a cache's device buffer (for tests and
-    checkpointing): lengths int32 [B], rk/rv [B,nR,max_len,D], sk/sv
+    checkpointing): lengths int32 [B], rk/rv [B,nR,max_len,D] (bf16, or uint8
+    codes with rks/rvs fp32 [B,nR,max_len] row scales for DUO_KV_INT8), sk/sv
     [B,nS,sink+recent,D] as bf16."""
     cfg, lay, buf = cache.cfg, cache.layout(), cache.buf
     if buf is None:
@@ -271,12 +278,18 @@ def cache_views(cache: Cache):
         nbytes *= torch.tensor([], dtype=dtype).element_size()
         return buf[off:off + nbytes].view(dtype).view(*shape)
 
-    return {
+    rdt = torch.uint8 if lay.kv_format == DUO_KV_INT8 else torch.bfloat16
+    rshape = (cfg.batch, lay.n_retrieval, cfg.max_len, d)
+    views = {
         "lengths": region(lay.lengths_offset, (cfg.batch,), torch.int32),
-        "rk": region(lay.rk_offset, (cfg.batch, lay.n_retrieval, cfg.max_len, d), torch.bfloat16),
-        "rv": region(lay.rv_offset, (cfg.batch, lay.n_retrieval, cfg.max_len, d), torch.bfloat16),
+        "rk": region(lay.rk_offset, rshape, rdt),
+        "rv": region(lay.rv_offset, rshape, rdt),
         "sk": region(lay.sk_offset, (cfg.batch, lay.n_streaming, lay.slots_per_streaming_head, d),
                      torch.bfloat16),
         "sv": region(lay.sv_offset, (cfg.batch, lay.n_streaming, lay.slots_per_streaming_head, d),
                      torch.bfloat16),
     }
+    if lay.kv_format == DUO_KV_INT8:
+        views["rks"] = region(lay.rks_offset, rshape[:3], torch.float32)
+        views["rvs"] = region(lay.rvs_offset, rshape[:3], torch.float32)
+    return views

@@ -8,6 +8,8 @@
 //   recent -- which overwrites (evicts) the token `recent` positions older.
 // Within one call only the last `recent` non-sink positions of a chunk are
 // written to the ring: older ones would be overwritten by the same call.
+// With an int8 retrieval cache (duo_kv_format DUO_KV_INT8) retrieval rows
+// are quantized as they are stored.
 #include "device_util.h"
 #include "duo_internal.h"
 
@@ -79,8 +81,17 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
       dv = g.sv + row * D;
     }
     int64_t src = (((int64_t)b * chunk + i) * g.Hkv + kvh) * D;
-    reinterpret_cast<uint4*>(dk)[c] = reinterpret_cast<const uint4*>(k + src)[c];
-    reinterpret_cast<uint4*>(dv)[c] = reinterpret_cast<const uint4*>(v + src)[c];
+    const uint4 kx = reinterpret_cast<const uint4*>(k + src)[c];
+    const uint4 vx = reinterpret_cast<const uint4*>(v + src)[c];
+    if (retrieval && g.kv_int8) {
+      // int8 row: the CH lanes of the row agree on its scale (group max)
+      const int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + p;
+      store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rk) + row * D, g.rks + row, kx, c);
+      store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rv) + row * D, g.rvs + row, vx, c);
+    } else {
+      reinterpret_cast<uint4*>(dk)[c] = kx;
+      reinterpret_cast<uint4*>(dv)[c] = vx;
+    }
   }
 }
 

@@ -257,7 +257,12 @@ __device__ void merge_records(const Geom& g, const DecodeArgs& a, char* lds, flo
   }
 }
 
-template <int D, int GC>
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+// Q8: the cache's retrieval rows are int8 codes with fp32 row scales
+// (DUO_KV_INT8); streaming units of the same launch stay bf16.
+template <int D, int GC, bool Q8>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, DecodeArgs a) {
   constexpr int LPR = D / 8;                  // lanes per row (8 bf16 each)
   constexpr int RPW = 64 / LPR;               // rows per wave per load
@@ -405,14 +410,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // While a pair's two batches are processed, the next pair's loads go out
   // batch by batch, and the claim for the pair after it is in flight.  The
   // claim reaches the other waves through a double-buffered LDS slot (one
-  // barrier per pair).
+  // barrier per pair).  `rows` bounds the streamed rows, `npr` the pairs;
+  // past the last pair the loads re-read the last row (cached):
+  // unconditional loads keep the outstanding-load count static.
   __shared__ int sm_claim[2];
   bool own_new = false;  // this work-group's rows hold the new token
-  {
-    uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
+  auto stream_pairs = [&](auto& ka, auto& va, auto& kb, auto& vb, auto&& ld, auto&& pr, int rows, int npr)
+      __attribute__((always_inline)) {
     int base = split * PAIR;
-    load(ka, va, base);
-    load(kb, vb, base + ROWS_ITER);
+    ld(ka, va, base);
+    ld(kb, vb, base + ROWS_ITER);
     for (int it = 0;; it ^= 1) {
       if (threadIdx.x == 0) {
         sm_claim[it] = ns + (int)claimed;
@@ -420,18 +427,137 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       }
       __syncthreads();
       const int p_next = __builtin_amdgcn_readfirstlane(sm_claim[it]);
-      const bool more = p_next < npairs;
-      // past the last pair the loads re-read the unit's last row (cached);
-      // unconditional loads keep the outstanding-load count static
-      const int nbase = more ? p_next * PAIR : T;
-      process(ka, va, base);
-      load(ka, va, nbase);
-      process(kb, vb, base + ROWS_ITER);
-      load(kb, vb, nbase + ROWS_ITER);
+      const bool more = p_next < npr;
+      const int nbase = more ? p_next * PAIR : rows;
+      pr(ka, va, base);
+      ld(ka, va, nbase);
+      pr(kb, vb, base + ROWS_ITER);
+      ld(kb, vb, nbase + ROWS_ITER);
       own_new = own_new || (new_row >= base && new_row < base + PAIR);
       if (!more) break;
       base = nbase;
     }
+  };
+  auto stream_bf16 = [&]() __attribute__((always_inline)) {
+    uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
+    stream_pairs(ka, va, kb, vb, load, process, T, npairs);
+  };
+  const bool q8 = Q8 && retrieval;
+  if constexpr (Q8) {
+    if (retrieval) {
+      // int8 rows 0..L-1 of the cache (a lane: 8 codes, its row's scale in
+      // .z); the new token (row L) is taken from the input below
+      const int Tc = L;
+      const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + ((int64_t)b * g.nR + idx) * g.max_len * D;
+      const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + ((int64_t)b * g.nR + idx) * g.max_len * D;
+      const float* cks = g.rks + ((int64_t)b * g.nR + idx) * g.max_len;
+      const float* cvs = g.rvs + ((int64_t)b * g.nR + idx) * g.max_len;
+      float qf[GC][8], qoff[GC], cacc[GC];
+#pragma unroll
+      for (int gg = 0; gg < GC; ++gg) {
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qf[gg][2 * e] = bf16_lo(qw[gg][e]);
+          qf[gg][2 * e + 1] = bf16_hi(qw[gg][e]);
+          sum += qf[gg][2 * e] + qf[gg][2 * e + 1];
+        }
+        qoff[gg] = -128.0f * sum;  // codes are stored as code + 128
+        cacc[gg] = 0.f;            // sum of p * scale_v, for the same offset in o
+      }
+      auto load8 = [&](u32x4_t (&kr)[kInFlight], u32x4_t (&vr)[kInFlight], int base) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+          const int row = min(row_of(base, j), Tc - 1);
+          const u32x2_t kc = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ck8 + (int64_t)row * D) + c);
+          const u32x2_t vc = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(cv8 + (int64_t)row * D) + c);
+          kr[j] = u32x4_t{kc.x, kc.y, __float_as_uint(cks[row]), 0u};
+          vr[j] = u32x4_t{vc.x, vc.y, __float_as_uint(cvs[row]), 0u};
+        }
+      };
+      auto process8 = [&](const u32x4_t (&kr)[kInFlight], const u32x4_t (&vr)[kInFlight], int base)
+          __attribute__((always_inline)) {
+        float s[kInFlight][GC];
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+          const bool valid = row_of(base, j) < Tc;
+          float ku[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ku[e] = (float)((kr[j][e >> 2] >> (8 * (e & 3))) & 0xffu);
+#pragma unroll
+          for (int gg = 0; gg < GC; ++gg) {
+            float acc = qoff[gg];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc = fmaf(ku[e], qf[gg][e], acc);
+            acc = group_sum<LPR>(acc);
+            s[j][gg] = valid ? acc * (__uint_as_float(kr[j].z) * g.scale_log2) : -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int gg = 0; gg < GC; ++gg) {
+          float mx = s[0][gg];
+#pragma unroll
+          for (int j = 1; j < kInFlight; ++j) mx = fmaxf(mx, s[j][gg]);
+          const float mn = fmaxf(m[gg], mx);
+          const float mu = max_or_zero(mn);
+          const float alpha = exp2_fast(m[gg] - mu);
+          l[gg] *= alpha;
+          cacc[gg] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[gg][e] *= alpha;
+#pragma unroll
+          for (int j = 0; j < kInFlight; ++j) {
+            const float p = exp2_fast(s[j][gg] - mu);
+            const float pv = p * __uint_as_float(vr[j].z);
+            l[gg] += p;
+            cacc[gg] += pv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              o[gg][e] = fmaf(pv, (float)((vr[j][e >> 2] >> (8 * (e & 3))) & 0xffu), o[gg][e]);
+          }
+          m[gg] = mn;
+        }
+      };
+      if (Tc > 0) {
+        u32x4_t ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
+        stream_pairs(ka, va, kb, vb, load8, process8, Tc, (Tc + PAIR - 1) / PAIR);
+      }
+#pragma unroll
+      for (int gg = 0; gg < GC; ++gg)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[gg][e] = fmaf(-128.0f, cacc[gg], o[gg][e]);
+      // The new token, at input precision: work-group 0, one lane group.
+      own_new = split == 0;
+      if (own_new) {
+        const uint4 kx = reinterpret_cast<const uint4*>(nk)[c];
+        const uint4 vx = reinterpret_cast<const uint4*>(nv)[c];
+        const bool mine = wave == 0 && grp == 0;
+        const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w}, vw[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+        for (int gg = 0; gg < GC; ++gg) {
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc = dot2_bf16(kw[e], qw[gg][e], acc);
+          acc = group_sum<LPR>(acc);
+          const float sc = mine ? acc * g.scale_log2 : -INFINITY;
+          const float mn = fmaxf(m[gg], sc);
+          const float mu = max_or_zero(mn);
+          const float alpha = exp2_fast(m[gg] - mu);
+          const float p = exp2_fast(sc - mu);
+          l[gg] = l[gg] * alpha + p;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[gg][2 * e] = fmaf(p, bf16_lo(vw[e]), o[gg][2 * e] * alpha);
+            o[gg][2 * e + 1] = fmaf(p, bf16_hi(vw[e]), o[gg][2 * e + 1] * alpha);
+          }
+          m[gg] = mn;
+        }
+      }
+    } else {
+      stream_bf16();
+    }
+  } else {
+    stream_bf16();
   }
 
   // ---- merge the row groups of the wave (same head, different rows)
@@ -468,9 +594,17 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 
   // ---- the owner of the new token stores it (one head chunk does it)
   if (hc == 0 && own_new && threadIdx.x < LPR) {
-    const int64_t off = (int64_t)new_row * D;
-    reinterpret_cast<uint4*>(ck + off)[threadIdx.x] = reinterpret_cast<const uint4*>(nk)[threadIdx.x];
-    reinterpret_cast<uint4*>(cv + off)[threadIdx.x] = reinterpret_cast<const uint4*>(nv)[threadIdx.x];
+    const uint4 kx = reinterpret_cast<const uint4*>(nk)[threadIdx.x];
+    const uint4 vx = reinterpret_cast<const uint4*>(nv)[threadIdx.x];
+    if (q8) {
+      const int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + new_row;
+      store_int8_row<LPR>(reinterpret_cast<uint8_t*>(g.rk) + row * D, g.rks + row, kx, threadIdx.x);
+      store_int8_row<LPR>(reinterpret_cast<uint8_t*>(g.rv) + row * D, g.rvs + row, vx, threadIdx.x);
+    } else {
+      const int64_t off = (int64_t)new_row * D;
+      reinterpret_cast<uint4*>(ck + off)[threadIdx.x] = kx;
+      reinterpret_cast<uint4*>(cv + off)[threadIdx.x] = vx;
+    }
     if (threadIdx.x == 0 && kvh == 0) g.lengths[b] = L + 1;
   }
   __syncthreads();
@@ -602,10 +736,13 @@ hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p, cons
   const int64_t items = (int64_t)g.B * g.nR * n_hc * p.splits_r + (int64_t)g.B * g.nS * n_hc * p.splits_s;
   if (items <= 0) return hipSuccess;
   const dim3 grid((unsigned)items), block(kThreads);
-#define DUO_DECODE_CASE(DD, GG)                                              \
-  if (g.D == DD && p.head_chunk == GG) {                                     \
-    hipLaunchKernelGGL((decode_kernel<DD, GG>), grid, block, 0, s, g, q, a); \
-    return hipGetLastError();                                                \
+#define DUO_DECODE_CASE(DD, GG)                                                     \
+  if (g.D == DD && p.head_chunk == GG) {                                            \
+    if (g.kv_int8)                                                                  \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), grid, block, 0, s, g, q, a);  \
+    else                                                                            \
+      hipLaunchKernelGGL((decode_kernel<DD, GG, false>), grid, block, 0, s, g, q, a); \
+    return hipGetLastError();                                                       \
   }
   DUO_DECODE_CASE(128, 1)
   DUO_DECODE_CASE(128, 2)

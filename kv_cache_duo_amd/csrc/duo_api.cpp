@@ -40,6 +40,7 @@ duo_status check_config(const duo_config* c) {
   if (c->sink < 0 || c->recent < 1 || c->max_len < 1) return DUO_ERR_INVALID_ARG;
   if (!(c->scale >= 0.f) || !std::isfinite(c->scale)) return DUO_ERR_INVALID_ARG;
   if (c->kv_head_is_retrieval == nullptr) return DUO_ERR_INVALID_ARG;
+  if (c->kv_format != DUO_KV_BF16 && c->kv_format != DUO_KV_INT8) return DUO_ERR_INVALID_ARG;
   if (c->head_dim != 64 && c->head_dim != 128) return DUO_ERR_UNSUPPORTED;
   if (c->batch > DUO_MAX_BATCH || c->num_kv_heads > duo::kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
   if (c->max_len > kMaxLen || (int64_t)c->sink + c->recent > kMaxLen) return DUO_ERR_UNSUPPORTED;
@@ -70,6 +71,7 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
     g->kv_of_unit[g->is_retrieval[k] ? g->index_of_kv[k] : nr + g->index_of_kv[k]] = (uint8_t)k;
   g->nR = nr;
   g->nS = ns;
+  g->kv_int8 = c->kv_format == DUO_KV_INT8;
   g->max_splits = duo::max_splits_for(c->max_len, g->slots, duo::decode_head_chunk(g->G));
 
   const int gc = duo::decode_head_chunk(g->G);
@@ -83,10 +85,19 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   off = align_up(off + 4 * units * g->max_splits * gc * (g->D + 2));
   L->work_bytes = off - L->work_offset;
   const int64_t row = 2 * (int64_t)g->D;
+  const int64_t rrow = g->kv_int8 ? (int64_t)g->D : row;  // retrieval row bytes
+  L->kv_format = c->kv_format;
   L->rk_offset = off;
-  off = align_up(off + (int64_t)g->B * nr * g->max_len * row);
+  off = align_up(off + (int64_t)g->B * nr * g->max_len * rrow);
   L->rv_offset = off;
-  off = align_up(off + (int64_t)g->B * nr * g->max_len * row);
+  off = align_up(off + (int64_t)g->B * nr * g->max_len * rrow);
+  L->rks_offset = L->rvs_offset = -1;
+  if (g->kv_int8) {
+    L->rks_offset = off;
+    off = align_up(off + (int64_t)g->B * nr * g->max_len * 4);
+    L->rvs_offset = off;
+    off = align_up(off + (int64_t)g->B * nr * g->max_len * 4);
+  }
   L->sk_offset = off;
   off = align_up(off + (int64_t)g->B * ns * g->slots * row);
   L->sv_offset = off;
@@ -105,6 +116,8 @@ void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units * g->tickets_per_unit));
   g->rk = reinterpret_cast<uint16_t*>(base + L.rk_offset);
   g->rv = reinterpret_cast<uint16_t*>(base + L.rv_offset);
+  g->rks = L.rks_offset >= 0 ? reinterpret_cast<float*>(base + L.rks_offset) : nullptr;
+  g->rvs = L.rvs_offset >= 0 ? reinterpret_cast<float*>(base + L.rvs_offset) : nullptr;
   g->sk = reinterpret_cast<uint16_t*>(base + L.sk_offset);
   g->sv = reinterpret_cast<uint16_t*>(base + L.sv_offset);
 }

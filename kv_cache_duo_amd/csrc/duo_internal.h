@@ -17,10 +17,13 @@ struct Geom {
   int32_t B, Hq, Hkv, G, D;
   int32_t S, W, slots;        // sink, recent, sink+recent
   int32_t nR, nS;             // retrieval / streaming KV heads
+  int32_t kv_int8;            // retrieval rows stored as int8 codes + fp32 scales
   int64_t max_len;
   float scale_log2;           // softmax scale * log2(e): scores in base-2 units
-  uint16_t* rk;               // bf16 bits [B][nR][max_len][D]
+  uint16_t* rk;               // bf16 bits [B][nR][max_len][D] (kv_int8: uint8 codes, D bytes per row)
   uint16_t* rv;
+  float* rks;                 // kv_int8: fp32 row scales [B][nR][max_len] of rk / rv
+  float* rvs;
   uint16_t* sk;               // bf16 bits [B][nS][slots][D]
   uint16_t* sv;
   int32_t* lengths;           // [B]

@@ -49,6 +49,8 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
@@ -113,7 +115,10 @@ __device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
   return pack_bf16x2(bf16_lo(w) * s, bf16_hi(w) * s);
 }
 
-template <int D>
+// Q8: the retrieval cache holds int8 rows (DUO_KV_INT8) and some sequence
+// has a stored prefix; tiles with stored retrieval rows are then staged
+// through registers and dequantized into the bf16 LDS layout.
+template <int D, bool Q8>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   using LD = Lds<D>;
@@ -177,7 +182,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     }
   }
   const int ntiles = tA + (tB1 - tB0 + 1);
-  auto tile_of = [&](int k) { return k < tA ? k : tB0 + (k - tA); };
+  auto tile_of = [&](int k) __attribute__((always_inline)) { return k < tA ? k : tB0 + (k - tA); };
 
   // ---- Q operand (B of S^T = K Q^T), scaled by scale * log2 e: lane holds
   // row `col`, k slice `half`
@@ -205,11 +210,11 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int pch = lane % CH;
   const int gK = pch ^ k_swizzle<D>(r0);  // the swizzles of rows r0 + j*ROWS_J equal r0's
   const int gV = pch ^ v_swizzle<D>(r0);
-  auto ring_slot = [&](int kp) {  // valid for kp >= S
+  auto ring_slot = [&](int kp) __attribute__((always_inline)) {  // valid for kp >= S
     return g.S + (kp - g.S) % g.W;
   };
   // Element offset of position kp's row and whether it comes from the cache.
-  auto row_src = [&](int kp, int64_t& off, bool& from_cache) {
+  auto row_src = [&](int kp, int64_t& off, bool& from_cache) __attribute__((always_inline)) {
     const bool in_chunk = kp >= L;
     const bool ok = kp <= qmax && (in_chunk || retrieval || kp < g.S || kp >= L - g.W);
     const int64_t cache_row = (retrieval || kp < g.S) ? (int64_t)kp : (int64_t)ring_slot(kp);
@@ -219,9 +224,49 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   };
   const int koff_in = r0 * in_stride + gK * 8, koff_c = r0 * D + gK * 8;
   const int voff_in = r0 * in_stride + gV * 8, voff_c = r0 * D + gV * 8;
-  auto load_tile = [&](int tile, int buf_off) {
+  // int8 retrieval rows (Q8): codes of granule g of row r at byte
+  // r*D + 8g, row scales apart; a staged tile's 16-byte granules wait in
+  // kst / vst (bit j of q8rows: row j holds codes + scale in .x .y .z).
+  const uint8_t* ck8 = nullptr;
+  const uint8_t* cv8 = nullptr;
+  const float* cks = nullptr;
+  const float* cvs = nullptr;
+  if constexpr (Q8) {
+    const int64_t r8 = ((int64_t)b * g.nR + idx) * g.max_len;
+    ck8 = reinterpret_cast<const uint8_t*>(g.rk) + r8 * D;
+    cv8 = reinterpret_cast<const uint8_t*>(g.rv) + r8 * D;
+    cks = g.rks + r8;
+    cvs = g.rvs + r8;
+  }
+  u32x4_t kst[Q8 ? NJ : 1], vst[Q8 ? NJ : 1];
+  uint32_t q8rows = 0;
+  auto load_tile = [&](int tile, int buf_off) -> bool __attribute__((always_inline)) {  // true: staged, store_tile to follow
     const int k0 = tile * kBN;
     const int dst = buf_off + wave * 1024;
+    if constexpr (Q8) {
+      if (retrieval && k0 < L) {
+        q8rows = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          // a retrieval row: stored (kp < L), in the chunk, or past qmax
+          // (unusable: chunk row 0 instead, as in row_src)
+          const int kp = k0 + r0 + j * ROWS_J;
+          const bool from_cache = kp < L;
+          const int64_t off = (kp >= L && kp <= qmax) ? in_base + (int64_t)(kp - L) * in_stride : in_base;
+          if (from_cache) {  // retrieval cache row kp
+            const u32x2_t kc = *reinterpret_cast<const u32x2_t*>(ck8 + (int64_t)kp * D + gK * 8);
+            const u32x2_t vc = *reinterpret_cast<const u32x2_t*>(cv8 + (int64_t)kp * D + gV * 8);
+            kst[j] = u32x4_t{kc.x, kc.y, __float_as_uint(cks[kp]), 0u};
+            vst[j] = u32x4_t{vc.x, vc.y, __float_as_uint(cvs[kp]), 0u};
+            q8rows |= 1u << j;
+          } else {
+            kst[j] = *reinterpret_cast<const u32x4_t*>(a.k + off + gK * 8);
+            vst[j] = *reinterpret_cast<const u32x4_t*>(a.v + off + gV * 8);
+          }
+        }
+        return true;
+      }
+    }
     const bool all_in = k0 >= L && k0 + kBN - 1 <= qmax;   // every row in the chunk
     const bool all_cache = retrieval && k0 + kBN - 1 < L;  // every row cached
     if (all_in || all_cache) {
@@ -232,7 +277,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       for (int j = 0; j < NJ; ++j) global_to_lds16(kb + j * ROWS_J * stride, dst + j * kWaves * 1024);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) global_to_lds16(vb + j * ROWS_J * stride, dst + LD::TILE + j * kWaves * 1024);
-      return;
+      return false;
     }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
@@ -242,17 +287,39 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       global_to_lds16((from_cache ? ck : a.k) + off + gK * 8, dst + j * kWaves * 1024);
       global_to_lds16((from_cache ? cv : a.v) + off + gV * 8, dst + LD::TILE + j * kWaves * 1024);
     }
+    return false;
+  };
+  // Write a staged tile: int8 granules become code * scale rounded to bf16.
+  auto store_tile = [&](int buf_off) __attribute__((always_inline)) {
+    auto granule = [&](const u32x4_t& x, bool q8) -> u32x4_t __attribute__((always_inline)) {
+      if (!q8) return x;
+      const float sc = __uint_as_float(x.z);
+      uint32_t w[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t cw = x[e >> 1] >> (16 * (e & 1));
+        w[e] = pack_bf16x2(((float)(cw & 0xffu) - 128.0f) * sc, ((float)((cw >> 8) & 0xffu) - 128.0f) * sc);
+      }
+      return u32x4_t{w[0], w[1], w[2], w[3]};
+    };
+    char* dst = prefill_smem + buf_off + wave * 1024 + lane * 16;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const bool q8 = (q8rows >> j) & 1u;
+      *reinterpret_cast<u32x4_t*>(dst + j * kWaves * 1024) = granule(kst[j], q8);
+      *reinterpret_cast<u32x4_t*>(dst + LD::TILE + j * kWaves * 1024) = granule(vst[j], q8);
+    }
   };
 
   // ---- LDS operand addresses (bytes inside a tile)
   // K rows kb2*32 + col, logical granule 2c + half
-  auto k_addr = [&](int kb2, int c) { return (kb2 * 32 + col) * LD::ROW + (((2 * c + half) ^ k_swizzle<D>(col)) * 16); };
+  auto k_addr = [&](int kb2, int c) __attribute__((always_inline)) { return (kb2 * 32 + col) * LD::ROW + (((2 * c + half) ^ k_swizzle<D>(col)) * 16); };
   // V^T operand of the 16-key step starting at key s16, rows d = db*32 + col:
   // lane l names key s16 + 8 t + 4 half + (l/4 mod 4), columns
   // db*32 + 16 ((l/16) mod 2) + 4 (l mod 4) .. +3, for t = 0, 1.
   const int vq = (lane >> 2) & 3;
   const int vg = 2 * ((lane >> 4) & 1) + ((lane >> 1) & 1);
-  auto v_addr = [&](int s16, int tt, int db) {
+  auto v_addr = [&](int s16, int tt, int db) __attribute__((always_inline)) {
     return (s16 + 8 * tt + 4 * half + vq) * LD::ROW + (((4 * db + vg) ^ v_swizzle<D>(vq)) * 16) + 8 * (lane & 1);
   };
 
@@ -271,10 +338,10 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   for (int r = 0; r < 16; ++r) negm[r] = 0.f;
   const uint32_t ones = 0x3f803f80u;  // bf16 pair (1, 1)
 
-  auto compute_tile = [&](int kt, auto cur_c) {
+  auto compute_tile = [&](int kt, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
     const int k0 = tile_of(kt) * kBN;
-    if (kt + 1 < ntiles) load_tile(tile_of(kt + 1), (cur ^ 1) * LD::BUF);
+    const bool staged = kt + 1 < ntiles && load_tile(tile_of(kt + 1), (cur ^ 1) * LD::BUF);
 
     // wave-uniform: can the block see a key of this tile, and does any key
     // need a mask (causal diagonal, or outside the streaming band)
@@ -350,11 +417,14 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           }
         }
     }
+    if constexpr (Q8) {
+      if (staged) store_tile((cur ^ 1) * LD::BUF);
+    }
     __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next tile
     __syncthreads();
   };
 
-  load_tile(tile_of(0), 0);
+  if (load_tile(tile_of(0), 0)) store_tile(0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < ntiles; kt += 2) {
@@ -385,11 +455,11 @@ int heads_per_group(int G) {
   return 1;
 }
 
-template <int D>
+template <int D, bool Q8>
 hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, Q8>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Lds<D>::TOTAL);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -399,7 +469,7 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
   a.items_r = a.tiles_max * g.B * g.nR * a.n_hc;
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * g.B * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<D>), dim3((unsigned)blocks), dim3(kThreads), Lds<D>::TOTAL, s, g, q, a);
+  hipLaunchKernelGGL((prefill_kernel<D, Q8>), dim3((unsigned)blocks), dim3(kThreads), Lds<D>::TOTAL, s, g, q, a);
   return hipGetLastError();
 }
 
@@ -416,7 +486,12 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   a.chunk = chunk;
   a.gh = heads_per_group(g.G);
   a.n_hc = g.G / a.gh;
-  return g.D == 128 ? launch_t<128>(g, q, a, max_n, s) : launch_t<64>(g, q, a, max_n, s);
+  // int8 retrieval rows are only read from a stored prefix
+  bool prefix = false;
+  for (int b = 0; b < g.B; ++b) prefix = prefix || (q.n[b] > 0 && q.len[b] > 0);
+  if (g.kv_int8 && g.nR > 0 && prefix)
+    return g.D == 128 ? launch_t<128, true>(g, q, a, max_n, s) : launch_t<64, true>(g, q, a, max_n, s);
+  return g.D == 128 ? launch_t<128, false>(g, q, a, max_n, s) : launch_t<64, false>(g, q, a, max_n, s);
 }
 
 }  // namespace duo

@@ -124,6 +124,30 @@ def test_layout_and_head_index():
     assert c.head_index() == [0, 0, 1, 1]
 
 
+def test_int8_layout():
+    """DUO_KV_INT8: retrieval rows of D bytes plus fp32 row-scale regions;
+    streaming regions unchanged; the bf16 layout reports no scale regions."""
+    cfg = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], kv_format=duo.DUO_KV_INT8)
+    c = _attach(cfg, [5, 7])
+    lay = c.layout()
+    assert lay.kv_format == duo.DUO_KV_INT8
+    offs = [lay.lengths_offset, lay.work_offset, lay.rk_offset, lay.rv_offset, lay.rks_offset, lay.rvs_offset,
+            lay.sk_offset, lay.sv_offset]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    assert lay.rv_offset - lay.rk_offset >= cfg.batch * 2 * cfg.max_len * cfg.head_dim
+    assert lay.rks_offset - lay.rv_offset >= cfg.batch * 2 * cfg.max_len * cfg.head_dim
+    assert lay.sk_offset - lay.rvs_offset >= cfg.batch * 2 * cfg.max_len * 4
+    bf = _attach(_cfg(kv_head_is_retrieval=[0, 1, 1, 0]), [5, 7]).layout()
+    assert bf.kv_format == duo.DUO_KV_BF16 and bf.rks_offset == -1 and bf.rvs_offset == -1
+    # retrieval bytes: D + 4 per row and tensor instead of 2 D
+    r8 = (lay.sk_offset - lay.rk_offset)
+    r16 = (bf.sk_offset - bf.rk_offset)
+    assert r8 < r16 * 0.6
+    with pytest.raises(duo.DuoError) as e:
+        duo.required_bytes(_cfg(kv_format=2))
+    assert e.value.status == duo.DUO_ERR_INVALID_ARG
+
+
 def _raw(c):
     return duo.load_library(), c.handle
 
