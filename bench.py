@@ -13,6 +13,9 @@ Inputs are resident in HBM before the timed region.  Reported:
              against 8 TB/s; one decode call is one kernel launch, and the
              mean launch time is the decode phase (HIP events on the launch
              stream) divided by the number of launches
+  decode_int8  the same decode phase over an int8 retrieval cache
+             (DUO_KV_INT8: codes + fp32 row scales), filled by an untimed
+             prefill; its algorithmic bytes count D + 4 per stored K or V row
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode work
 Algorithmic counts: each K/V byte once per (sequence, KV head) plus q, out
 and the appended token; flops = 4*D per allowed (query, key) pair per query
@@ -23,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import json
 import math
 import os
@@ -104,6 +108,20 @@ def decode_bytes(w, mask, ctx: int) -> float:
     kv = 2 * row * w.batch * (nr * (ctx + 1) + ns * min(ctx + 1, w.sink + w.recent))
     qo = 2 * row * w.batch * w.num_q_heads
     append = 2 * row * w.batch * w.num_kv_heads
+    return float(kv + qo + append)
+
+
+def decode_bytes_int8(w, mask, ctx: int) -> float:
+    """Algorithmic bytes of one decode call with an int8 retrieval cache: each
+    stored retrieval row once as D codes + a 4-byte scale for K and for V, the
+    new token read (bf16) and stored (int8), streaming rows as bf16, q/out."""
+    nr = int(sum(mask))
+    ns = w.num_kv_heads - nr
+    row = 2 * w.head_dim
+    row8 = w.head_dim + 4
+    kv = 2 * w.batch * (nr * (ctx * row8 + row + row8) + ns * row * min(ctx + 1, w.sink + w.recent))
+    qo = 2 * row * w.batch * w.num_q_heads
+    append = 2 * row * w.batch * ns  # streaming heads' new token stored as bf16
     return float(kv + qo + append)
 
 
@@ -202,6 +220,29 @@ def main():
     mean_pre_launch = pre_ms / (args.steps * nl)     # ms per prefill call (prefill + append kernels)
     pre_achieved = (flops_step / nl) / (mean_pre_launch * 1e-3) / 1e12
 
+    # the same decode phase with an int8 retrieval cache (DUO_KV_INT8); the
+    # caches are filled by an untimed prefill
+    cfgs8 = [dataclasses.replace(c, kv_format=duo.DUO_KV_INT8) for c in cfgs]
+    bufs8 = [torch.empty(duo.required_bytes(c), dtype=torch.uint8, device=dev) for c in cfgs8]
+    dec8_ms = 0.0
+    for it in range(args.warmup + args.steps):
+        caches8 = [duo.duo_cache_init(cfgs8[l], bufs8[l]) for l in range(nl)]
+        hs8 = [c.handle for c in caches8]
+        for l in range(nl):
+            check(lib.duo_prefill(hs8[l], ptr(pq[l]), ptr(pk[l]), ptr(pv[l]), n_new, w.prefill, op_p, sp),
+                  "prefill int8")
+        ph[1].record(stream)
+        for s in range(w.decode_steps):
+            for l in range(nl):
+                check(lib.duo_decode(hs8[l], dq_p[l][s], dk_p[l][s], dv_p[l][s], od_p, sp), "decode int8")
+        ph[2].record(stream)
+        torch.cuda.synchronize()
+        if it >= args.warmup:
+            dec8_ms += ph[1].elapsed_time(ph[2])
+    del caches8
+    bytes8_step = sum(decode_bytes_int8(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
+    dec8_gbs = bytes8_step * args.steps / (dec8_ms * 1e-3) / 1e9
+
     result = {
         "metric": "decode attn HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak), 1 MI355X",
         "value": round(dec_gbs, 1),
@@ -227,6 +268,11 @@ def main():
                     "frac_of_mfma_peak": round(pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                     "phase_ms_per_step": round(pre_ms / args.steps, 3),
                     "flops_per_step": flops_step},
+        "decode_int8": {"gbs": round(dec8_gbs, 1), "frac_of_hbm_peak": round(dec8_gbs / HBM_PEAK_GBS, 4),
+                        "phase_ms_per_step": round(dec8_ms / args.steps, 3),
+                        "bytes_per_launch": bytes8_step / n_dec,
+                        "decode_time_vs_bf16": round(dec8_ms / dec_ms, 4),
+                        "cache": "retrieval K/V as int8 codes + fp32 row scales (DUO_KV_INT8)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_kernel (one launch per decode call)",
