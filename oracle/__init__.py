@@ -19,11 +19,13 @@ pages this project was built from):
   listed in ``mixed_attention`` and ``cache_state``.
 
 Every function here is pinned by ``tests/test_oracle.py`` and
-``tests/test_oracle_quant.py`` against closed forms, a library routine (torch
+``tests/test_oracle_quant.py`` and ``tests/test_oracle_rope.py`` against closed forms, a library routine (torch
 fp64 scaled-dot-product attention), brute force on tiny inputs and
 hand-derived fixtures under ``tests/golden/``.  ``quantized_cache`` adds the
 int8 retrieval cache the pages allude to ("combined with quantization",
-abstract), with the scheme taken as a stated reading.
+abstract), with the scheme taken as a stated reading; ``rope`` adds rotary
+position embedding on the way into the cache (cited by the pages only, in the
+pith.science reference list), restated from its published definition.
 """
 
 from .mixed_attention import (  # noqa: F401
@@ -41,4 +43,10 @@ from .quantized_cache import (  # noqa: F401
     dequantize_rows,
     quantize_rows,
     seen_rows,
+)
+from .rope import (  # noqa: F401
+    apply_rope,
+    rope_frequencies,
+    rotated_qk,
+    round_bf16,
 )
