@@ -22,7 +22,8 @@
  *     token is stored;
  *   - query head h uses KV head h / (num_q_heads / num_kv_heads) (grouped
  *     query attention) and inherits that KV head's kind;
- *   - no positional encoding is applied here: q and k arrive positioned;
+ *   - positional encoding: none by default (q and k arrive positioned), or
+ *     rotary position embedding applied by the library (duo_rope_style);
  *   - retrieval heads never evict: running out of `max_len` is an error.
  *
  * Conventions for every call:
@@ -72,6 +73,21 @@ typedef enum duo_status {
  * Streaming heads' caches are bf16 in both formats. */
 typedef enum duo_kv_format { DUO_KV_BF16 = 0, DUO_KV_INT8 = 1 } duo_kv_format;
 
+/* Rotary position embedding applied inside the library (RoFormer, cited in
+ * the reference list of the pith.science review page), when
+ * duo_config.rope_base > 0.  q and k are then passed UN-rotated.  Pair i of
+ * a head turns by p * theta_i, theta_i = rope_base^(-2i/head_dim), where p is
+ * the token's position in its sequence (len_b + i for chunk row i; the
+ * streaming cache keeps original positions); (a, b) -> (a cos - b sin,
+ * a sin + b cos).  K is stored rotated, rounded to bf16 (nearest even), and
+ * every key is attended through that stored value; q is rotated at its
+ * position before the product; V is not rotated.  Angles are formed in fp64
+ * and reduced before the fp32 sine and cosine, so positions in the millions
+ * keep their accuracy.  Not combined with DUO_KV_INT8 (UNSUPPORTED).
+ *   DUO_ROPE_INTERLEAVED: pair i = dims (2i, 2i+1) (the RoFormer form);
+ *   DUO_ROPE_HALF: pair i = dims (i, i + head_dim/2). */
+typedef enum duo_rope_style { DUO_ROPE_INTERLEAVED = 0, DUO_ROPE_HALF = 1 } duo_rope_style;
+
 /* Configuration of one attention layer's cache. */
 typedef struct duo_config {
   int32_t batch;        /* B, 1..DUO_MAX_BATCH sequences */
@@ -84,6 +100,8 @@ typedef struct duo_config {
   float scale;          /* softmax scale; 0 selects 1/sqrt(head_dim) */
   const uint8_t* kv_head_is_retrieval; /* HOST [Hkv]: nonzero = retrieval; copied */
   int32_t kv_format;    /* duo_kv_format of the retrieval cache */
+  float rope_base;      /* 0: no rotary embedding; > 0: its base (e.g. 10000) */
+  int32_t rope_style;   /* duo_rope_style (read when rope_base > 0) */
 } duo_config;
 
 /* Opaque host-side handle: configuration, head maps, region offsets and the
@@ -122,8 +140,9 @@ typedef struct duo_layout {
  * counters are zeroed on `stream` by a fill kernel; *out gets a new handle.
  * Errors: INVALID_ARG (null cfg / mask / out, B < 1, Hkv < 1, Hq % Hkv != 0,
  * sink < 0, recent < 1, max_len < 1, misaligned dev_buf, scale < 0 or not
- * finite, kv_format not a duo_kv_format), UNSUPPORTED (head_dim, batch),
- * BUFFER_TOO_SMALL, HIP. */
+ * finite, kv_format not a duo_kv_format, rope_base < 0 or not finite,
+ * rope_style not a duo_rope_style), UNSUPPORTED (head_dim, batch, rope_base
+ * > 0 with DUO_KV_INT8), BUFFER_TOO_SMALL, HIP. */
 duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
                           size_t* required_bytes, duo_cache** out, void* stream);
 
@@ -139,7 +158,8 @@ void duo_cache_destroy(duo_cache* h);
 
 /* Append n_new[b] tokens to every sequence without attending.
  * k, v: bf16 [B][chunk][Hkv][D]; rows i >= n_new[b] of sequence b are
- * ignored.  Token i of sequence b gets position len_b + i.  Retrieval heads
+ * ignored.  Token i of sequence b gets position len_b + i (with rotary
+ * embedding, k is stored rotated at that position).  Retrieval heads
  * store it at row len_b + i; streaming heads store positions < sink in their
  * sink slot and the last `recent` non-sink positions in their ring slot
  * (older ones would be overwritten at once).  Lengths advance by n_new.

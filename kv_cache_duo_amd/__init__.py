@@ -39,6 +39,7 @@ DUO_MAX_BATCH = 128
 
 
 DUO_KV_BF16, DUO_KV_INT8 = 0, 1
+DUO_ROPE_INTERLEAVED, DUO_ROPE_HALF = 0, 1
 
 
 class DuoError(RuntimeError):
@@ -53,7 +54,7 @@ class _Config(ctypes.Structure):
         ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("max_len", ctypes.c_int64), ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
         ("scale", ctypes.c_float), ("kv_head_is_retrieval", ctypes.POINTER(ctypes.c_uint8)),
-        ("kv_format", ctypes.c_int32),
+        ("kv_format", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
     ]
 
 
@@ -135,13 +136,16 @@ class Config:
     kv_head_is_retrieval: Sequence[int]
     scale: float = 0.0
     kv_format: int = 0  # DUO_KV_BF16; DUO_KV_INT8 = 1 stores retrieval rows as int8 + fp32 row scales
+    rope_base: float = 0.0  # > 0: rotary position embedding applied to q and k inside the library
+    rope_style: int = 0     # DUO_ROPE_INTERLEAVED (pairs 2i, 2i+1) or DUO_ROPE_HALF (pairs i, i + D/2)
 
     def _c(self):
         mask = (ctypes.c_uint8 * max(len(self.kv_head_is_retrieval), 1))(
             *[1 if x else 0 for x in self.kv_head_is_retrieval])
         c = _Config(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim, self.max_len,
                     self.sink, self.recent, self.scale,
-                    ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)), self.kv_format)
+                    ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)), self.kv_format, self.rope_base,
+                    self.rope_style)
         return c, mask  # keep the mask alive for the call
 
 

@@ -9,7 +9,9 @@
 // Within one call only the last `recent` non-sink positions of a chunk are
 // written to the ring: older ones would be overwritten by the same call.
 // With an int8 retrieval cache (duo_kv_format DUO_KV_INT8) retrieval rows
-// are quantized as they are stored.
+// are quantized as they are stored.  With rotary position embedding, K rows
+// are turned to their position as they are stored (RoFormer, cited in the
+// pith.science review page's reference list).
 #include "device_util.h"
 #include "duo_internal.h"
 
@@ -26,15 +28,16 @@ __global__ __launch_bounds__(kAppendThreads) void zero_words_kernel(uint32_t* p,
 }
 
 // One block copies up to 64 token rows of one (sequence, KV head).
-// Blocks [0, B*nR*xr) handle retrieval heads, the rest streaming heads.
+// Blocks [0, nr_blocks) handle retrieval heads, the rest streaming heads
+// (nr_blocks = 0 when only streaming heads are stored).
 template <int D>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, const uint16_t* __restrict__ k,
                                                                 const uint16_t* __restrict__ v, int32_t chunk,
-                                                                int32_t xr, int32_t xs) {
+                                                                int32_t xr, int32_t xs, int32_t nr_blocks) {
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int ROWS_PER_PASS = kAppendThreads / CH;
   int id = blockIdx.x;
-  const int retrieval_blocks = g.B * g.nR * xr;
+  const int retrieval_blocks = nr_blocks;
   bool retrieval = id < retrieval_blocks;
   int b, idx, x;
   if (retrieval) {
@@ -81,8 +84,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
       dv = g.sv + row * D;
     }
     int64_t src = (((int64_t)b * chunk + i) * g.Hkv + kvh) * D;
-    const uint4 kx = reinterpret_cast<const uint4*>(k + src)[c];
+    uint4 kx = reinterpret_cast<const uint4*>(k + src)[c];
     const uint4 vx = reinterpret_cast<const uint4*>(v + src)[c];
+    if (g.rope) {
+      float cs[8], sn[8];
+      rope_angles8<D>((int)p, c, g.rope_half, g.rope_rho, cs, sn);
+      kx = rope_apply8<CH>(kx, cs, sn, g.rope_half, c);
+    }
     if (retrieval && g.kv_int8) {
       // int8 row: the CH lanes of the row agree on its scale (group max)
       const int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + p;
@@ -106,18 +114,21 @@ hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s) {
 }
 
 hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v, int32_t chunk,
-                         int32_t max_n, hipStream_t s) {
+                         int32_t max_n, hipStream_t s, int kinds) {
   int32_t xr = (max_n + kRowsPerBlock - 1) / kRowsPerBlock;
   int32_t xs = (min(max_n, g.slots) + kRowsPerBlock - 1) / kRowsPerBlock;
   if (xr < 1) xr = 1;  // still one block per head so that the lengths are written
   if (xs < 1) xs = 1;
-  int64_t blocks = (int64_t)g.B * g.nR * xr + (int64_t)g.B * g.nS * xs;
+  const int64_t nr_blocks = (kinds & kAppendRetrieval) ? (int64_t)g.B * g.nR * xr : 0;
+  const int64_t ns_blocks = (kinds & kAppendStreaming) ? (int64_t)g.B * g.nS * xs : 0;
+  const int64_t blocks = nr_blocks + ns_blocks;
+  if (blocks <= 0) return hipSuccess;
   if (g.D == 128)
     hipLaunchKernelGGL(append_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, chunk,
-                       xr, xs);
+                       xr, xs, (int32_t)nr_blocks);
   else
     hipLaunchKernelGGL(append_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, chunk,
-                       xr, xs);
+                       xr, xs, (int32_t)nr_blocks);
   return hipGetLastError();
 }
 

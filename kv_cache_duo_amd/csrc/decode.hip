@@ -23,7 +23,9 @@
 // Records and tickets use agent-coherent (sc1) accesses without fences: an
 // agent-scope fence on gfx950 writes back and invalidates the whole L2.
 // Scores are kept in base-2 units (scale * log2 e folded in), so exp2 is the
-// only transcendental.
+// only transcendental of the row loop.  With rotary position embedding q
+// and the new K row are turned to position L once, in the prologue, and the
+// new token is scored outside the row loop (by work-group 0 of the unit).
 #include <cfloat>
 #include <cstdlib>
 
@@ -340,6 +342,25 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     qw[gg][0] = t.x; qw[gg][1] = t.y; qw[gg][2] = t.z; qw[gg][3] = t.w;
   }
 
+  // The new token's K chunk c, turned to position L with rotary embedding
+  // (rows are stored rotated: the cached rows already are).
+  uint4 knew = reinterpret_cast<const uint4*>(nk)[c];
+  if (g.rope) {
+    float cs[8], sn[8];
+    rope_angles8<D>(L, c, g.rope_half, g.rope_rho, cs, sn);
+#pragma unroll
+    for (int gg = 0; gg < GC; ++gg) {
+      const uint4 t = rope_apply8<LPR>(make_uint4(qw[gg][0], qw[gg][1], qw[gg][2], qw[gg][3]), cs, sn, g.rope_half, c);
+      qw[gg][0] = t.x; qw[gg][1] = t.y; qw[gg][2] = t.z; qw[gg][3] = t.w;
+    }
+    knew = rope_apply8<LPR>(knew, cs, sn, g.rope_half, c);
+  }
+  // Rows streamed by the row loop.  With rotary embedding the new token is
+  // scored separately: retrieval units stream rows 0..L-1, streaming units
+  // mask the new token's slot (its load reads the input row: finite).
+  const int Tst = (g.rope && retrieval) ? L : T;
+  const int skip_row = (g.rope && !retrieval) ? new_row : -1;
+
   float m[GC], l[GC], o[GC][8];
 #pragma unroll
   for (int gg = 0; gg < GC; ++gg) {
@@ -358,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   auto load = [&](uint4 (&kr)[kInFlight], uint4 (&vr)[kInFlight], int base) {
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const int row = min(row_of(base, j), T - 1);
+      const int row = min(row_of(base, j), Tst - 1);
       const uint16_t* pk = row == new_row ? nk : ck + (int64_t)row * D;
       const uint16_t* pv = row == new_row ? nv : cv + (int64_t)row * D;
       kr[j] = load_nt(reinterpret_cast<const uint4*>(pk) + c);  // streamed once: non-temporal
@@ -369,7 +390,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     float s[kInFlight][GC];
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
-      const bool valid = row_of(base, j) < T;
+      const int rj = row_of(base, j);
+      const bool valid = rj < Tst && rj != skip_row;
 #pragma unroll
       for (int gg = 0; gg < GC; ++gg) {
         float acc = dot2_bf16(kr[j].x, qw[gg][0], 0.f);
@@ -439,8 +461,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     }
   };
   auto stream_bf16 = [&]() __attribute__((always_inline)) {
-    uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
-    stream_pairs(ka, va, kb, vb, load, process, T, npairs);
+    if (Tst > 0) {
+      uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
+      stream_pairs(ka, va, kb, vb, load, process, Tst, (Tst + PAIR - 1) / PAIR);
+    }
   };
   const bool q8 = Q8 && retrieval;
   if constexpr (Q8) {
@@ -526,38 +550,41 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       for (int gg = 0; gg < GC; ++gg)
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[gg][e] = fmaf(-128.0f, cacc[gg], o[gg][e]);
-      // The new token, at input precision: work-group 0, one lane group.
-      own_new = split == 0;
-      if (own_new) {
-        const uint4 kx = reinterpret_cast<const uint4*>(nk)[c];
-        const uint4 vx = reinterpret_cast<const uint4*>(nv)[c];
-        const bool mine = wave == 0 && grp == 0;
-        const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w}, vw[4] = {vx.x, vx.y, vx.z, vx.w};
-#pragma unroll
-        for (int gg = 0; gg < GC; ++gg) {
-          float acc = 0.f;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc = dot2_bf16(kw[e], qw[gg][e], acc);
-          acc = group_sum<LPR>(acc);
-          const float sc = mine ? acc * g.scale_log2 : -INFINITY;
-          const float mn = fmaxf(m[gg], sc);
-          const float mu = max_or_zero(mn);
-          const float alpha = exp2_fast(m[gg] - mu);
-          const float p = exp2_fast(sc - mu);
-          l[gg] = l[gg] * alpha + p;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            o[gg][2 * e] = fmaf(p, bf16_lo(vw[e]), o[gg][2 * e] * alpha);
-            o[gg][2 * e + 1] = fmaf(p, bf16_hi(vw[e]), o[gg][2 * e + 1] * alpha);
-          }
-          m[gg] = mn;
-        }
-      }
     } else {
       stream_bf16();
     }
   } else {
     stream_bf16();
+  }
+  // The new token, scored outside the row loop (int8 retrieval rows: at
+  // input precision; rotary embedding: rotated): work-group 0, one lane
+  // group of wave 0.
+  if (q8 || g.rope) {
+    own_new = split == 0;
+    if (own_new) {
+      const uint4 vx = reinterpret_cast<const uint4*>(nv)[c];
+      const bool mine = wave == 0 && grp == 0;
+      const uint32_t kw[4] = {knew.x, knew.y, knew.z, knew.w}, vw[4] = {vx.x, vx.y, vx.z, vx.w};
+#pragma unroll
+      for (int gg = 0; gg < GC; ++gg) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = dot2_bf16(kw[e], qw[gg][e], acc);
+        acc = group_sum<LPR>(acc);
+        const float sc = mine ? acc * g.scale_log2 : -INFINITY;
+        const float mn = fmaxf(m[gg], sc);
+        const float mu = max_or_zero(mn);
+        const float alpha = exp2_fast(m[gg] - mu);
+        const float p = exp2_fast(sc - mu);
+        l[gg] = l[gg] * alpha + p;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[gg][2 * e] = fmaf(p, bf16_lo(vw[e]), o[gg][2 * e] * alpha);
+          o[gg][2 * e + 1] = fmaf(p, bf16_hi(vw[e]), o[gg][2 * e + 1] * alpha);
+        }
+        m[gg] = mn;
+      }
+    }
   }
 
   // ---- merge the row groups of the wave (same head, different rows)
@@ -594,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 
   // ---- the owner of the new token stores it (one head chunk does it)
   if (hc == 0 && own_new && threadIdx.x < LPR) {
-    const uint4 kx = reinterpret_cast<const uint4*>(nk)[threadIdx.x];
+    const uint4 kx = knew;  // threads 0..LPR-1 hold chunks c = 0..LPR-1
     const uint4 vx = reinterpret_cast<const uint4*>(nv)[threadIdx.x];
     if (q8) {
       const int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + new_row;

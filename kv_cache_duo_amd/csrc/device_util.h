@@ -89,4 +89,100 @@ __device__ __forceinline__ void store_int8_row(uint8_t* codes, float* scale_out,
   if (c == 0) *scale_out = scale;
 }
 
+// Rotary position embedding (RoFormer): pair i of a head turns by p * theta_i
+// at position p, theta_i = base^(-2i/D) = rho^i, (a, b) -> (a cos - b sin,
+// a sin + b cos).  The angle is formed in fp64 revolutions (p * theta_i / 2 pi)
+// and reduced to [-1/2, 1/2] before the fp32 sine and cosine: an fp32
+// product p * theta_i would be off by whole radians at positions in the
+// millions.  Revolutions per position of pair i, rho^i / (2 pi) by binary
+// powering (a few fp64 roundings, ~1e-15 relative):
+__device__ __forceinline__ double rope_rev(int i, double rho) {
+  double r = 0.15915494309189535, b = rho;
+#pragma unroll
+  for (int k = 0; k < 6; ++k) {
+    if (i & (1 << k)) r *= b;
+    b *= b;
+  }
+  return r;
+}
+
+// sin and cos of 2 pi r (r in turns, fp64).  Whole and quarter turns come
+// out in fp64 (exact); the rest, |x| <= pi/4, goes through the Taylor series
+// of sin (to x^9) and cos (to x^10) in fp32, truncation below 3e-9.
+__device__ __forceinline__ void sincos_turns(double r, float& s, float& c) {
+  r -= rint(r);
+  const double q = rint(4.0 * r);
+  const float x = (float)((r - 0.25 * q) * 6.283185307179586);
+  const float x2 = x * x;
+  float sp = fmaf(x2, 1.0f / 362880.0f, -1.0f / 5040.0f);
+  sp = fmaf(x2, sp, 1.0f / 120.0f);
+  sp = fmaf(x2, sp, -1.0f / 6.0f);
+  const float sx = fmaf(x * x2, sp, x);
+  float cp = fmaf(x2, -1.0f / 3628800.0f, 1.0f / 40320.0f);
+  cp = fmaf(x2, cp, -1.0f / 720.0f);
+  cp = fmaf(x2, cp, 1.0f / 24.0f);
+  cp = fmaf(x2, cp, -0.5f);
+  const float cx = fmaf(x2, cp, 1.0f);
+  const int k = (int)q & 3;  // quarter turns: the angle is x + k pi/2
+  s = k == 0 ? sx : k == 1 ? cx : k == 2 ? -sx : -cx;
+  c = k == 0 ? cx : k == 1 ? -sx : k == 2 ? -cx : sx;
+}
+
+__device__ __forceinline__ void rope_cos_sin(int p, double rev, float& c, float& s) {
+  sincos_turns((double)p * rev, s, c);
+}
+
+// cos and sin of the angles of dims 8c .. 8c+7 at position p: interleaved
+// pairs (2i, 2i+1) give 4 pairs (i = 4c ..), half-split pairs (i, i + D/2)
+// 8 (i = 8c mod D/2 ..).
+template <int D>
+__device__ __forceinline__ void rope_angles8(int p, int c, bool half, double rho, float (&cs)[8], float (&sn)[8]) {
+  double rev = rope_rev(half ? (8 * c) % (D / 2) : 4 * c, rho);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (half || (e & 1) == 0) {
+      if (e > 0) rev *= rho;
+      rope_cos_sin(p, rev, cs[e], sn[e]);
+    } else {
+      cs[e] = cs[e - 1];
+      sn[e] = sn[e - 1];
+    }
+  }
+}
+
+// Rotate the 8 bf16 values x (dims 8c .. 8c+7 of a row) by the angles of
+// rope_angles8 and round them to bf16.  Half-split pairs join chunk c with
+// chunk c ^ (CH/2), held by lane ^ (CH/2): the CH lanes of a row are
+// consecutive and all call this together.
+template <int CH>
+__device__ __forceinline__ uint4 rope_apply8(const uint4& x, const float (&cs)[8], const float (&sn)[8], bool half,
+                                             int c) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  float v[8], o[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    v[2 * e] = bf16_lo(w[e]);
+    v[2 * e + 1] = bf16_hi(w[e]);
+  }
+  if (!half) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      o[e] = fmaf(v[e], cs[e], -v[e + 1] * sn[e]);
+      o[e + 1] = fmaf(v[e], sn[e], v[e + 1] * cs[e]);
+    }
+  } else {
+    const bool first = c < CH / 2;  // this lane holds the pairs' first dims
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t pw = (uint32_t)__shfl_xor((int)w[e], CH / 2);
+      const float p0 = bf16_lo(pw), p1 = bf16_hi(pw);
+      o[2 * e] = first ? fmaf(v[2 * e], cs[2 * e], -p0 * sn[2 * e]) : fmaf(p0, sn[2 * e], v[2 * e] * cs[2 * e]);
+      o[2 * e + 1] = first ? fmaf(v[2 * e + 1], cs[2 * e + 1], -p1 * sn[2 * e + 1])
+                           : fmaf(p1, sn[2 * e + 1], v[2 * e + 1] * cs[2 * e + 1]);
+    }
+  }
+  return make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                    pack_bf16x2(o[6], o[7]));
+}
+
 }  // namespace duo

@@ -41,9 +41,13 @@ duo_status check_config(const duo_config* c) {
   if (!(c->scale >= 0.f) || !std::isfinite(c->scale)) return DUO_ERR_INVALID_ARG;
   if (c->kv_head_is_retrieval == nullptr) return DUO_ERR_INVALID_ARG;
   if (c->kv_format != DUO_KV_BF16 && c->kv_format != DUO_KV_INT8) return DUO_ERR_INVALID_ARG;
+  if (!(c->rope_base >= 0.f) || !std::isfinite(c->rope_base)) return DUO_ERR_INVALID_ARG;
+  if (c->rope_base > 0.f && c->rope_style != DUO_ROPE_INTERLEAVED && c->rope_style != DUO_ROPE_HALF)
+    return DUO_ERR_INVALID_ARG;
   if (c->head_dim != 64 && c->head_dim != 128) return DUO_ERR_UNSUPPORTED;
   if (c->batch > DUO_MAX_BATCH || c->num_kv_heads > duo::kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
   if (c->max_len > kMaxLen || (int64_t)c->sink + c->recent > kMaxLen) return DUO_ERR_UNSUPPORTED;
+  if (c->rope_base > 0.f && c->kv_format == DUO_KV_INT8) return DUO_ERR_UNSUPPORTED;
   return DUO_OK;
 }
 
@@ -72,6 +76,9 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   g->nR = nr;
   g->nS = ns;
   g->kv_int8 = c->kv_format == DUO_KV_INT8;
+  g->rope = c->rope_base > 0.f;
+  g->rope_half = g->rope && c->rope_style == DUO_ROPE_HALF;
+  g->rope_rho = g->rope ? std::pow((double)c->rope_base, -2.0 / c->head_dim) : 0.0;
   g->max_splits = duo::max_splits_for(c->max_len, g->slots, duo::decode_head_chunk(g->G));
 
   const int gc = duo::decode_head_chunk(g->G);
@@ -238,13 +245,23 @@ duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v
   duo_status st = check_chunk(h, n_new, chunk, &sq, &max_n);
   if (st != DUO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  // Attention first: streaming heads read ring slots that this chunk's
-  // append will overwrite.  Then the append stores the chunk.
-  hipError_t e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                     static_cast<const uint16_t*>(v), chunk, max_n, static_cast<uint16_t*>(out), s);
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  // Streaming heads read ring slots that this chunk's append overwrites, so
+  // their rows are stored after the attention.  With rotary embedding the
+  // retrieval rows are stored (rotated) first and the attention reads every
+  // retrieval key from the cache; streaming heads rotate their chunk rows
+  // as they load them.
+  hipError_t e = hipSuccess;
+  if (h->geom.rope) {
+    e = duo::launch_append(h->geom, sq, kk, vv, chunk, max_n, s, duo::kAppendRetrieval);
+    if (e != hipSuccess) return DUO_ERR_HIP;
+  }
+  e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), kk, vv, chunk, max_n,
+                          static_cast<uint16_t*>(out), s);
   if (e != hipSuccess) return DUO_ERR_HIP;
-  e = duo::launch_append(h->geom, sq, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), chunk,
-                         max_n, s);
+  e = duo::launch_append(h->geom, sq, kk, vv, chunk, max_n, s,
+                         h->geom.rope ? duo::kAppendStreaming : duo::kAppendRetrieval | duo::kAppendStreaming);
   if (e != hipSuccess) return DUO_ERR_HIP;
   for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += n_new[b];
   return DUO_OK;

@@ -20,6 +20,9 @@ struct Geom {
   int32_t kv_int8;            // retrieval rows stored as int8 codes + fp32 scales
   int64_t max_len;
   float scale_log2;           // softmax scale * log2(e): scores in base-2 units
+  int32_t rope;               // rotary position embedding applied to q and k
+  int32_t rope_half;          // pairs (i, i + D/2) instead of (2i, 2i + 1)
+  double rope_rho;            // rotary base^(-2/D): pair i turns by rho^i per position
   uint16_t* rk;               // bf16 bits [B][nR][max_len][D] (kv_int8: uint8 codes, D bytes per row)
   uint16_t* rv;
   float* rks;                 // kv_int8: fp32 row scales [B][nR][max_len] of rk / rv
@@ -57,8 +60,11 @@ struct Seqs {
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s);
 
+// kinds: kAppendRetrieval | kAppendStreaming, the heads whose rows are stored
+constexpr int kAppendRetrieval = 1, kAppendStreaming = 2;
 hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v,
-                         int32_t chunk, int32_t max_n, hipStream_t s);
+                         int32_t chunk, int32_t max_n, hipStream_t s,
+                         int kinds = kAppendRetrieval | kAppendStreaming);
 
 struct DecodePlan {
   int32_t split_tokens;      // rows per work-group on average (a multiple of the pair rows)

@@ -36,6 +36,12 @@
 //     share the same reference;
 //   * l sums the bf16 P that the MFMA consumes (v_dot2 with ones);
 //   * work-groups run longest query tile first, t-major and unit-minor.
+// With rotary position embedding (RoFormer, cited in the pith.science review
+// page's reference list) q is turned to its position in the prologue; the
+// chunk's retrieval rows are stored (rotated) before this kernel, so every
+// retrieval key comes from the cache; streaming tiles holding chunk rows are
+// staged through registers and their chunk K rows turned before the LDS
+// write.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -118,9 +124,11 @@ __device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
 // Q8: the retrieval cache holds int8 rows (DUO_KV_INT8) and some sequence
 // has a stored prefix; tiles with stored retrieval rows are then staged
 // through registers and dequantized into the bf16 LDS layout.
-template <int D, bool Q8>
+// ROPE: rotary position embedding (never together with Q8).
+template <int D, bool Q8, bool ROPE>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
+  static_assert(!(Q8 && ROPE), "rotary embedding with an int8 cache is not supported");
   using LD = Lds<D>;
   constexpr int CH = D / 8;                 // 16-byte granules per row
   constexpr int RPC = 64 / CH;              // rows per 1 KB wave load (4 or 8)
@@ -191,12 +199,60 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   {
     const bool ok = my_i <= i_hi;
     const uint4* src = reinterpret_cast<const uint4*>(a.q + (((int64_t)b * a.chunk + (ok ? my_i : i_lo)) * g.Hq + h) * D);
+    const float s = ok ? c2 : 0.f;
+    if constexpr (ROPE) {
+      // k-step c holds dims 16c + 8 half + 0..7 (chunk 2c + half of the
+      // row): interleaved pairs lie inside it; half-split pairs join k-step c
+      // with c + QC/2 (dims d and d + D/2), in this same lane.
+      float x[QC][8];
 #pragma unroll
-    for (int c = 0; c < QC; ++c) {
-      const uint4 x = src[2 * c + half];
-      const float s = ok ? c2 : 0.f;
-      qreg[c] = __builtin_bit_cast(bf16x8_t, make_uint4(scaled_pair(x.x, s), scaled_pair(x.y, s),
-                                                        scaled_pair(x.z, s), scaled_pair(x.w, s)));
+      for (int c = 0; c < QC; ++c) {
+        const uint4 t = src[2 * c + half];
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[c][2 * e] = bf16_lo(w[e]);
+          x[c][2 * e + 1] = bf16_hi(w[e]);
+        }
+      }
+      if (!g.rope_half) {
+#pragma unroll
+        for (int c = 0; c < QC; ++c) {
+          float cs[8], sn[8];
+          rope_angles8<D>(my_q, 2 * c + half, false, g.rope_rho, cs, sn);
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float u = x[c][e], w = x[c][e + 1];
+            x[c][e] = fmaf(u, cs[e], -w * sn[e]);
+            x[c][e + 1] = fmaf(u, sn[e], w * cs[e]);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < QC / 2; ++c) {
+          float cs[8], sn[8];
+          rope_angles8<D>(my_q, 2 * c + half, true, g.rope_rho, cs, sn);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float u = x[c][e], w = x[c + QC / 2][e];
+            x[c][e] = fmaf(u, cs[e], -w * sn[e]);
+            x[c + QC / 2][e] = fmaf(u, sn[e], w * cs[e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < QC; ++c)
+        qreg[c] = __builtin_bit_cast(bf16x8_t, make_uint4(pack_bf16x2(x[c][0] * s, x[c][1] * s),
+                                                          pack_bf16x2(x[c][2] * s, x[c][3] * s),
+                                                          pack_bf16x2(x[c][4] * s, x[c][5] * s),
+                                                          pack_bf16x2(x[c][6] * s, x[c][7] * s)));
+    } else {
+#pragma unroll
+      for (int c = 0; c < QC; ++c) {
+        const uint4 x = src[2 * c + half];
+        qreg[c] = __builtin_bit_cast(bf16x8_t, make_uint4(scaled_pair(x.x, s), scaled_pair(x.y, s),
+                                                          scaled_pair(x.z, s), scaled_pair(x.w, s)));
+      }
     }
   }
 
@@ -238,11 +294,57 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     cks = g.rks + r8;
     cvs = g.rvs + r8;
   }
-  u32x4_t kst[Q8 ? NJ : 1], vst[Q8 ? NJ : 1];
+  // ROPE: a staged streaming tile's rows wait in kst / vst as bf16 granules
+  // (bit j of q8rows: row j is a chunk row whose K is turned in store_tile).
+  u32x4_t kst[(Q8 || ROPE) ? NJ : 1], vst[(Q8 || ROPE) ? NJ : 1];
   uint32_t q8rows = 0;
-  auto load_tile = [&](int tile, int buf_off) -> bool __attribute__((always_inline)) {  // true: staged, store_tile to follow
+  int st_k0 = 0;  // first key of the staged tile
+  auto load_tile = [&](int tile, int buf_off) __attribute__((always_inline)) -> bool {  // true: staged, store_tile to follow
     const int k0 = tile * kBN;
     const int dst = buf_off + wave * 1024;
+    if constexpr (ROPE) {
+      if (retrieval) {
+        // every key row is in the cache (this chunk's rows were stored,
+        // rotated, before the kernel); rows past qmax read row 0 instead
+        if (k0 + kBN - 1 <= qmax) {
+          const uint16_t* kb = ck + (int64_t)k0 * D + koff_c;
+          const uint16_t* vb = cv + (int64_t)k0 * D + voff_c;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) global_to_lds16(kb + j * ROWS_J * D, dst + j * kWaves * 1024);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) global_to_lds16(vb + j * ROWS_J * D, dst + LD::TILE + j * kWaves * 1024);
+        } else {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const int kp = k0 + r0 + j * ROWS_J;
+            const int64_t row = kp <= qmax ? (int64_t)kp : 0;
+            global_to_lds16(ck + row * D + gK * 8, dst + j * kWaves * 1024);
+            global_to_lds16(cv + row * D + gV * 8, dst + LD::TILE + j * kWaves * 1024);
+          }
+        }
+        return false;
+      }
+      if (k0 + kBN - 1 >= L) {  // a streaming tile with chunk rows: stage it
+        st_k0 = k0;
+        q8rows = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          // row_src for a streaming head, written out (a second call of
+          // that lambda makes the compiler copy the kernel arguments to
+          // scratch)
+          const int kp = k0 + r0 + j * ROWS_J;
+          const bool in_chunk = kp >= L;
+          const bool ok = kp <= qmax && (in_chunk || kp < g.S || kp >= L - g.W);
+          const bool from_cache = !in_chunk && ok;
+          const int64_t cache_row = kp < g.S ? (int64_t)kp : (int64_t)(g.S + (kp - g.S) % g.W);
+          const int64_t off = !ok ? in_base : in_chunk ? in_base + (int64_t)(kp - L) * in_stride : cache_row * D;
+          kst[j] = *reinterpret_cast<const u32x4_t*>((from_cache ? ck : a.k) + off + gK * 8);
+          vst[j] = *reinterpret_cast<const u32x4_t*>((from_cache ? cv : a.v) + off + gV * 8);
+          if (!from_cache && kp >= L && kp <= qmax) q8rows |= 1u << j;
+        }
+        return true;
+      }
+    }
     if constexpr (Q8) {
       if (retrieval && k0 < L) {
         q8rows = 0;
@@ -291,7 +393,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   };
   // Write a staged tile: int8 granules become code * scale rounded to bf16.
   auto store_tile = [&](int buf_off) __attribute__((always_inline)) {
-    auto granule = [&](const u32x4_t& x, bool q8) -> u32x4_t __attribute__((always_inline)) {
+    auto granule = [&](const u32x4_t& x, bool q8) __attribute__((always_inline)) -> u32x4_t {
       if (!q8) return x;
       const float sc = __uint_as_float(x.z);
       uint32_t w[4];
@@ -303,6 +405,21 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       return u32x4_t{w[0], w[1], w[2], w[3]};
     };
     char* dst = prefill_smem + buf_off + wave * 1024 + lane * 16;
+    if constexpr (ROPE) {
+      // chunk K rows turned to their positions (every lane takes part: the
+      // half-split pairs exchange values across lanes)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        float cs[8], sn[8];
+        rope_angles8<D>(st_k0 + r0 + j * ROWS_J, gK, g.rope_half, g.rope_rho, cs, sn);
+        const uint4 x = make_uint4(kst[j].x, kst[j].y, kst[j].z, kst[j].w);
+        const uint4 r = rope_apply8<CH>(x, cs, sn, g.rope_half, gK);
+        const u32x4_t kr = ((q8rows >> j) & 1u) ? u32x4_t{r.x, r.y, r.z, r.w} : kst[j];
+        *reinterpret_cast<u32x4_t*>(dst + j * kWaves * 1024) = kr;
+        *reinterpret_cast<u32x4_t*>(dst + LD::TILE + j * kWaves * 1024) = vst[j];
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       const bool q8 = (q8rows >> j) & 1u;
@@ -417,7 +534,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           }
         }
     }
-    if constexpr (Q8) {
+    if constexpr (Q8 || ROPE) {
       if (staged) store_tile((cur ^ 1) * LD::BUF);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next tile
@@ -455,11 +572,11 @@ int heads_per_group(int G) {
   return 1;
 }
 
-template <int D, bool Q8>
+template <int D, bool Q8, bool ROPE>
 hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, Q8>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, Q8, ROPE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Lds<D>::TOTAL);
     if (e != hipSuccess) return e;
     attr_set = true;
@@ -469,7 +586,7 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
   a.items_r = a.tiles_max * g.B * g.nR * a.n_hc;
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * g.B * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<D, Q8>), dim3((unsigned)blocks), dim3(kThreads), Lds<D>::TOTAL, s, g, q, a);
+  hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE>), dim3((unsigned)blocks), dim3(kThreads), Lds<D>::TOTAL, s, g, q, a);
   return hipGetLastError();
 }
 
@@ -489,9 +606,11 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   // int8 retrieval rows are only read from a stored prefix
   bool prefix = false;
   for (int b = 0; b < g.B; ++b) prefix = prefix || (q.n[b] > 0 && q.len[b] > 0);
+  if (g.rope)  // never with an int8 cache (rejected by the configuration check)
+    return g.D == 128 ? launch_t<128, false, true>(g, q, a, max_n, s) : launch_t<64, false, true>(g, q, a, max_n, s);
   if (g.kv_int8 && g.nR > 0 && prefix)
-    return g.D == 128 ? launch_t<128, true>(g, q, a, max_n, s) : launch_t<64, true>(g, q, a, max_n, s);
-  return g.D == 128 ? launch_t<128, false>(g, q, a, max_n, s) : launch_t<64, false>(g, q, a, max_n, s);
+    return g.D == 128 ? launch_t<128, true, false>(g, q, a, max_n, s) : launch_t<64, true, false>(g, q, a, max_n, s);
+  return g.D == 128 ? launch_t<128, false, false>(g, q, a, max_n, s) : launch_t<64, false, false>(g, q, a, max_n, s);
 }
 
 }  // namespace duo

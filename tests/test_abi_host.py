@@ -71,6 +71,10 @@ def test_required_bytes_for_workloads(name):
     (dict(scale=-1.0), duo.DUO_ERR_INVALID_ARG),
     (dict(scale=float("nan")), duo.DUO_ERR_INVALID_ARG),
     (dict(max_len=1 << 31), duo.DUO_ERR_UNSUPPORTED),
+    (dict(rope_base=-1.0), duo.DUO_ERR_INVALID_ARG),
+    (dict(rope_base=float("inf")), duo.DUO_ERR_INVALID_ARG),
+    (dict(rope_base=10000.0, rope_style=2), duo.DUO_ERR_INVALID_ARG),
+    (dict(rope_base=10000.0, kv_format=1), duo.DUO_ERR_UNSUPPORTED),  # rotary + int8 cache
 ])
 def test_invalid_configs(kw, status):
     with pytest.raises(duo.DuoError) as e:
@@ -199,3 +203,14 @@ def test_binding_rejects_cpu_tensors():
     q = torch.zeros(2, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         duo.duo_decode(c, q, q[:, :4], q[:, :4], q)
+
+
+def test_rope_config_accepted_and_layout_unchanged():
+    """Rotary embedding changes no region: the layout equals the plain one."""
+    base = duo.Config(2, 8, 4, 128, 1000, 4, 64, [1, 0, 1, 0])
+    for style in (duo.DUO_ROPE_INTERLEAVED, duo.DUO_ROPE_HALF):
+        cfg = duo.Config(2, 8, 4, 128, 1000, 4, 64, [1, 0, 1, 0], rope_base=500000.0, rope_style=style)
+        assert duo.required_bytes(cfg) == duo.required_bytes(base)
+    # the style is not read without a base
+    cfg = duo.Config(2, 8, 4, 128, 1000, 4, 64, [1, 0, 1, 0], rope_base=0.0, rope_style=7)
+    assert duo.required_bytes(cfg) == duo.required_bytes(base)
