@@ -14,8 +14,10 @@ Inputs are resident in HBM before the timed region.  Reported:
              mean launch time is the decode phase (HIP events on the launch
              stream) divided by the number of launches
   decode_int8  the same decode phase over an int8 retrieval cache
-             (DUO_KV_INT8: codes + fp32 row scales), filled by an untimed
+             (DUO_KV_INT8: codes + fp32 row scales), filled by the same
              prefill; its algorithmic bytes count D + 4 per stored K or V row
+  rope       the same step with rotary position embedding applied inside the
+             library (same algorithmic counts; rotation work is overhead)
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode work
 Algorithmic counts: each K/V byte once per (sequence, KV head) plus q, out
 and the appended token; flops = 4*D per allowed (query, key) pair per query
@@ -220,26 +222,35 @@ def main():
     mean_pre_launch = pre_ms / (args.steps * nl)     # ms per prefill call (prefill + append kernels)
     pre_achieved = (flops_step / nl) / (mean_pre_launch * 1e-3) / 1e12
 
-    # the same decode phase with an int8 retrieval cache (DUO_KV_INT8); the
-    # caches are filled by an untimed prefill
-    cfgs8 = [dataclasses.replace(c, kv_format=duo.DUO_KV_INT8) for c in cfgs]
-    bufs8 = [torch.empty(duo.required_bytes(c), dtype=torch.uint8, device=dev) for c in cfgs8]
-    dec8_ms = 0.0
-    for it in range(args.warmup + args.steps):
-        caches8 = [duo.duo_cache_init(cfgs8[l], bufs8[l]) for l in range(nl)]
-        hs8 = [c.handle for c in caches8]
-        for l in range(nl):
-            check(lib.duo_prefill(hs8[l], ptr(pq[l]), ptr(pk[l]), ptr(pv[l]), n_new, w.prefill, op_p, sp),
-                  "prefill int8")
-        ph[1].record(stream)
-        for s in range(w.decode_steps):
+    def variant_phases(cfgs_v, what):
+        """Prefill and decode phase times (ms, summed over the timed steps)
+        of the same step on caches of another configuration; the buffers of
+        the main run are reused."""
+        pre_v = dec_v = 0.0
+        for it in range(args.warmup + args.steps):
+            cv = [duo.duo_cache_init(cfgs_v[l], bufs[l]) for l in range(nl)]
+            hv = [c.handle for c in cv]
+            ph[0].record(stream)
             for l in range(nl):
-                check(lib.duo_decode(hs8[l], dq_p[l][s], dk_p[l][s], dv_p[l][s], od_p, sp), "decode int8")
-        ph[2].record(stream)
-        torch.cuda.synchronize()
-        if it >= args.warmup:
-            dec8_ms += ph[1].elapsed_time(ph[2])
-    del caches8
+                check(lib.duo_prefill(hv[l], ptr(pq[l]), ptr(pk[l]), ptr(pv[l]), n_new, w.prefill, op_p, sp),
+                      f"prefill {what}")
+            ph[1].record(stream)
+            for s in range(w.decode_steps):
+                for l in range(nl):
+                    check(lib.duo_decode(hv[l], dq_p[l][s], dk_p[l][s], dv_p[l][s], od_p, sp), f"decode {what}")
+            ph[2].record(stream)
+            torch.cuda.synchronize()
+            if it >= args.warmup:
+                pre_v += ph[0].elapsed_time(ph[1])
+                dec_v += ph[1].elapsed_time(ph[2])
+        return pre_v, dec_v
+
+    # the same step with an int8 retrieval cache (DUO_KV_INT8: smaller, so
+    # the bf16 buffers hold it), and with rotary position embedding applied
+    # inside the library (base 10000, half-split pairs)
+    _, dec8_ms = variant_phases([dataclasses.replace(c, kv_format=duo.DUO_KV_INT8) for c in cfgs], "int8")
+    pre_r_ms, dec_r_ms = variant_phases(
+        [dataclasses.replace(c, rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF) for c in cfgs], "rope")
     bytes8_step = sum(decode_bytes_int8(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
     dec8_gbs = bytes8_step * args.steps / (dec8_ms * 1e-3) / 1e9
 
@@ -273,6 +284,11 @@ def main():
                         "bytes_per_launch": bytes8_step / n_dec,
                         "decode_time_vs_bf16": round(dec8_ms / dec_ms, 4),
                         "cache": "retrieval K/V as int8 codes + fp32 row scales (DUO_KV_INT8)"},
+        "rope": {"decode_gbs": round(bytes_step * args.steps / (dec_r_ms * 1e-3) / 1e9, 1),
+                 "prefill_tflops": round(flops_step * args.steps / (pre_r_ms * 1e-3) / 1e12, 1),
+                 "decode_time_vs_plain": round(dec_r_ms / dec_ms, 4),
+                 "prefill_time_vs_plain": round(pre_r_ms / pre_ms, 4),
+                 "embedding": "rotary, base 10000, pairs (i, i + D/2), applied to q and k inside the library"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_kernel (one launch per decode call)",

@@ -28,6 +28,7 @@
 // new token is scored outside the row loop (by work-group 0 of the unit).
 #include <cfloat>
 #include <cstdlib>
+#include <type_traits>
 
 #include "device_util.h"
 #include "duo_internal.h"
@@ -38,7 +39,9 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxMergeRecords = 1024;  // (m, l) pairs the merge stages in LDS
-constexpr int kMinPairs = 4;            // pairs of batches per work-group, at least, on average
+// pairs of batches per work-group, at least, on average (bf16 rows; int8
+// rows, whose pairs hold twice the rows): measured best on the 32K MHA layer
+constexpr int kMinPairs = 3, kMinPairsInt8 = 2;
 
 struct DecodeArgs {
   const uint16_t* q;  // [B][Hq][D]
@@ -437,11 +440,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // unconditional loads keep the outstanding-load count static.
   __shared__ int sm_claim[2];
   bool own_new = false;  // this work-group's rows hold the new token
-  auto stream_pairs = [&](auto& ka, auto& va, auto& kb, auto& vb, auto&& ld, auto&& pr, int rows, int npr)
-      __attribute__((always_inline)) {
-    int base = split * PAIR;
+  auto stream_pairs = [&](auto& ka, auto& va, auto& kb, auto& vb, auto&& ld, auto&& pr, int rows, int npr,
+                          auto pair_c, auto iter_c) __attribute__((always_inline)) {
+    constexpr int P = decltype(pair_c)::value, IT = decltype(iter_c)::value;  // rows per pair, per batch
+    int base = split * P;
     ld(ka, va, base);
-    ld(kb, vb, base + ROWS_ITER);
+    ld(kb, vb, base + IT);
     for (int it = 0;; it ^= 1) {
       if (threadIdx.x == 0) {
         sm_claim[it] = ns + (int)claimed;
@@ -450,12 +454,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       __syncthreads();
       const int p_next = __builtin_amdgcn_readfirstlane(sm_claim[it]);
       const bool more = p_next < npr;
-      const int nbase = more ? p_next * PAIR : rows;
+      const int nbase = more ? p_next * P : rows;
       pr(ka, va, base);
       ld(ka, va, nbase);
-      pr(kb, vb, base + ROWS_ITER);
-      ld(kb, vb, nbase + ROWS_ITER);
-      own_new = own_new || (new_row >= base && new_row < base + PAIR);
+      pr(kb, vb, base + IT);
+      ld(kb, vb, nbase + IT);
+      own_new = own_new || (new_row >= base && new_row < base + P);
       if (!more) break;
       base = nbase;
     }
@@ -463,58 +467,100 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   auto stream_bf16 = [&]() __attribute__((always_inline)) {
     if (Tst > 0) {
       uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
-      stream_pairs(ka, va, kb, vb, load, process, Tst, (Tst + PAIR - 1) / PAIR);
+      stream_pairs(ka, va, kb, vb, load, process, Tst, (Tst + PAIR - 1) / PAIR, std::integral_constant<int, PAIR>(),
+                   std::integral_constant<int, ROWS_ITER>());
     }
   };
   const bool q8 = Q8 && retrieval;
   if constexpr (Q8) {
     if (retrieval) {
-      // int8 rows 0..L-1 of the cache (a lane: 8 codes, its row's scale in
-      // .z); the new token (row L) is taken from the input below
+      // int8 rows 0..L-1 of the cache; the new token (row L) is scored from
+      // the input below.  A row of D codes is read by LPR8 = D/16 lanes with
+      // 16-byte loads (one wave instruction: 1 KB of consecutive rows, as in
+      // the bf16 path).  K: the codes b (stored code + 128) become the f16
+      // values 1024 + b (byte b under the exponent byte 0x64, one v_perm per
+      // two codes) and meet q in v_dot2_f32_f16; q is held in f16 scaled by a
+      // power of two (2^(15 - e), amax = m 2^e over the head: no overflow,
+      // bf16 values stay exact), and the 1024 + 128 offset comes back as one
+      // per-lane constant -1152 * sum(q).  V: o += (p * scale_v) * b in fp32,
+      // with 128 * sum(p * scale_v) taken off once at the end.
+      constexpr int LPR8 = D / 16;
+      constexpr int RPW8 = 64 / LPR8;
+      constexpr int ITER8 = kWaves * RPW8 * kInFlight;
+      constexpr int PAIR8 = 2 * ITER8;
+      static_assert(PAIR8 == decode_pair_rows_int8(D, GC), "host and kernel int8 pair sizes");
+      const int grp8 = lane / LPR8, c8 = lane % LPR8;
       const int Tc = L;
       const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + ((int64_t)b * g.nR + idx) * g.max_len * D;
       const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + ((int64_t)b * g.nR + idx) * g.max_len * D;
       const float* cks = g.rks + ((int64_t)b * g.nR + idx) * g.max_len;
       const float* cvs = g.rvs + ((int64_t)b * g.nR + idx) * g.max_len;
-      float qf[GC][8], qoff[GC], cacc[GC];
+      typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+      uint32_t q16[GC][8];  // f16 pairs of dims 16 c8 .. 16 c8 + 15
+      float qoff[GC], qsc[GC], cacc[GC], o8[GC][16];
 #pragma unroll
       for (int gg = 0; gg < GC; ++gg) {
+        const uint4* src = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * g.Hq + h0 + gg) * D) + 2 * c8;
+        const uint4 x0 = src[0], x1 = src[1];
+        const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        float amax = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+        amax = group_max<LPR8>(amax);
+        int ex;
+        frexpf(amax, &ex);  // amax = m 2^ex, m in [0.5, 1) (ex = 0 for a zero head)
+        const float up = ldexpf(1.0f, 15 - ex);
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qf[gg][2 * e] = bf16_lo(qw[gg][e]);
-          qf[gg][2 * e + 1] = bf16_hi(qw[gg][e]);
-          sum += qf[gg][2 * e] + qf[gg][2 * e + 1];
+        for (int e = 0; e < 8; ++e) {
+          const f16x2_t hq = {(_Float16)(bf16_lo(w[e]) * up), (_Float16)(bf16_hi(w[e]) * up)};
+          q16[gg][e] = __builtin_bit_cast(uint32_t, hq);
+          sum += (float)hq.x + (float)hq.y;
         }
-        qoff[gg] = -128.0f * sum;  // codes are stored as code + 128
-        cacc[gg] = 0.f;            // sum of p * scale_v, for the same offset in o
+        qoff[gg] = -1152.0f * sum;
+        qsc[gg] = ldexpf(g.scale_log2, ex - 15);
+        cacc[gg] = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o8[gg][e] = 0.f;
       }
-      auto load8 = [&](u32x4_t (&kr)[kInFlight], u32x4_t (&vr)[kInFlight], int base) __attribute__((always_inline)) {
+      struct Rows8 {
+        u32x4_t k, v;
+        float ks, vs;
+      };
+      auto row_of8 = [&](int base, int j) __attribute__((always_inline)) {
+        return base + (j * kWaves + wave) * RPW8 + grp8;
+      };
+      auto load8 = [&](Rows8 (&r)[kInFlight], Rows8 (&)[kInFlight], int base) __attribute__((always_inline)) {
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
-          const int row = min(row_of(base, j), Tc - 1);
-          const u32x2_t kc = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(ck8 + (int64_t)row * D) + c);
-          const u32x2_t vc = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(cv8 + (int64_t)row * D) + c);
-          kr[j] = u32x4_t{kc.x, kc.y, __float_as_uint(cks[row]), 0u};
-          vr[j] = u32x4_t{vc.x, vc.y, __float_as_uint(cvs[row]), 0u};
+          const int row = min(row_of8(base, j), Tc - 1);
+          r[j].k = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ck8 + (int64_t)row * D) + c8);
+          r[j].v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cv8 + (int64_t)row * D) + c8);
+          r[j].ks = cks[row];
+          r[j].vs = cvs[row];
         }
       };
-      auto process8 = [&](const u32x4_t (&kr)[kInFlight], const u32x4_t (&vr)[kInFlight], int base)
+      auto process8 = [&](const Rows8 (&r)[kInFlight], const Rows8 (&)[kInFlight], int base)
           __attribute__((always_inline)) {
         float s[kInFlight][GC];
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
-          const bool valid = row_of(base, j) < Tc;
-          float ku[8];
+          const bool valid = row_of8(base, j) < Tc;
+          uint32_t kh[8];  // f16 pairs 1024 + b of the 16 codes
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ku[e] = (float)((kr[j][e >> 2] >> (8 * (e & 3))) & 0xffu);
+          for (int e = 0; e < 4; ++e) {
+            kh[2 * e] = __builtin_amdgcn_perm(0x64646464u, r[j].k[e], 0x04010400u);
+            kh[2 * e + 1] = __builtin_amdgcn_perm(0x64646464u, r[j].k[e], 0x04030402u);
+          }
 #pragma unroll
           for (int gg = 0; gg < GC; ++gg) {
             float acc = qoff[gg];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) acc = fmaf(ku[e], qf[gg][e], acc);
-            acc = group_sum<LPR>(acc);
-            s[j][gg] = valid ? acc * (__uint_as_float(kr[j].z) * g.scale_log2) : -INFINITY;
+            for (int e = 0; e < 8; ++e)
+              acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, kh[e]), __builtin_bit_cast(f16x2_t, q16[gg][e]),
+                                           acc, false);
+            acc = group_sum<LPR8>(acc);
+            s[j][gg] = valid ? acc * (r[j].ks * qsc[gg]) : -INFINITY;
           }
         }
 #pragma unroll
@@ -528,28 +574,66 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
           l[gg] *= alpha;
           cacc[gg] *= alpha;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) o[gg][e] *= alpha;
+          for (int e = 0; e < 16; ++e) o8[gg][e] *= alpha;
 #pragma unroll
           for (int j = 0; j < kInFlight; ++j) {
             const float p = exp2_fast(s[j][gg] - mu);
-            const float pv = p * __uint_as_float(vr[j].z);
+            const float pv = p * r[j].vs;
             l[gg] += p;
             cacc[gg] += pv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              o[gg][e] = fmaf(pv, (float)((vr[j][e >> 2] >> (8 * (e & 3))) & 0xffu), o[gg][e]);
+            for (int e = 0; e < 16; ++e)
+              o8[gg][e] = fmaf(pv, (float)((r[j].v[e >> 2] >> (8 * (e & 3))) & 0xffu), o8[gg][e]);
           }
           m[gg] = mn;
         }
       };
       if (Tc > 0) {
-        u32x4_t ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
-        stream_pairs(ka, va, kb, vb, load8, process8, Tc, (Tc + PAIR - 1) / PAIR);
+        Rows8 ra[kInFlight], rb[kInFlight];
+        stream_pairs(ra, ra, rb, rb, load8, process8, Tc, (Tc + PAIR8 - 1) / PAIR8,
+                     std::integral_constant<int, PAIR8>(), std::integral_constant<int, ITER8>());
       }
+      // merge the row groups of the wave (16 dims per lane), then hand the
+      // wave's state to the 8-dims-per-lane layout of the code below: lane
+      // c < LPR takes dims 8c .. 8c+7 (half c mod 2 of lane c/2); the other
+      // row groups are left empty
 #pragma unroll
       for (int gg = 0; gg < GC; ++gg)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[gg][e] = fmaf(-128.0f, cacc[gg], o[gg][e]);
+        for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-128.0f, cacc[gg], o8[gg][e]);
+#pragma unroll
+      for (int off = LPR8; off < 64; off <<= 1) {
+#pragma unroll
+        for (int gg = 0; gg < GC; ++gg) {
+          const float mo = __shfl_xor(m[gg], off);
+          const float lo = __shfl_xor(l[gg], off);
+          const float mn = fmaxf(m[gg], mo);
+          const float mu = max_or_zero(mn);
+          const float a1 = exp2_fast(m[gg] - mu);
+          const float a2 = exp2_fast(mo - mu);
+          l[gg] = l[gg] * a1 + lo * a2;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float oo = __shfl_xor(o8[gg][e], off);
+            o8[gg][e] = o8[gg][e] * a1 + oo * a2;
+          }
+          m[gg] = mn;
+        }
+      }
+      const int src_lane = c >> 1;
+      const bool keep = grp == 0;
+#pragma unroll
+      for (int gg = 0; gg < GC; ++gg) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lo8 = __shfl(o8[gg][e], src_lane);
+          const float hi8 = __shfl(o8[gg][8 + e], src_lane);
+          o[gg][e] = keep ? ((c & 1) ? hi8 : lo8) : 0.f;
+        }
+        const float mw = __shfl(m[gg], src_lane), lw = __shfl(l[gg], src_lane);
+        m[gg] = keep ? mw : -INFINITY;
+        l[gg] = keep ? lw : 0.f;
+      }
     } else {
       stream_bf16();
     }
@@ -727,9 +811,10 @@ int32_t max_splits_for(int64_t max_len, int32_t slots, int head_chunk) {
 
 DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   DecodePlan p;
-  p.head_chunk = decode_head_chunk(g.G);
+  p.head_chunk = decode_head_chunk(g.G, g.kv_int8 != 0);
   const int n_hc = g.G / p.head_chunk;
-  const int64_t pair = decode_pair_rows(g.D, p.head_chunk);
+  // the larger pair when the retrieval rows are int8 (a multiple of the bf16 one)
+  const int64_t pair = g.kv_int8 ? decode_pair_rows_int8(g.D, p.head_chunk) : decode_pair_rows(g.D, p.head_chunk);
   int64_t total = 0;
   int32_t tmax = 1;
   for (int b = 0; b < g.B; ++b) {
@@ -741,7 +826,8 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   // kMinPairs pairs each, and few enough work-groups per unit for its records.
   auto round_pair = [&](int64_t x) { return (x + pair - 1) / pair * pair; };
   int64_t ts = round_pair((total + 2047) / 2048);
-  if (ts < kMinPairs * pair) ts = kMinPairs * pair;
+  const int min_pairs = g.kv_int8 ? kMinPairsInt8 : kMinPairs;
+  if (ts < min_pairs * pair) ts = min_pairs * pair;
   const int64_t ts_cap = round_pair(((int64_t)tmax + g.max_splits - 1) / g.max_splits);
   if (ts < ts_cap) ts = ts_cap;
   static const int64_t env_ts = [] {
@@ -756,6 +842,20 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   return p;
 }
 
+// int8 retrieval caches use head chunks of at most 4 (decode_head_chunk).
+template <int DD, int GG>
+hipError_t launch_dg(const Geom& g, const Seqs& q, const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
+  if constexpr (GG <= 4) {
+    if (g.kv_int8) {
+      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), grid, block, 0, s, g, q, a);
+      return hipGetLastError();
+    }
+  }
+  if (g.kv_int8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_kernel<DD, GG, false>), grid, block, 0, s, g, q, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p, const uint16_t* qin,
                          const uint16_t* kin, const uint16_t* vin, uint16_t* out, hipStream_t s) {
   DecodeArgs a{qin, kin, vin, out, p.split_tokens, p.splits_r, p.splits_s};
@@ -763,14 +863,8 @@ hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p, cons
   const int64_t items = (int64_t)g.B * g.nR * n_hc * p.splits_r + (int64_t)g.B * g.nS * n_hc * p.splits_s;
   if (items <= 0) return hipSuccess;
   const dim3 grid((unsigned)items), block(kThreads);
-#define DUO_DECODE_CASE(DD, GG)                                                     \
-  if (g.D == DD && p.head_chunk == GG) {                                            \
-    if (g.kv_int8)                                                                  \
-      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), grid, block, 0, s, g, q, a);  \
-    else                                                                            \
-      hipLaunchKernelGGL((decode_kernel<DD, GG, false>), grid, block, 0, s, g, q, a); \
-    return hipGetLastError();                                                       \
-  }
+#define DUO_DECODE_CASE(DD, GG) \
+  if (g.D == DD && p.head_chunk == GG) return launch_dg<DD, GG>(g, q, a, grid, block, s);
   DUO_DECODE_CASE(128, 1)
   DUO_DECODE_CASE(128, 2)
   DUO_DECODE_CASE(128, 4)

@@ -79,9 +79,9 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   g->rope = c->rope_base > 0.f;
   g->rope_half = g->rope && c->rope_style == DUO_ROPE_HALF;
   g->rope_rho = g->rope ? std::pow((double)c->rope_base, -2.0 / c->head_dim) : 0.0;
-  g->max_splits = duo::max_splits_for(c->max_len, g->slots, duo::decode_head_chunk(g->G));
+  g->max_splits = duo::max_splits_for(c->max_len, g->slots, duo::decode_head_chunk(g->G, g->kv_int8 != 0));
 
-  const int gc = duo::decode_head_chunk(g->G);
+  const int gc = duo::decode_head_chunk(g->G, g->kv_int8 != 0);
   const int64_t units = (int64_t)g->B * g->Hkv * (g->G / gc);
   int64_t off = 0;
   L->lengths_offset = off;
@@ -117,7 +117,7 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
 
 void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   char* base = static_cast<char*>(buf);
-  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / duo::decode_head_chunk(g->G));
+  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / duo::decode_head_chunk(g->G, g->kv_int8 != 0));
   g->lengths = reinterpret_cast<int32_t*>(base + L.lengths_offset);
   g->tickets = reinterpret_cast<uint32_t*>(base + L.work_offset);
   g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units * g->tickets_per_unit));

@@ -81,10 +81,11 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
                           const uint16_t* vin, int32_t chunk, int32_t max_n, uint16_t* out,
                           hipStream_t s);
 
-// Query heads of one KV group handled together by a decode work-group.
-inline int decode_head_chunk(int G) {
+// Query heads of one KV group handled together by a decode work-group (at
+// most 4 with an int8 retrieval cache, whose lanes hold 16 dims each).
+inline int decode_head_chunk(int G, bool kv_int8) {
   for (int c : {8, 4, 2, 1})
-    if (G % c == 0) return c;
+    if (G % c == 0 && !(kv_int8 && c > 4)) return c;
   return 1;
 }
 
@@ -103,6 +104,8 @@ inline int32_t tickets_per_unit(int32_t max_splits) {
 // 64 / (D/8) rows per wave load, 4 loads in flight per lane (2 for chunks of
 // 4 or more query heads), two batches.
 constexpr int decode_pair_rows(int D, int head_chunk) { return 2 * 4 * (64 / (D / 8)) * (head_chunk >= 4 ? 2 : 4); }
+// int8 retrieval rows: a lane loads 16 codes, so a pair holds twice the rows.
+constexpr int decode_pair_rows_int8(int D, int head_chunk) { return 2 * decode_pair_rows(D, head_chunk); }
 
 // Split-K record capacity per (sequence, KV head, head chunk): enough for
 // splits of >= 256 rows, and at most 1024 / head_chunk records so that the

@@ -138,8 +138,8 @@ def test_q8_chunked_prefill_and_decode(d):
 @pytest.mark.parametrize("hq,hkv,mask", [(32, 8, [1, 0, 0, 1, 1, 0, 1, 0]), (16, 2, [1, 0]), (4, 4, [1, 1, 0, 1]),
                                           (24, 3, [0, 1, 1])])
 def test_q8_group_sizes(hq, hkv, mask):
-    """Head chunks of 4, 8, 1 and 1 query heads per decode work-group, and
-    G = 8 (chunks of 8, the two-level merge path)."""
+    """G = 4, 8, 1, 8: with an int8 cache a decode work-group serves at most
+    4 query heads, so G = 8 runs two head chunks per KV head."""
     require_gpu()
     _say(f"groups Hq={hq} Hkv={hkv}")
     q, k, v = qkv(3, 300, hq, hkv, 128, 42, "cuda")
