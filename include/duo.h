@@ -102,6 +102,15 @@ typedef struct duo_config {
   int32_t kv_format;    /* duo_kv_format of the retrieval cache */
   float rope_base;      /* 0: no rotary embedding; > 0: its base (e.g. 10000) */
   int32_t rope_style;   /* duo_rope_style (read when rope_base > 0) */
+  /* Paged retrieval cache (0 = contiguous [B][nR][max_len] rows).  With
+   * page_tokens > 0 the retrieval rows live in a pool of num_pages pages of
+   * page_tokens positions each, shared by all sequences; a sequence takes
+   * pages as it grows (one page covers page_tokens positions of every
+   * retrieval head) and gives them back with duo_cache_release.  max_len
+   * still bounds each sequence.  page_tokens: a power of two, 512..65536
+   * (a page holds whole decode row batches and prefill tiles). */
+  int32_t page_tokens;
+  int64_t num_pages;
 } duo_config;
 
 /* Opaque host-side handle: configuration, head maps, region offsets and the
@@ -109,7 +118,11 @@ typedef struct duo_config {
 typedef struct duo_cache duo_cache;
 
 /* Byte offsets of the regions inside the caller's device buffer (all 256-byte
- * aligned).  nR / nS = number of retrieval / streaming KV heads; retrieval
+ * aligned).  With a paged retrieval cache (page_tokens > 0) rk / rv (and
+ * rks / rvs) are page pools [num_pages][nR][page_tokens][D] (scales
+ * [num_pages][nR][page_tokens]) and page_table int32 [B][max_pages_per_seq]
+ * names the pool page holding positions [j P, (j+1) P) of sequence b
+ * (entries past a sequence's length are unspecified).  nR / nS = number of retrieval / streaming KV heads; retrieval
  * KV head k is stored at index head_index[k] among the retrieval heads
  * (in increasing k), likewise for streaming heads.
  *   lengths  int32 [B]                     tokens stored per sequence
@@ -131,6 +144,9 @@ typedef struct duo_layout {
   int32_t slots_per_streaming_head; /* sink + recent */
   int32_t kv_format;                /* duo_kv_format */
   int64_t rks_offset, rvs_offset;
+  int64_t page_table_offset;        /* -1 for a contiguous cache */
+  int32_t page_tokens, max_pages_per_seq;
+  int64_t num_pages;
 } duo_layout;
 
 /* Lay out a new, empty cache in `dev_buf`.
@@ -141,20 +157,29 @@ typedef struct duo_layout {
  * Errors: INVALID_ARG (null cfg / mask / out, B < 1, Hkv < 1, Hq % Hkv != 0,
  * sink < 0, recent < 1, max_len < 1, misaligned dev_buf, scale < 0 or not
  * finite, kv_format not a duo_kv_format, rope_base < 0 or not finite,
- * rope_style not a duo_rope_style), UNSUPPORTED (head_dim, batch, rope_base
- * > 0 with DUO_KV_INT8), BUFFER_TOO_SMALL, HIP. */
+ * rope_style not a duo_rope_style, page_tokens not 0 or a power of two in
+ * 512..65536, page_tokens > 0 with num_pages < 1), UNSUPPORTED (head_dim,
+ * batch, rope_base > 0 with DUO_KV_INT8), BUFFER_TOO_SMALL, HIP. */
 duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
                           size_t* required_bytes, duo_cache** out, void* stream);
 
 /* Wrap a buffer that already holds a cache laid out for `cfg` (for example a
  * copy of another handle's buffer: checkpoint / resume), with the host
  * lengths `lengths[B]` (each 0..max_len).  Enqueues nothing.  Same errors as
- * duo_cache_init, plus INVALID_ARG for null or out-of-range lengths. */
+ * duo_cache_init, plus INVALID_ARG for null or out-of-range lengths, and for
+ * a paged cache any nonzero length (the page table is not recoverable from
+ * the buffer alone). */
 duo_status duo_cache_attach(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
                             const int64_t* lengths, duo_cache** out);
 
 /* Free the host handle only (the device buffer stays the caller's). */
 void duo_cache_destroy(duo_cache* h);
+
+/* Sequence b ends: its length becomes 0 and, in a paged cache, its pages go
+ * back to the pool; the slot can start a new sequence.  Enqueues a small
+ * kernel (the device copy of the length) on `stream`.
+ * Errors: INVALID_ARG (null handle, b out of range), HIP. */
+duo_status duo_cache_release(duo_cache* h, int32_t b, void* stream);
 
 /* Append n_new[b] tokens to every sequence without attending.
  * k, v: bf16 [B][chunk][Hkv][D]; rows i >= n_new[b] of sequence b are
@@ -165,9 +190,21 @@ void duo_cache_destroy(duo_cache* h);
  * (older ones would be overwritten at once).  Lengths advance by n_new.
  * n_new: HOST int32 [B], each in [0, chunk].
  * Errors: INVALID_ARG (null handle/k/v/n_new, misaligned, chunk < 1,
- * n_new out of range), CAPACITY (len_b + n_new[b] > max_len), HIP. */
+ * n_new out of range), CAPACITY (len_b + n_new[b] > max_len, or a paged
+ * cache without enough free pages), HIP. */
 duo_status duo_cache_append(duo_cache* h, const void* k, const void* v,
                             const int32_t* n_new, int32_t chunk, void* stream);
+
+/* Packed (variable-length) inputs: the new rows of all sequences back to
+ * back, sequence b's in rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of
+ * k, v: bf16 [cu_seqlens[B]][Hkv][D] (q, out: [cu_seqlens[B]][Hq][D]).
+ * cu_seqlens: HOST int32 [B+1], cu_seqlens[0] = 0, nondecreasing; a
+ * sequence with no rows is skipped.  Otherwise as duo_cache_append and
+ * duo_prefill (INVALID_ARG also for a bad cu_seqlens). */
+duo_status duo_cache_append_varlen(duo_cache* h, const void* k, const void* v,
+                                   const int32_t* cu_seqlens, void* stream);
+duo_status duo_prefill_varlen(duo_cache* h, const void* q, const void* k, const void* v,
+                              const int32_t* cu_seqlens, void* out, void* stream);
 
 /* Pre-filling: for every new token i < n_new[b] of sequence b at position
  * p = len_b + i and every query head, out = softmax(scale * q k^T) v over
@@ -195,6 +232,11 @@ duo_status duo_cache_lengths(const duo_cache* h, int64_t* out /* [B] */);
 duo_status duo_cache_layout(const duo_cache* h, duo_layout* out);
 /* out[k] = index of KV head k among the heads of its own kind. */
 duo_status duo_cache_head_index(const duo_cache* h, int32_t* out /* [Hkv] */);
+/* Paged cache: *n = pages held by sequence b, and their pool indices in
+ * out[0 .. min(*n, cap)) (in position order); *free_pages = pages left in
+ * the pool.  A contiguous cache reports 0 pages. */
+duo_status duo_cache_pages(const duo_cache* h, int32_t b, int32_t* out, int32_t cap, int32_t* n,
+                           int64_t* free_pages);
 
 #ifdef __cplusplus
 }

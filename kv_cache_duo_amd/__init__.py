@@ -55,6 +55,7 @@ class _Config(ctypes.Structure):
         ("max_len", ctypes.c_int64), ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
         ("scale", ctypes.c_float), ("kv_head_is_retrieval", ctypes.POINTER(ctypes.c_uint8)),
         ("kv_format", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
+        ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int64),
     ]
 
 
@@ -67,6 +68,8 @@ class Layout(ctypes.Structure):
         ("n_retrieval", ctypes.c_int32), ("n_streaming", ctypes.c_int32),
         ("slots_per_streaming_head", ctypes.c_int32), ("kv_format", ctypes.c_int32),
         ("rks_offset", ctypes.c_int64), ("rvs_offset", ctypes.c_int64),
+        ("page_table_offset", ctypes.c_int64), ("page_tokens", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int64),
     ]
 
 
@@ -87,6 +90,10 @@ _SIGNATURES = {
     "duo_cache_lengths": (ctypes.c_int, [_P, _I64P]),
     "duo_cache_layout": (ctypes.c_int, [_P, ctypes.POINTER(Layout)]),
     "duo_cache_head_index": (ctypes.c_int, [_P, _I32P]),
+    "duo_cache_release": (ctypes.c_int, [_P, ctypes.c_int32, _P]),
+    "duo_cache_append_varlen": (ctypes.c_int, [_P, _P, _P, _I32P, _P]),
+    "duo_prefill_varlen": (ctypes.c_int, [_P, _P, _P, _P, _I32P, _P, _P]),
+    "duo_cache_pages": (ctypes.c_int, [_P, ctypes.c_int32, _I32P, ctypes.c_int32, _I32P, _I64P]),
 }
 
 _lib = None
@@ -138,6 +145,8 @@ class Config:
     kv_format: int = 0  # DUO_KV_BF16; DUO_KV_INT8 = 1 stores retrieval rows as int8 + fp32 row scales
     rope_base: float = 0.0  # > 0: rotary position embedding applied to q and k inside the library
     rope_style: int = 0     # DUO_ROPE_INTERLEAVED (pairs 2i, 2i+1) or DUO_ROPE_HALF (pairs i, i + D/2)
+    page_tokens: int = 0    # > 0: paged retrieval cache, pages of this many positions
+    num_pages: int = 0      # paged: pages in the pool
 
     def _c(self):
         mask = (ctypes.c_uint8 * max(len(self.kv_head_is_retrieval), 1))(
@@ -145,7 +154,7 @@ class Config:
         c = _Config(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim, self.max_len,
                     self.sink, self.recent, self.scale,
                     ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)), self.kv_format, self.rope_base,
-                    self.rope_style)
+                    self.rope_style, self.page_tokens, self.num_pages)
         return c, mask  # keep the mask alive for the call
 
 
@@ -206,6 +215,16 @@ class Cache:
         _check(load_library().duo_cache_head_index(self._h, out), "duo_cache_head_index")
         return list(out)
 
+    def pages(self, b: int) -> tuple[list[int], int]:
+        """(pool pages of sequence b in position order, free pages left)."""
+        n = ctypes.c_int32(0)
+        free = ctypes.c_int64(0)
+        lib = load_library()
+        _check(lib.duo_cache_pages(self._h, b, None, 0, ctypes.byref(n), ctypes.byref(free)), "duo_cache_pages")
+        out = (ctypes.c_int32 * max(n.value, 1))()
+        _check(lib.duo_cache_pages(self._h, b, out, n.value, ctypes.byref(n), None), "duo_cache_pages")
+        return list(out)[:n.value], int(free.value)
+
 
 def duo_cache_init(cfg: Config, buf: torch.Tensor, stream=None) -> Cache:
     if buf.device.type != "cuda" or buf.dtype != torch.uint8 or not buf.is_contiguous():
@@ -256,6 +275,37 @@ def duo_prefill(cache: Cache, q, k, v, n_new, out, stream=None) -> None:
                                       _stream(stream)), "duo_prefill")
 
 
+def _cu_array(cu_seqlens, batch):
+    if len(cu_seqlens) != batch + 1:
+        raise ValueError(f"cu_seqlens has {len(cu_seqlens)} entries, expected {batch + 1}")
+    return (ctypes.c_int32 * (batch + 1))(*[int(x) for x in cu_seqlens])
+
+
+def duo_cache_append_varlen(cache: Cache, k, v, cu_seqlens, stream=None) -> None:
+    """Packed rows: k, v [cu_seqlens[-1], Hkv, D]."""
+    cfg = cache.cfg
+    shape = (int(cu_seqlens[-1]), cfg.num_kv_heads, cfg.head_dim)
+    pk, pv = _dev(k, shape, "k"), _dev(v, shape, "v")
+    _check(load_library().duo_cache_append_varlen(cache.handle, pk, pv, _cu_array(cu_seqlens, cfg.batch),
+                                                  _stream(stream)), "duo_cache_append_varlen")
+
+
+def duo_prefill_varlen(cache: Cache, q, k, v, cu_seqlens, out, stream=None) -> None:
+    """Packed rows: q, out [cu_seqlens[-1], Hq, D]; k, v [cu_seqlens[-1], Hkv, D]."""
+    cfg = cache.cfg
+    rows = int(cu_seqlens[-1])
+    pq = _dev(q, (rows, cfg.num_q_heads, cfg.head_dim), "q")
+    po = _dev(out, (rows, cfg.num_q_heads, cfg.head_dim), "out")
+    kv_shape = (rows, cfg.num_kv_heads, cfg.head_dim)
+    pk, pv = _dev(k, kv_shape, "k"), _dev(v, kv_shape, "v")
+    _check(load_library().duo_prefill_varlen(cache.handle, pq, pk, pv, _cu_array(cu_seqlens, cfg.batch), po,
+                                             _stream(stream)), "duo_prefill_varlen")
+
+
+def duo_cache_release(cache: Cache, b: int, stream=None) -> None:
+    _check(load_library().duo_cache_release(cache.handle, int(b), _stream(stream)), "duo_cache_release")
+
+
 def duo_decode(cache: Cache, q, k, v, out, stream=None) -> None:
     cfg = cache.cfg
     pq = _dev(q, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
@@ -283,17 +333,37 @@ def cache_views(cache: Cache):
         return buf[off:off + nbytes].view(dtype).view(*shape)
 
     rdt = torch.uint8 if lay.kv_format == DUO_KV_INT8 else torch.bfloat16
-    rshape = (cfg.batch, lay.n_retrieval, cfg.max_len, d)
-    views = {
-        "lengths": region(lay.lengths_offset, (cfg.batch,), torch.int32),
-        "rk": region(lay.rk_offset, rshape, rdt),
-        "rv": region(lay.rv_offset, rshape, rdt),
+    views = {"lengths": region(lay.lengths_offset, (cfg.batch,), torch.int32)}
+    if lay.page_tokens > 0:
+        # pools, the page table, and copies of every sequence's rows gathered
+        # through the pages it holds: rk/rv [B, nR, pages held * P, D]
+        pt = lay.page_tokens
+        pshape = (lay.num_pages, lay.n_retrieval, pt, d)
+        views["page_table"] = region(lay.page_table_offset, (cfg.batch, lay.max_pages_per_seq), torch.int32)
+        names = [("rk", lay.rk_offset, pshape, rdt), ("rv", lay.rv_offset, pshape, rdt)]
+        if lay.kv_format == DUO_KV_INT8:
+            names += [("rks", lay.rks_offset, pshape[:3], torch.float32), ("rvs", lay.rvs_offset, pshape[:3], torch.float32)]
+        held = [cache.pages(b)[0] for b in range(cfg.batch)]
+        most = max([len(h) for h in held] + [1])
+        for name, off, shape, dt in names:
+            pool = region(off, shape, dt)
+            views[name + "_pool"] = pool
+            g = torch.zeros((cfg.batch, lay.n_retrieval, most * pt) + tuple(shape[3:]), dtype=dt, device=buf.device)
+            for b, pages in enumerate(held):
+                for j, page in enumerate(pages):
+                    g[b, :, j * pt:(j + 1) * pt] = pool[page]
+            views[name] = g
+    else:
+        rshape = (cfg.batch, lay.n_retrieval, cfg.max_len, d)
+        views["rk"] = region(lay.rk_offset, rshape, rdt)
+        views["rv"] = region(lay.rv_offset, rshape, rdt)
+        if lay.kv_format == DUO_KV_INT8:
+            views["rks"] = region(lay.rks_offset, rshape[:3], torch.float32)
+            views["rvs"] = region(lay.rvs_offset, rshape[:3], torch.float32)
+    views.update({
         "sk": region(lay.sk_offset, (cfg.batch, lay.n_streaming, lay.slots_per_streaming_head, d),
                      torch.bfloat16),
         "sv": region(lay.sv_offset, (cfg.batch, lay.n_streaming, lay.slots_per_streaming_head, d),
                      torch.bfloat16),
-    }
-    if lay.kv_format == DUO_KV_INT8:
-        views["rks"] = region(lay.rks_offset, rshape[:3], torch.float32)
-        views["rvs"] = region(lay.rvs_offset, rshape[:3], torch.float32)
+    })
     return views

@@ -32,8 +32,8 @@ __global__ __launch_bounds__(kAppendThreads) void zero_words_kernel(uint32_t* p,
 // (nr_blocks = 0 when only streaming heads are stored).
 template <int D>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, const uint16_t* __restrict__ k,
-                                                                const uint16_t* __restrict__ v, int32_t chunk,
-                                                                int32_t xr, int32_t xs, int32_t nr_blocks) {
+                                                                const uint16_t* __restrict__ v, int32_t xr,
+                                                                int32_t xs, int32_t nr_blocks) {
   constexpr int CH = D / 8;                  // 16-byte chunks per row
   constexpr int ROWS_PER_PASS = kAppendThreads / CH;
   int id = blockIdx.x;
@@ -73,17 +73,18 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
     int i = retrieval ? j : (j < sinks_here ? j : first_ring + (j - sinks_here));
     int64_t p = (int64_t)len + i;
     uint16_t *dk, *dv;
+    int64_t rrow = 0;  // retrieval row (contiguous or through the page table)
     if (retrieval) {
-      int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + p;
-      dk = g.rk + row * D;
-      dv = g.rv + row * D;
+      rrow = retrieval_row0(g, b, idx, (int)p) + p;
+      dk = g.rk + rrow * D;
+      dv = g.rv + rrow * D;
     } else {
       int64_t slot = p < g.S ? p : g.S + (p - g.S) % g.W;
       int64_t row = ((int64_t)b * g.nS + idx) * g.slots + slot;
       dk = g.sk + row * D;
       dv = g.sv + row * D;
     }
-    int64_t src = (((int64_t)b * chunk + i) * g.Hkv + kvh) * D;
+    int64_t src = (((int64_t)q.off[b] + i) * g.Hkv + kvh) * D;
     uint4 kx = reinterpret_cast<const uint4*>(k + src)[c];
     const uint4 vx = reinterpret_cast<const uint4*>(v + src)[c];
     if (g.rope) {
@@ -93,9 +94,8 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
     }
     if (retrieval && g.kv_int8) {
       // int8 row: the CH lanes of the row agree on its scale (group max)
-      const int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + p;
-      store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rk) + row * D, g.rks + row, kx, c);
-      store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rv) + row * D, g.rvs + row, vx, c);
+      store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rk) + rrow * D, g.rks + rrow, kx, c);
+      store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rv) + rrow * D, g.rvs + rrow, vx, c);
     } else {
       reinterpret_cast<uint4*>(dk)[c] = kx;
       reinterpret_cast<uint4*>(dv)[c] = vx;
@@ -103,7 +103,18 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
   }
 }
 
+// Page-table entries and device lengths written by the host's calls.
+__global__ __launch_bounds__(kAppendThreads) void word_writes_kernel(int32_t* base, WordWrites w) {
+  for (int i = threadIdx.x; i < w.n; i += blockDim.x) base[w.index[i]] = w.value[i];
+}
+
 }  // namespace
+
+hipError_t launch_word_writes(int32_t* base, const WordWrites& w, hipStream_t s) {
+  if (w.n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(word_writes_kernel, dim3(1), dim3(kAppendThreads), 0, s, base, w);
+  return hipGetLastError();
+}
 
 hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s) {
   if (words <= 0) return hipSuccess;
@@ -113,8 +124,8 @@ hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v, int32_t chunk,
-                         int32_t max_n, hipStream_t s, int kinds) {
+hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v, int32_t max_n,
+                         hipStream_t s, int kinds) {
   int32_t xr = (max_n + kRowsPerBlock - 1) / kRowsPerBlock;
   int32_t xs = (min(max_n, g.slots) + kRowsPerBlock - 1) / kRowsPerBlock;
   if (xr < 1) xr = 1;  // still one block per head so that the lengths are written
@@ -124,11 +135,11 @@ hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const 
   const int64_t blocks = nr_blocks + ns_blocks;
   if (blocks <= 0) return hipSuccess;
   if (g.D == 128)
-    hipLaunchKernelGGL(append_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, chunk,
-                       xr, xs, (int32_t)nr_blocks);
+    hipLaunchKernelGGL(append_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, xr, xs,
+                       (int32_t)nr_blocks);
   else
-    hipLaunchKernelGGL(append_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, chunk,
-                       xr, xs, (int32_t)nr_blocks);
+    hipLaunchKernelGGL(append_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, xr, xs,
+                       (int32_t)nr_blocks);
   return hipGetLastError();
 }
 

@@ -318,9 +318,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   const int npairs = (T + PAIR - 1) / PAIR;
   const int kvh = kv_head_of_unit(g, retrieval ? idx : g.nR + idx);
   const int64_t unit_rows = retrieval ? g.max_len : (int64_t)g.slots;
-  const int64_t cache_off = ((int64_t)b * nkind + idx) * unit_rows * D;
-  uint16_t* ck = (retrieval ? g.rk : g.sk) + cache_off;
-  uint16_t* cv = (retrieval ? g.rv : g.sv) + cache_off;
+  const int64_t unit_row0 = ((int64_t)b * nkind + idx) * unit_rows;  // contiguous rows of the unit
+  uint16_t* ck = (retrieval ? g.rk : g.sk) + unit_row0 * D;          // (streaming units)
+  uint16_t* cv = (retrieval ? g.rv : g.sv) + unit_row0 * D;
+  // Row base of the pair of batches starting at row `base` (rows past
+  // `rows` - 1 read row rows - 1): a paged retrieval cache keeps a pair in
+  // one page; other units are contiguous.
+  auto pair_row0 = [&](int base, int rows) __attribute__((always_inline)) -> int64_t {
+    return (retrieval && g.paged) ? retrieval_row0(g, b, idx, min(base, rows - 1)) : unit_row0;
+  };
   const uint16_t* nk = a.k + ((int64_t)b * g.Hkv + kvh) * D;
   const uint16_t* nv = a.v + ((int64_t)b * g.Hkv + kvh) * D;
   const int h0 = kvh * g.G + hc * GC;
@@ -379,12 +385,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // Loads are unconditional per lane (rows past the unit's end re-read its
   // last row and get a -inf score), so the compiler can count outstanding
   // loads and wait only for the older batch.
-  auto load = [&](uint4 (&kr)[kInFlight], uint4 (&vr)[kInFlight], int base) {
+  auto load = [&](uint4 (&kr)[kInFlight], uint4 (&vr)[kInFlight], int base, int64_t r0) {
+    const uint16_t* ckp = (retrieval ? g.rk : g.sk) + r0 * D;
+    const uint16_t* cvp = (retrieval ? g.rv : g.sv) + r0 * D;
 #pragma unroll
     for (int j = 0; j < kInFlight; ++j) {
       const int row = min(row_of(base, j), Tst - 1);
-      const uint16_t* pk = row == new_row ? nk : ck + (int64_t)row * D;
-      const uint16_t* pv = row == new_row ? nv : cv + (int64_t)row * D;
+      const uint16_t* pk = row == new_row ? nk : ckp + (int64_t)row * D;
+      const uint16_t* pv = row == new_row ? nv : cvp + (int64_t)row * D;
       kr[j] = load_nt(reinterpret_cast<const uint4*>(pk) + c);  // streamed once: non-temporal
       vr[j] = load_nt(reinterpret_cast<const uint4*>(pv) + c);
     }
@@ -444,8 +452,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
                           auto pair_c, auto iter_c) __attribute__((always_inline)) {
     constexpr int P = decltype(pair_c)::value, IT = decltype(iter_c)::value;  // rows per pair, per batch
     int base = split * P;
-    ld(ka, va, base);
-    ld(kb, vb, base + IT);
+    const int64_t r0 = pair_row0(base, rows);
+    ld(ka, va, base, r0);
+    ld(kb, vb, base + IT, r0);
     for (int it = 0;; it ^= 1) {
       if (threadIdx.x == 0) {
         sm_claim[it] = ns + (int)claimed;
@@ -455,10 +464,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       const int p_next = __builtin_amdgcn_readfirstlane(sm_claim[it]);
       const bool more = p_next < npr;
       const int nbase = more ? p_next * P : rows;
+      const int64_t nr0 = pair_row0(nbase, rows);  // page lookup: in flight while this pair is scored
       pr(ka, va, base);
-      ld(ka, va, nbase);
+      ld(ka, va, nbase, nr0);
       pr(kb, vb, base + IT);
-      ld(kb, vb, nbase + IT);
+      ld(kb, vb, nbase + IT, nr0);
       own_new = own_new || (new_row >= base && new_row < base + P);
       if (!more) break;
       base = nbase;
@@ -491,10 +501,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       static_assert(PAIR8 == decode_pair_rows_int8(D, GC), "host and kernel int8 pair sizes");
       const int grp8 = lane / LPR8, c8 = lane % LPR8;
       const int Tc = L;
-      const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + ((int64_t)b * g.nR + idx) * g.max_len * D;
-      const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + ((int64_t)b * g.nR + idx) * g.max_len * D;
-      const float* cks = g.rks + ((int64_t)b * g.nR + idx) * g.max_len;
-      const float* cvs = g.rvs + ((int64_t)b * g.nR + idx) * g.max_len;
       typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
       uint32_t q16[GC][8];  // f16 pairs of dims 16 c8 .. 16 c8 + 15
       float qoff[GC], qsc[GC], cacc[GC], o8[GC][16];
@@ -530,7 +536,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       auto row_of8 = [&](int base, int j) __attribute__((always_inline)) {
         return base + (j * kWaves + wave) * RPW8 + grp8;
       };
-      auto load8 = [&](Rows8 (&r)[kInFlight], Rows8 (&)[kInFlight], int base) __attribute__((always_inline)) {
+      auto load8 = [&](Rows8 (&r)[kInFlight], Rows8 (&)[kInFlight], int base, int64_t r0) __attribute__((always_inline)) {
+        const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + r0 * D;
+        const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + r0 * D;
+        const float* cks = g.rks + r0;
+        const float* cvs = g.rvs + r0;
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
           const int row = min(row_of8(base, j), Tc - 1);
@@ -707,14 +717,13 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   if (hc == 0 && own_new && threadIdx.x < LPR) {
     const uint4 kx = knew;  // threads 0..LPR-1 hold chunks c = 0..LPR-1
     const uint4 vx = reinterpret_cast<const uint4*>(nv)[threadIdx.x];
+    const int64_t row = retrieval ? retrieval_row0(g, b, idx, new_row) + new_row : unit_row0 + new_row;
     if (q8) {
-      const int64_t row = ((int64_t)b * g.nR + idx) * g.max_len + new_row;
       store_int8_row<LPR>(reinterpret_cast<uint8_t*>(g.rk) + row * D, g.rks + row, kx, threadIdx.x);
       store_int8_row<LPR>(reinterpret_cast<uint8_t*>(g.rv) + row * D, g.rvs + row, vx, threadIdx.x);
     } else {
-      const int64_t off = (int64_t)new_row * D;
-      reinterpret_cast<uint4*>(ck + off)[threadIdx.x] = kx;
-      reinterpret_cast<uint4*>(cv + off)[threadIdx.x] = vx;
+      reinterpret_cast<uint4*>((retrieval ? g.rk : g.sk) + row * D)[threadIdx.x] = kx;
+      reinterpret_cast<uint4*>((retrieval ? g.rv : g.sv) + row * D)[threadIdx.x] = vx;
     }
     if (threadIdx.x == 0 && kvh == 0) g.lengths[b] = L + 1;
   }

@@ -22,6 +22,11 @@ struct duo_cache {
   duo::Geom geom;
   duo_layout layout;
   std::vector<int64_t> len;  // host mirror of the stored tokens per sequence
+  int32_t* buf_words;        // the device buffer, as int32 words
+  // paged retrieval cache: free pool pages (used from the back) and the
+  // pages of every sequence in position order (host mirror of page_table)
+  std::vector<int32_t> free_pages;
+  std::vector<std::vector<int32_t>> seq_pages;
 };
 
 namespace {
@@ -48,6 +53,11 @@ duo_status check_config(const duo_config* c) {
   if (c->batch > DUO_MAX_BATCH || c->num_kv_heads > duo::kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
   if (c->max_len > kMaxLen || (int64_t)c->sink + c->recent > kMaxLen) return DUO_ERR_UNSUPPORTED;
   if (c->rope_base > 0.f && c->kv_format == DUO_KV_INT8) return DUO_ERR_UNSUPPORTED;
+  if (c->page_tokens != 0) {
+    const int32_t p = c->page_tokens;
+    if (p < 512 || p > 65536 || (p & (p - 1)) != 0) return DUO_ERR_INVALID_ARG;
+    if (c->num_pages < 1 || c->num_pages > (int64_t(1) << 31) - 1) return DUO_ERR_INVALID_ARG;
+  }
   return DUO_OK;
 }
 
@@ -86,6 +96,22 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   int64_t off = 0;
   L->lengths_offset = off;
   off = align_up(off + 4 * (int64_t)g->B);
+  // paged: page table right after the lengths (word indices stay small)
+  L->page_table_offset = -1;
+  g->paged = c->page_tokens > 0;
+  int64_t pool_rows = (int64_t)g->B * g->max_len;  // retrieval rows per head
+  if (g->paged) {
+    int shift = 0;
+    while ((1 << shift) < c->page_tokens) ++shift;
+    g->page_shift = shift;
+    g->max_pages = (int32_t)((c->max_len + c->page_tokens - 1) / c->page_tokens);
+    L->page_tokens = c->page_tokens;
+    L->max_pages_per_seq = g->max_pages;
+    L->num_pages = c->num_pages;
+    L->page_table_offset = off;
+    off = align_up(off + 4 * (int64_t)g->B * g->max_pages);
+    pool_rows = c->num_pages * c->page_tokens;
+  }
   L->work_offset = off;  // merge tickets, then the split records
   g->tickets_per_unit = duo::tickets_per_unit(g->max_splits);
   off = align_up(off + 4 * units * g->tickets_per_unit);
@@ -95,15 +121,15 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   const int64_t rrow = g->kv_int8 ? (int64_t)g->D : row;  // retrieval row bytes
   L->kv_format = c->kv_format;
   L->rk_offset = off;
-  off = align_up(off + (int64_t)g->B * nr * g->max_len * rrow);
+  off = align_up(off + pool_rows * nr * rrow);
   L->rv_offset = off;
-  off = align_up(off + (int64_t)g->B * nr * g->max_len * rrow);
+  off = align_up(off + pool_rows * nr * rrow);
   L->rks_offset = L->rvs_offset = -1;
   if (g->kv_int8) {
     L->rks_offset = off;
-    off = align_up(off + (int64_t)g->B * nr * g->max_len * 4);
+    off = align_up(off + pool_rows * nr * 4);
     L->rvs_offset = off;
-    off = align_up(off + (int64_t)g->B * nr * g->max_len * 4);
+    off = align_up(off + pool_rows * nr * 4);
   }
   L->sk_offset = off;
   off = align_up(off + (int64_t)g->B * ns * g->slots * row);
@@ -127,6 +153,7 @@ void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   g->rvs = L.rvs_offset >= 0 ? reinterpret_cast<float*>(base + L.rvs_offset) : nullptr;
   g->sk = reinterpret_cast<uint16_t*>(base + L.sk_offset);
   g->sv = reinterpret_cast<uint16_t*>(base + L.sv_offset);
+  g->page_table = L.page_table_offset >= 0 ? reinterpret_cast<const int32_t*>(base + L.page_table_offset) : nullptr;
 }
 
 duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int64_t* lengths, duo_cache** out,
@@ -141,7 +168,8 @@ duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int6
   if ((int64_t)bytes < L.total_bytes) return DUO_ERR_BUFFER_TOO_SMALL;
   if (lengths != nullptr)
     for (int b = 0; b < cfg->batch; ++b)
-      if (lengths[b] < 0 || lengths[b] > cfg->max_len) return DUO_ERR_INVALID_ARG;
+      if (lengths[b] < 0 || lengths[b] > cfg->max_len || (cfg->page_tokens > 0 && lengths[b] != 0))
+        return DUO_ERR_INVALID_ARG;
   duo_cache* h = new (std::nothrow) duo_cache;
   if (h == nullptr) return DUO_ERR_INVALID_ARG;
   h->cfg = *cfg;
@@ -153,6 +181,12 @@ duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int6
   h->len.assign(cfg->batch, 0);
   if (lengths != nullptr)
     for (int b = 0; b < cfg->batch; ++b) h->len[b] = lengths[b];
+  h->buf_words = static_cast<int32_t*>(buf);
+  h->seq_pages.assign(cfg->batch, {});
+  if (h->geom.paged) {
+    h->free_pages.resize((size_t)cfg->num_pages);
+    for (int64_t i = 0; i < cfg->num_pages; ++i) h->free_pages[(size_t)i] = (int32_t)(cfg->num_pages - 1 - i);
+  }
   if (zero) {
     // lengths, then the merge tickets (contiguous up to the split records)
     const int64_t words = (reinterpret_cast<char*>(h->geom.partials) - reinterpret_cast<char*>(h->geom.lengths)) / 4;
@@ -181,8 +215,109 @@ duo_status check_chunk(const duo_cache* h, const int32_t* n_new, int32_t chunk, 
   for (int b = 0; b < h->cfg.batch; ++b) {
     sq->len[b] = (int32_t)h->len[b];
     sq->n[b] = n_new[b];
+    sq->off[b] = b * chunk;
   }
   *max_n = mx;
+  return DUO_OK;
+}
+
+// Packed inputs: cu_seqlens[B+1] host, from 0, nondecreasing.
+duo_status check_varlen(const duo_cache* h, const int32_t* cu, duo::Seqs* sq, int32_t* max_n) {
+  if (cu == nullptr || cu[0] != 0) return DUO_ERR_INVALID_ARG;
+  int32_t mx = 0;
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    const int64_t n = (int64_t)cu[b + 1] - cu[b];
+    if (n < 0) return DUO_ERR_INVALID_ARG;
+    if (h->len[b] + n > h->cfg.max_len) return DUO_ERR_CAPACITY;
+    mx = n > mx ? (int32_t)n : mx;
+  }
+  std::memset(sq, 0, sizeof(*sq));
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    sq->len[b] = (int32_t)h->len[b];
+    sq->n[b] = cu[b + 1] - cu[b];
+    sq->off[b] = cu[b];
+  }
+  *max_n = mx;
+  return DUO_OK;
+}
+
+// Paged cache: pages that the call's new tokens need, checked before
+// anything is enqueued.
+duo_status check_pages(const duo_cache* h, const duo::Seqs& sq) {
+  if (!h->geom.paged) return DUO_OK;
+  const int64_t p = h->cfg.page_tokens;
+  int64_t need = 0;
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    const int64_t pages = ((int64_t)sq.len[b] + sq.n[b] + p - 1) / p;
+    need += pages - (int64_t)h->seq_pages[b].size();
+  }
+  return need <= (int64_t)h->free_pages.size() ? DUO_OK : DUO_ERR_CAPACITY;
+}
+
+// Take the pages (check_pages passed) and enqueue the page-table writes.
+hipError_t take_pages(duo_cache* h, const duo::Seqs& sq, hipStream_t s) {
+  if (!h->geom.paged) return hipSuccess;
+  const int64_t p = h->cfg.page_tokens;
+  const int64_t table_word = h->layout.page_table_offset / 4;
+  duo::WordWrites w;
+  w.n = 0;
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    const int64_t pages = ((int64_t)sq.len[b] + sq.n[b] + p - 1) / p;
+    while ((int64_t)h->seq_pages[b].size() < pages) {
+      const int32_t page = h->free_pages.back();
+      h->free_pages.pop_back();
+      w.index[w.n] = (int32_t)(table_word + (int64_t)b * h->geom.max_pages + (int64_t)h->seq_pages[b].size());
+      w.value[w.n] = page;
+      ++w.n;
+      h->seq_pages[b].push_back(page);
+      if (w.n == duo::kWordWritesPerLaunch) {
+        hipError_t e = duo::launch_word_writes(h->buf_words, w, s);
+        if (e != hipSuccess) return e;
+        w.n = 0;
+      }
+    }
+  }
+  return w.n > 0 ? duo::launch_word_writes(h->buf_words, w, s) : hipSuccess;
+}
+
+// The kernels of one append call (validated: sq, max_n).
+duo_status append_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const void* k, const void* v, void* stream) {
+  duo_status st = check_pages(h, sq);
+  if (st != DUO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (take_pages(h, sq, s) != hipSuccess) return DUO_ERR_HIP;
+  hipError_t e = duo::launch_append(h->geom, sq, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
+                                    max_n, s);
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += sq.n[b];
+  return DUO_OK;
+}
+
+// The kernels of one prefill call (validated: sq, max_n).
+duo_status prefill_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const void* q, const void* k, const void* v,
+                        void* out, void* stream) {
+  duo_status st = check_pages(h, sq);
+  if (st != DUO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (take_pages(h, sq, s) != hipSuccess) return DUO_ERR_HIP;
+  const uint16_t* kk = static_cast<const uint16_t*>(k);
+  const uint16_t* vv = static_cast<const uint16_t*>(v);
+  // Streaming heads read ring slots that this chunk's append overwrites, so
+  // their rows are stored after the attention.  With rotary embedding the
+  // retrieval rows are stored (rotated) first and the attention reads every
+  // retrieval key from the cache; streaming heads rotate their chunk rows
+  // as they load them.
+  hipError_t e = hipSuccess;
+  if (h->geom.rope) {
+    e = duo::launch_append(h->geom, sq, kk, vv, max_n, s, duo::kAppendRetrieval);
+    if (e != hipSuccess) return DUO_ERR_HIP;
+  }
+  e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), kk, vv, max_n, static_cast<uint16_t*>(out), s);
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  e = duo::launch_append(h->geom, sq, kk, vv, max_n, s,
+                         h->geom.rope ? duo::kAppendStreaming : duo::kAppendRetrieval | duo::kAppendStreaming);
+  if (e != hipSuccess) return DUO_ERR_HIP;
+  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += sq.n[b];
   return DUO_OK;
 }
 
@@ -196,7 +331,7 @@ const char* duo_status_string(duo_status s) {
     case DUO_ERR_INVALID_ARG: return "invalid argument";
     case DUO_ERR_UNSUPPORTED: return "unsupported configuration";
     case DUO_ERR_BUFFER_TOO_SMALL: return "device buffer too small";
-    case DUO_ERR_CAPACITY: return "sequence would exceed max_len";
+    case DUO_ERR_CAPACITY: return "sequence would exceed max_len (or the page pool is used up)";
     case DUO_ERR_HIP: return "HIP launch failed";
   }
   return "unknown status";
@@ -222,6 +357,19 @@ duo_status duo_cache_attach(const duo_config* cfg, void* dev_buf, size_t buf_byt
 
 void duo_cache_destroy(duo_cache* h) { delete h; }
 
+duo_status duo_cache_release(duo_cache* h, int32_t b, void* stream) {
+  if (h == nullptr || b < 0 || b >= h->cfg.batch) return DUO_ERR_INVALID_ARG;
+  duo::WordWrites w;
+  w.n = 1;
+  w.index[0] = (int32_t)(h->layout.lengths_offset / 4 + b);
+  w.value[0] = 0;
+  if (duo::launch_word_writes(h->buf_words, w, static_cast<hipStream_t>(stream)) != hipSuccess) return DUO_ERR_HIP;
+  for (auto it = h->seq_pages[b].rbegin(); it != h->seq_pages[b].rend(); ++it) h->free_pages.push_back(*it);
+  h->seq_pages[b].clear();
+  h->len[b] = 0;
+  return DUO_OK;
+}
+
 duo_status duo_cache_append(duo_cache* h, const void* k, const void* v, const int32_t* n_new, int32_t chunk,
                             void* stream) {
   if (h == nullptr || !aligned16(k) || !aligned16(v)) return DUO_ERR_INVALID_ARG;
@@ -229,11 +377,17 @@ duo_status duo_cache_append(duo_cache* h, const void* k, const void* v, const in
   int32_t max_n = 0;
   duo_status st = check_chunk(h, n_new, chunk, &sq, &max_n);
   if (st != DUO_OK) return st;
-  hipError_t e = duo::launch_append(h->geom, sq, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                                    chunk, max_n, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return DUO_ERR_HIP;
-  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += n_new[b];
-  return DUO_OK;
+  return append_call(h, sq, max_n, k, v, stream);
+}
+
+duo_status duo_cache_append_varlen(duo_cache* h, const void* k, const void* v, const int32_t* cu_seqlens,
+                                   void* stream) {
+  if (h == nullptr || !aligned16(k) || !aligned16(v)) return DUO_ERR_INVALID_ARG;
+  duo::Seqs sq;
+  int32_t max_n = 0;
+  duo_status st = check_varlen(h, cu_seqlens, &sq, &max_n);
+  if (st != DUO_OK) return st;
+  return append_call(h, sq, max_n, k, v, stream);
 }
 
 duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v, const int32_t* n_new,
@@ -244,27 +398,18 @@ duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v
   int32_t max_n = 0;
   duo_status st = check_chunk(h, n_new, chunk, &sq, &max_n);
   if (st != DUO_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const uint16_t* kk = static_cast<const uint16_t*>(k);
-  const uint16_t* vv = static_cast<const uint16_t*>(v);
-  // Streaming heads read ring slots that this chunk's append overwrites, so
-  // their rows are stored after the attention.  With rotary embedding the
-  // retrieval rows are stored (rotated) first and the attention reads every
-  // retrieval key from the cache; streaming heads rotate their chunk rows
-  // as they load them.
-  hipError_t e = hipSuccess;
-  if (h->geom.rope) {
-    e = duo::launch_append(h->geom, sq, kk, vv, chunk, max_n, s, duo::kAppendRetrieval);
-    if (e != hipSuccess) return DUO_ERR_HIP;
-  }
-  e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), kk, vv, chunk, max_n,
-                          static_cast<uint16_t*>(out), s);
-  if (e != hipSuccess) return DUO_ERR_HIP;
-  e = duo::launch_append(h->geom, sq, kk, vv, chunk, max_n, s,
-                         h->geom.rope ? duo::kAppendStreaming : duo::kAppendRetrieval | duo::kAppendStreaming);
-  if (e != hipSuccess) return DUO_ERR_HIP;
-  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += n_new[b];
-  return DUO_OK;
+  return prefill_call(h, sq, max_n, q, k, v, out, stream);
+}
+
+duo_status duo_prefill_varlen(duo_cache* h, const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                              void* out, void* stream) {
+  if (h == nullptr || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return DUO_ERR_INVALID_ARG;
+  duo::Seqs sq;
+  int32_t max_n = 0;
+  duo_status st = check_varlen(h, cu_seqlens, &sq, &max_n);
+  if (st != DUO_OK) return st;
+  return prefill_call(h, sq, max_n, q, k, v, out, stream);
 }
 
 duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v, void* out, void* stream) {
@@ -277,11 +422,15 @@ duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v,
   for (int b = 0; b < h->cfg.batch; ++b) {
     sq.len[b] = (int32_t)h->len[b];
     sq.n[b] = 1;
+    sq.off[b] = b;
   }
+  duo_status st = check_pages(h, sq);
+  if (st != DUO_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (take_pages(h, sq, s) != hipSuccess) return DUO_ERR_HIP;
   const duo::DecodePlan p = duo::plan_decode(h->geom, sq);
   hipError_t e = duo::launch_decode(h->geom, sq, p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                    static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out),
-                                    static_cast<hipStream_t>(stream));
+                                    static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), s);
   if (e != hipSuccess) return DUO_ERR_HIP;
   for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += 1;
   return DUO_OK;
@@ -302,6 +451,16 @@ duo_status duo_cache_layout(const duo_cache* h, duo_layout* out) {
 duo_status duo_cache_head_index(const duo_cache* h, int32_t* out) {
   if (h == nullptr || out == nullptr) return DUO_ERR_INVALID_ARG;
   for (int k = 0; k < h->cfg.num_kv_heads; ++k) out[k] = h->geom.index_of_kv[k];
+  return DUO_OK;
+}
+
+duo_status duo_cache_pages(const duo_cache* h, int32_t b, int32_t* out, int32_t cap, int32_t* n, int64_t* free_pages) {
+  if (h == nullptr || b < 0 || b >= h->cfg.batch || n == nullptr || cap < 0 || (cap > 0 && out == nullptr))
+    return DUO_ERR_INVALID_ARG;
+  const std::vector<int32_t>& pg = h->seq_pages[b];
+  *n = (int32_t)pg.size();
+  for (int32_t i = 0; i < *n && i < cap; ++i) out[i] = pg[i];
+  if (free_pages != nullptr) *free_pages = (int64_t)h->free_pages.size();
   return DUO_OK;
 }
 

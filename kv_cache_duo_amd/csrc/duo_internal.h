@@ -30,6 +30,13 @@ struct Geom {
   uint16_t* sk;               // bf16 bits [B][nS][slots][D]
   uint16_t* sv;
   int32_t* lengths;           // [B]
+  // Paged retrieval cache (paged != 0): rk / rv (rks / rvs) are pools
+  // [num_pages][nR][1 << page_shift][D]; page_table[b * max_pages + j] is
+  // the pool page of positions [j << page_shift, (j + 1) << page_shift).
+  int32_t paged;
+  int32_t page_shift;
+  int32_t max_pages;
+  const int32_t* page_table;
   float* partials;            // split-K records, see decode.hip
   uint32_t* tickets;          // [units][tickets_per_unit] split counters (zero between calls)
   int32_t tickets_per_unit;   // words: arrivals, pair claims, then one line per group of kMergeGroup splits
@@ -43,6 +50,17 @@ struct Geom {
 
 static_assert(offsetof(Geom, kv_of_unit) % 4 == 0, "kv_of_unit is read as 32-bit words");
 
+// Row index (in rows of D elements) of retrieval row p of (sequence b,
+// retrieval index idx), minus p: adding p to it gives the row, for every p
+// of the page holding `p_page` (contiguous caches: any p).  Hot loops take
+// it once per page-aligned batch of rows.
+__device__ __forceinline__ int64_t retrieval_row0(const Geom& g, int b, int idx, int p_page) {
+  if (!g.paged) return ((int64_t)b * g.nR + idx) * g.max_len;
+  const int j = p_page >> g.page_shift;
+  const int64_t page = g.page_table[(int64_t)b * g.max_pages + j];
+  return ((page * g.nR + idx) << g.page_shift) - ((int64_t)j << g.page_shift);
+}
+
 // KV head of unit u.  Read as a 32-bit word of the kernel argument: for a
 // work-group-uniform u that is a scalar load, where a byte load of the
 // argument would be a vector memory round trip.
@@ -51,11 +69,24 @@ __device__ __forceinline__ int kv_head_of_unit(const Geom& g, int u) {
   return (int)((w >> (8 * (u & 3))) & 0xffu);
 }
 
-// Per-call sequence table: tokens already stored and tokens added.
+// Per-call sequence table: tokens already stored, tokens added, and the
+// input row of sequence b's first new token (b * chunk for padded inputs,
+// cu_seqlens[b] for packed ones).
 struct Seqs {
   int32_t len[DUO_MAX_BATCH];
   int32_t n[DUO_MAX_BATCH];
+  int32_t off[DUO_MAX_BATCH];
 };
+
+// Writes of int32 words of the cache buffer (page-table entries, device
+// lengths), carried in the kernel arguments.
+constexpr int kWordWritesPerLaunch = 448;
+struct WordWrites {
+  int32_t n;
+  int32_t index[kWordWritesPerLaunch];  // word index from the buffer start
+  int32_t value[kWordWritesPerLaunch];
+};
+hipError_t launch_word_writes(int32_t* base, const WordWrites& w, hipStream_t s);
 
 // Launchers (each returns hipGetLastError() after the launch).
 hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s);
@@ -63,7 +94,7 @@ hipError_t launch_zero_words(uint32_t* p, int64_t words, hipStream_t s);
 // kinds: kAppendRetrieval | kAppendStreaming, the heads whose rows are stored
 constexpr int kAppendRetrieval = 1, kAppendStreaming = 2;
 hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v,
-                         int32_t chunk, int32_t max_n, hipStream_t s,
+                         int32_t max_n, hipStream_t s,
                          int kinds = kAppendRetrieval | kAppendStreaming);
 
 struct DecodePlan {
@@ -78,8 +109,7 @@ hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p,
                          uint16_t* out, hipStream_t s);
 
 hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, const uint16_t* kin,
-                          const uint16_t* vin, int32_t chunk, int32_t max_n, uint16_t* out,
-                          hipStream_t s);
+                          const uint16_t* vin, int32_t max_n, uint16_t* out, hipStream_t s);
 
 // Query heads of one KV group handled together by a decode work-group (at
 // most 4 with an int8 retrieval cache, whose lanes hold 16 dims each).

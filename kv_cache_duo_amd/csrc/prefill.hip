@@ -64,11 +64,10 @@ constexpr int kBN = 64;               // keys per tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: rescale when the max grows by > 2^8
 
 struct PrefillArgs {
-  const uint16_t* q;  // [B][chunk][Hq][D]
-  const uint16_t* k;  // [B][chunk][Hkv][D]
+  const uint16_t* q;  // [rows][Hq][D]: sequence b's new rows from Seqs::off[b]
+  const uint16_t* k;  // [rows][Hkv][D]
   const uint16_t* v;
-  uint16_t* out;      // [B][chunk][Hq][D]
-  int32_t chunk;
+  uint16_t* out;      // [rows][Hq][D]
   int32_t tiles_max;  // query tiles per sequence, max over sequences
   int32_t gh;         // query heads per work-group (1, 2 or 4)
   int32_t tq;         // tokens per query tile
@@ -162,7 +161,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int64_t cache_off = ((int64_t)b * nkind + idx) * unit_rows * D;
   const uint16_t* ck = (retrieval ? g.rk : g.sk) + cache_off;
   const uint16_t* cv = (retrieval ? g.rv : g.sv) + cache_off;
-  const int64_t in_base = ((int64_t)b * a.chunk * g.Hkv + kvh) * D;  // chunk row 0
+  const int64_t in_base = ((int64_t)sq.off[b] * g.Hkv + kvh) * D;  // chunk row 0
   const int in_stride = g.Hkv * D;
 
   // query positions of the work-group and of this wave's block
@@ -198,7 +197,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   bf16x8_t qreg[QC];
   {
     const bool ok = my_i <= i_hi;
-    const uint4* src = reinterpret_cast<const uint4*>(a.q + (((int64_t)b * a.chunk + (ok ? my_i : i_lo)) * g.Hq + h) * D);
+    const uint4* src = reinterpret_cast<const uint4*>(a.q + (((int64_t)sq.off[b] + (ok ? my_i : i_lo)) * g.Hq + h) * D);
     const float s = ok ? c2 : 0.f;
     if constexpr (ROPE) {
       // k-step c holds dims 16c + 8 half + 0..7 (chunk 2c + half of the
@@ -283,17 +282,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // int8 retrieval rows (Q8): codes of granule g of row r at byte
   // r*D + 8g, row scales apart; a staged tile's 16-byte granules wait in
   // kst / vst (bit j of q8rows: row j holds codes + scale in .x .y .z).
-  const uint8_t* ck8 = nullptr;
-  const uint8_t* cv8 = nullptr;
-  const float* cks = nullptr;
-  const float* cvs = nullptr;
-  if constexpr (Q8) {
-    const int64_t r8 = ((int64_t)b * g.nR + idx) * g.max_len;
-    ck8 = reinterpret_cast<const uint8_t*>(g.rk) + r8 * D;
-    cv8 = reinterpret_cast<const uint8_t*>(g.rv) + r8 * D;
-    cks = g.rks + r8;
-    cvs = g.rvs + r8;
-  }
+  // (the retrieval pointers are set per tile: a paged cache keeps a tile's
+  // 64 rows in one page)
   // ROPE: a staged streaming tile's rows wait in kst / vst as bf16 granules
   // (bit j of q8rows: row j is a chunk row whose K is turned in store_tile).
   u32x4_t kst[(Q8 || ROPE) ? NJ : 1], vst[(Q8 || ROPE) ? NJ : 1];
@@ -302,13 +292,22 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   auto load_tile = [&](int tile, int buf_off) __attribute__((always_inline)) -> bool {  // true: staged, store_tile to follow
     const int k0 = tile * kBN;
     const int dst = buf_off + wave * 1024;
+    // retrieval rows of this tile: row r at (row0 + r) * D of the pool
+    const uint16_t* ckr = ck;
+    const uint16_t* cvr = cv;
+    int64_t row0 = 0;
+    if (retrieval) {
+      row0 = retrieval_row0(g, b, idx, k0);
+      ckr = g.rk + row0 * D;
+      cvr = g.rv + row0 * D;
+    }
     if constexpr (ROPE) {
       if (retrieval) {
         // every key row is in the cache (this chunk's rows were stored,
         // rotated, before the kernel); rows past qmax read row 0 instead
         if (k0 + kBN - 1 <= qmax) {
-          const uint16_t* kb = ck + (int64_t)k0 * D + koff_c;
-          const uint16_t* vb = cv + (int64_t)k0 * D + voff_c;
+          const uint16_t* kb = ckr + (int64_t)k0 * D + koff_c;
+          const uint16_t* vb = cvr + (int64_t)k0 * D + voff_c;
 #pragma unroll
           for (int j = 0; j < NJ; ++j) global_to_lds16(kb + j * ROWS_J * D, dst + j * kWaves * 1024);
 #pragma unroll
@@ -317,9 +316,9 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int kp = k0 + r0 + j * ROWS_J;
-            const int64_t row = kp <= qmax ? (int64_t)kp : 0;
-            global_to_lds16(ck + row * D + gK * 8, dst + j * kWaves * 1024);
-            global_to_lds16(cv + row * D + gV * 8, dst + LD::TILE + j * kWaves * 1024);
+            const int64_t row = kp <= qmax ? (int64_t)kp : (int64_t)k0;  // k0 <= qmax: same page
+            global_to_lds16(ckr + row * D + gK * 8, dst + j * kWaves * 1024);
+            global_to_lds16(cvr + row * D + gV * 8, dst + LD::TILE + j * kWaves * 1024);
           }
         }
         return false;
@@ -347,6 +346,10 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     }
     if constexpr (Q8) {
       if (retrieval && k0 < L) {
+        const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + row0 * D;
+        const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + row0 * D;
+        const float* cks = g.rks + row0;
+        const float* cvs = g.rvs + row0;
         q8rows = 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
@@ -373,8 +376,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     const bool all_cache = retrieval && k0 + kBN - 1 < L;  // every row cached
     if (all_in || all_cache) {
       const int64_t stride = all_in ? in_stride : D;
-      const uint16_t* kb = all_in ? a.k + in_base + (int64_t)(k0 - L) * in_stride + koff_in : ck + (int64_t)k0 * D + koff_c;
-      const uint16_t* vb = all_in ? a.v + in_base + (int64_t)(k0 - L) * in_stride + voff_in : cv + (int64_t)k0 * D + voff_c;
+      const uint16_t* kb = all_in ? a.k + in_base + (int64_t)(k0 - L) * in_stride + koff_in : ckr + (int64_t)k0 * D + koff_c;
+      const uint16_t* vb = all_in ? a.v + in_base + (int64_t)(k0 - L) * in_stride + voff_in : cvr + (int64_t)k0 * D + voff_c;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) global_to_lds16(kb + j * ROWS_J * stride, dst + j * kWaves * 1024);
 #pragma unroll
@@ -386,8 +389,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       int64_t off;
       bool from_cache;
       row_src(k0 + r0 + j * ROWS_J, off, from_cache);
-      global_to_lds16((from_cache ? ck : a.k) + off + gK * 8, dst + j * kWaves * 1024);
-      global_to_lds16((from_cache ? cv : a.v) + off + gV * 8, dst + LD::TILE + j * kWaves * 1024);
+      global_to_lds16((from_cache ? ckr : a.k) + off + gK * 8, dst + j * kWaves * 1024);
+      global_to_lds16((from_cache ? cvr : a.v) + off + gV * 8, dst + LD::TILE + j * kWaves * 1024);
     }
     return false;
   };
@@ -553,7 +556,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (my_i <= i_hi) {
     const float inv = 1.0f / l_tot;
-    uint16_t* dst = a.out + (((int64_t)b * a.chunk + my_i) * g.Hq + h) * D;
+    uint16_t* dst = a.out + (((int64_t)sq.off[b] + my_i) * g.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -593,14 +596,13 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
 }  // namespace
 
 hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, const uint16_t* kin,
-                          const uint16_t* vin, int32_t chunk, int32_t max_n, uint16_t* out, hipStream_t s) {
+                          const uint16_t* vin, int32_t max_n, uint16_t* out, hipStream_t s) {
   if (max_n <= 0) return hipSuccess;
   PrefillArgs a;
   a.q = qin;
   a.k = kin;
   a.v = vin;
   a.out = out;
-  a.chunk = chunk;
   a.gh = heads_per_group(g.G);
   a.n_hc = g.G / a.gh;
   // int8 retrieval rows are only read from a stored prefix

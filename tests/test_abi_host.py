@@ -75,6 +75,10 @@ def test_required_bytes_for_workloads(name):
     (dict(rope_base=float("inf")), duo.DUO_ERR_INVALID_ARG),
     (dict(rope_base=10000.0, rope_style=2), duo.DUO_ERR_INVALID_ARG),
     (dict(rope_base=10000.0, kv_format=1), duo.DUO_ERR_UNSUPPORTED),  # rotary + int8 cache
+    (dict(page_tokens=256, num_pages=8), duo.DUO_ERR_INVALID_ARG),     # pages below 512 positions
+    (dict(page_tokens=1000, num_pages=8), duo.DUO_ERR_INVALID_ARG),    # not a power of two
+    (dict(page_tokens=131072, num_pages=8), duo.DUO_ERR_INVALID_ARG),  # above 65536
+    (dict(page_tokens=512, num_pages=0), duo.DUO_ERR_INVALID_ARG),     # empty pool
 ])
 def test_invalid_configs(kw, status):
     with pytest.raises(duo.DuoError) as e:
@@ -214,3 +218,75 @@ def test_rope_config_accepted_and_layout_unchanged():
     # the style is not read without a base
     cfg = duo.Config(2, 8, 4, 128, 1000, 4, 64, [1, 0, 1, 0], rope_base=0.0, rope_style=7)
     assert duo.required_bytes(cfg) == duo.required_bytes(base)
+
+
+def test_paged_layout_sizes_the_pool_not_the_batch():
+    """A paged cache holds num_pages pages of every retrieval head instead of
+    B * max_len rows: 32 sequences of up to 65536 positions in a pool of 100
+    pages of 1024 positions."""
+    pg = _cfg(batch=32, max_len=65536, page_tokens=1024, num_pages=100)
+    flat = _cfg(batch=32, max_len=65536)
+    c = _attach(pg)
+    lay = c.layout()
+    row = 2 * pg.head_dim
+    assert (lay.page_tokens, lay.num_pages, lay.max_pages_per_seq) == (1024, 100, 64)
+    assert lay.page_table_offset > lay.lengths_offset and lay.page_table_offset % 256 == 0
+    assert lay.rv_offset - lay.rk_offset == 100 * 2 * 1024 * row  # pages * nR * P * row
+    assert duo.required_bytes(pg) < duo.required_bytes(flat) / 15
+    flay = _attach(flat).layout()
+    assert flay.page_table_offset == -1 and flay.page_tokens == 0
+    # int8 pools: codes and scales per page
+    q8 = _cfg(batch=32, max_len=65536, page_tokens=1024, num_pages=100, kv_format=duo.DUO_KV_INT8)
+    lay8 = _attach(q8).layout()
+    assert lay8.rv_offset - lay8.rk_offset == 100 * 2 * 1024 * pg.head_dim
+    assert lay8.rvs_offset - lay8.rks_offset == 100 * 2 * 1024 * 4
+
+
+def test_paged_attach_needs_empty_sequences():
+    cfg = _cfg(page_tokens=512, num_pages=4)
+    with pytest.raises(duo.DuoError) as e:
+        _attach(cfg, [0, 3])
+    assert e.value.status == duo.DUO_ERR_INVALID_ARG
+    assert _attach(cfg).pages(0) == ([], 4)
+
+
+def test_paged_pool_exhaustion_is_checked_before_any_work():
+    """Calls that would need more pages than the pool has free fail with
+    CAPACITY and change nothing (no device work is enqueued)."""
+    lib = duo.load_library()
+    cfg = _cfg(max_len=4096, page_tokens=512, num_pages=3)
+    c = _attach(cfg)
+    A = ctypes.c_void_p(FAKE)
+    # 2 sequences x 1000 tokens need 2 + 2 pages > 3
+    n = (ctypes.c_int32 * 2)(1000, 1000)
+    assert lib.duo_prefill(c.handle, A, A, A, n, 1000, A, None) == duo.DUO_ERR_CAPACITY
+    assert lib.duo_cache_append(c.handle, A, A, n, 1000, None) == duo.DUO_ERR_CAPACITY
+    cu = (ctypes.c_int32 * 3)(0, 1000, 2000)
+    assert lib.duo_prefill_varlen(c.handle, A, A, A, cu, A, None) == duo.DUO_ERR_CAPACITY
+    assert lib.duo_cache_append_varlen(c.handle, A, A, cu, None) == duo.DUO_ERR_CAPACITY
+    assert c.lengths() == [0, 0] and c.pages(0) == ([], 3) and c.pages(1) == ([], 3)
+    # decode needs one page per sequence: a pool of 1 is too small for 2
+    one = _attach(_cfg(max_len=4096, page_tokens=512, num_pages=1))
+    assert lib.duo_decode(one.handle, A, A, A, A, None) == duo.DUO_ERR_CAPACITY
+    assert one.pages(0) == ([], 1)
+
+
+def test_varlen_validation():
+    lib = duo.load_library()
+    c = _attach(_cfg())
+    A = ctypes.c_void_p(FAKE)
+    for cu in [(1, 2, 3), (0, 5, 3), (0, 600, 1601)]:  # cu[0] != 0, decreasing, over max_len
+        arr = (ctypes.c_int32 * 3)(*cu)
+        st = lib.duo_prefill_varlen(c.handle, A, A, A, arr, A, None)
+        assert st in (duo.DUO_ERR_INVALID_ARG, duo.DUO_ERR_CAPACITY)
+    assert lib.duo_prefill_varlen(c.handle, A, A, A, None, A, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_cache_append_varlen(c.handle, A, None, (ctypes.c_int32 * 3)(0, 1, 2), None) == duo.DUO_ERR_INVALID_ARG
+    assert c.lengths() == [0, 0]
+
+
+def test_release_checks_its_arguments():
+    lib = duo.load_library()
+    c = _attach(_cfg())
+    assert lib.duo_cache_release(None, 0, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_cache_release(c.handle, 2, None) == duo.DUO_ERR_INVALID_ARG
+    assert lib.duo_cache_release(c.handle, -1, None) == duo.DUO_ERR_INVALID_ARG
