@@ -18,6 +18,7 @@ Inputs are resident in HBM before the timed region.  Reported:
              prefill; its algorithmic bytes count D + 4 per stored K or V row
   rope       the same step with rotary position embedding applied inside the
              library (same algorithmic counts; rotation work is overhead)
+  paged      the same step over a paged retrieval cache (1024-position pages)
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode work
 Algorithmic counts: each K/V byte once per (sequence, KV head) plus q, out
 and the appended token; flops = 4*D per allowed (query, key) pair per query
@@ -224,11 +225,13 @@ def main():
 
     def variant_phases(cfgs_v, what):
         """Prefill and decode phase times (ms, summed over the timed steps)
-        of the same step on caches of another configuration; the buffers of
-        the main run are reused."""
+        of the same step on caches of another configuration (the buffers of
+        the main run are reused where they are large enough)."""
+        bv = [bufs[l] if duo.required_bytes(cfgs_v[l]) <= bufs[l].numel() else
+              torch.empty(duo.required_bytes(cfgs_v[l]), dtype=torch.uint8, device=dev) for l in range(nl)]
         pre_v = dec_v = 0.0
         for it in range(args.warmup + args.steps):
-            cv = [duo.duo_cache_init(cfgs_v[l], bufs[l]) for l in range(nl)]
+            cv = [duo.duo_cache_init(cfgs_v[l], bv[l]) for l in range(nl)]
             hv = [c.handle for c in cv]
             ph[0].record(stream)
             for l in range(nl):
@@ -251,6 +254,11 @@ def main():
     _, dec8_ms = variant_phases([dataclasses.replace(c, kv_format=duo.DUO_KV_INT8) for c in cfgs], "int8")
     pre_r_ms, dec_r_ms = variant_phases(
         [dataclasses.replace(c, rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF) for c in cfgs], "rope")
+    # and with a paged retrieval cache (pages of 1024 positions, a pool just
+    # large enough)
+    page = 1024
+    pre_p_ms, dec_p_ms = variant_phases(
+        [dataclasses.replace(c, page_tokens=page, num_pages=(t_all + page - 1) // page) for c in cfgs], "paged")
     bytes8_step = sum(decode_bytes_int8(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
     dec8_gbs = bytes8_step * args.steps / (dec8_ms * 1e-3) / 1e9
 
@@ -289,6 +297,11 @@ def main():
                  "decode_time_vs_plain": round(dec_r_ms / dec_ms, 4),
                  "prefill_time_vs_plain": round(pre_r_ms / pre_ms, 4),
                  "embedding": "rotary, base 10000, pairs (i, i + D/2), applied to q and k inside the library"},
+        "paged": {"decode_gbs": round(bytes_step * args.steps / (dec_p_ms * 1e-3) / 1e9, 1),
+                  "prefill_tflops": round(flops_step * args.steps / (pre_p_ms * 1e-3) / 1e12, 1),
+                  "decode_time_vs_contiguous": round(dec_p_ms / dec_ms, 4),
+                  "prefill_time_vs_contiguous": round(pre_p_ms / pre_ms, 4),
+                  "page_tokens": page},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_kernel (one launch per decode call)",
