@@ -64,12 +64,13 @@ def measured_traffic():
 
 def measured_ceilings(decode_mib: int):
     """Streaming-read (launches of the decode call's size over 8 buffers in
-    turn, and 4 GiB) and bf16 MFMA-loop ceilings from kv_cache_duo_amd/ceiling,
-    run as a child."""
+    turn, and 4 GiB) and bf16 MFMA-loop ceilings (constant operands, and
+    changing random operands: the sustained MFMA rate is power-limited and
+    depends on the data) from kv_cache_duo_amd/ceiling, run as a child."""
     import subprocess
     exe = os.path.join(ROOT, "kv_cache_duo_amd", "ceiling")
     out = {}
-    for args in (["stream_read_rotating", str(decode_mib), "8"], ["stream_read", "4096"], ["mfma"]):
+    for args in (["stream_read_rotating", str(decode_mib), "8"], ["stream_read", "4096"], ["mfma"], ["mfma_random"]):
         r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=120)
         if r.returncode != 0:
             raise RuntimeError(f"{exe} {' '.join(args)} failed: {r.stderr}")

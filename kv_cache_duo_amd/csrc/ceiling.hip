@@ -3,6 +3,7 @@
 //   ceiling stream_read <MiB>  -- 16-byte streaming reads of a buffer (HBM)
 //   ceiling stream_read_rotating <MiB> <n> -- the same over n buffers in turn
 //   ceiling mfma               -- back-to-back v_mfma_f32_32x32x16_bf16
+//   ceiling mfma_random        -- the same with changing pseudo-random operands
 // Standalone executable (not part of the C ABI); prints one JSON line.
 #include <hip/hip_runtime.h>
 
@@ -49,6 +50,49 @@ __global__ __launch_bounds__(256) void mfma_loop(float* out, int iters) {
     c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
     c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
     c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  if (s == 1234.5f) out[blockIdx.x] = s;
+}
+
+// The same with operands that change from one MFMA to the next: 4 A and 4 B
+// fragments of pseudo-random bf16 values (uniform in [-2, 2), as attention
+// inputs of unit variance), paired differently by every MFMA of a round.
+// The MFMA rate under sustained load is power-limited, and constant operands
+// switch far fewer bits than real data.
+__device__ __forceinline__ float hash_unit(unsigned x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return (float)(x >> 8) * (4.0f / 16777216.0f) - 2.0f;
+}
+__global__ __launch_bounds__(256) void mfma_loop_random(float* out, int iters) {
+  bf16x8 a[4], b[4];
+  const unsigned seed = (blockIdx.x * 256u + threadIdx.x) * 64u;
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[f][j] = (__bf16)hash_unit(seed + f * 8 + j);
+      b[f][j] = (__bf16)hash_unit(seed + 32 + f * 8 + j);
+    }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; i += 4) {
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[2], c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], b[3], c3, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[2], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[3], c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], b[0], c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], c3, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], b[1], c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[3], c3, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[3], b[3], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], c1, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], c2, 0, 0, 0);
+    c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[2], c3, 0, 0, 0);
   }
   float s = 0.f;
   for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
@@ -123,7 +167,7 @@ int run_stream_read_rotating(size_t mib, int nbuf) {
   return 0;
 }
 
-int run_mfma() {
+int run_mfma(bool random) {
   int dev = 0, cus = 0;
   if (!ok(hipGetDevice(&dev), "device") ||
       !ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "attr"))
@@ -134,16 +178,18 @@ int run_mfma() {
   if (!ok(hipMalloc(&out, blocks * 4), "hipMalloc")) return 1;
   hipEvent_t a, b;
   if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return 1;
-  hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(256), 0, 0, out, iters);
+  auto kernel = random ? mfma_loop_random : mfma_loop;
+  hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, 0, out, iters);
   (void)hipEventRecord(a, 0);
   const int reps = 5;
-  for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(mfma_loop, dim3(blocks), dim3(256), 0, 0, out, iters);
+  for (int r = 0; r < reps; ++r) hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, 0, out, iters);
   (void)hipEventRecord(b, 0);
   if (!ok(hipEventSynchronize(b), "sync")) return 1;
   float ms = 0.f;
   (void)hipEventElapsedTime(&ms, a, b);
   const double flop = (double)reps * blocks * 4 /*waves*/ * iters * 4 /*mfma*/ * 32768.0;
-  printf("{\"ceiling\": \"mfma_bf16_32x32x16\", \"cus\": %d, \"tflops\": %.1f}\n", cus, flop / (ms * 1e-3) / 1e12);
+  printf("{\"ceiling\": \"%s\", \"cus\": %d, \"tflops\": %.1f}\n",
+         random ? "mfma_bf16_32x32x16_random_operands" : "mfma_bf16_32x32x16", cus, flop / (ms * 1e-3) / 1e12);
   return 0;
 }
 
@@ -154,7 +200,9 @@ int main(int argc, char** argv) {
     return run_stream_read(argc >= 3 ? (size_t)std::atoll(argv[2]) : 4096);
   if (argc >= 2 && std::strcmp(argv[1], "stream_read_rotating") == 0)
     return run_stream_read_rotating(argc >= 3 ? (size_t)std::atoll(argv[2]) : 132, argc >= 4 ? std::atoi(argv[3]) : 8);
-  if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma();
-  fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling stream_read_rotating <MiB> <buffers> | ceiling mfma\n");
+  if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma(false);
+  if (argc >= 2 && std::strcmp(argv[1], "mfma_random") == 0) return run_mfma(true);
+  fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling stream_read_rotating <MiB> <buffers> | ceiling mfma"
+                  " | ceiling mfma_random\n");
   return 2;
 }

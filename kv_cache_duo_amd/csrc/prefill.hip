@@ -60,6 +60,7 @@ typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 constexpr int kBN = 64;               // keys per tile
 constexpr float kRescaleSlack = 8.f;  // log2 units: rescale when the max grows by > 2^8
 
@@ -91,28 +92,24 @@ template <int D>
 struct Lds {
   static constexpr int ROW = D * 2;       // bytes per K or V row
   static constexpr int TILE = kBN * ROW;  // one K or V tile
-  static constexpr int BUF = 2 * TILE;    // K tile, then V tile
-  static constexpr int TOTAL = 2 * BUF;   // double buffered
 };
-
-// Dynamic LDS of the prefill kernel (two K/V tile buffers).
-extern __shared__ __attribute__((aligned(16))) char prefill_smem[];
 
 // The helpers below wrap target builtins that take LDS pointers; they stay
 // out of the kernel template, whose host-side stub is otherwise not emitted.
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave
-// writes bytes [lds_off + 16 l, lds_off + 16 l + 16); lds_off is wave-uniform.
-__device__ __forceinline__ void global_to_lds16(const void* src, int lds_off) {
-  __builtin_amdgcn_global_load_lds(src, prefill_smem + lds_off, 16, 0, 0);
+// writes bytes [lds + 16 l, lds + 16 l + 16); lds is wave-uniform.
+__device__ __forceinline__ void global_to_lds16(const void* src, char* lds) {
+  typedef __attribute__((address_space(3))) void lds_void_t;
+  __builtin_amdgcn_global_load_lds(src, (lds_void_t*)lds, 16, 0, 0);
 }
 
 // ds_read_b64_tr_b16: every lane names 8 bytes (four 16-bit elements) of
 // LDS; inside each group of 16 lanes, lane i receives as element j the
 // element (i mod 4) of the 8 bytes named by lane 4 j + i / 4 of its group.
-__device__ __forceinline__ uint2 lds_read_tr16(int lds_off) {
+__device__ __forceinline__ uint2 lds_read_tr16(const char* lds) {
   typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
-  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(prefill_smem + lds_off));
+  const i16x4_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)lds);
   return __builtin_bit_cast(uint2, r);
 }
 
@@ -128,6 +125,14 @@ template <int D, bool Q8, bool ROPE>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   static_assert(!(Q8 && ROPE), "rotary embedding with an int8 cache is not supported");
+  // The K and V tiles of the two pipeline stages are four distinct LDS
+  // objects: the compiler then knows that the next tile's direct-to-LDS
+  // loads cannot alias the transposing reads of the current one, and does
+  // not wait for those loads before the P V products.
+  __shared__ __attribute__((aligned(16))) char lds_k0[Lds<D>::TILE];
+  __shared__ __attribute__((aligned(16))) char lds_v0[Lds<D>::TILE];
+  __shared__ __attribute__((aligned(16))) char lds_k1[Lds<D>::TILE];
+  __shared__ __attribute__((aligned(16))) char lds_v1[Lds<D>::TILE];
   using LD = Lds<D>;
   constexpr int CH = D / 8;                 // 16-byte granules per row
   constexpr int RPC = 64 / CH;              // rows per 1 KB wave load (4 or 8)
@@ -141,14 +146,26 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int col = lane & 31;   // query row of the 32-row block held by this lane
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group
 
-  // ---- work item: t-major (longest tiles first), unit-minor
+  // ---- work item: longest query tiles first.  Work-groups go to the 8 XCDs
+  // round-robin (blockIdx mod 8); when the units (sequence, KV head, head
+  // chunk) of a kind split evenly over the XCDs, every unit stays on one XCD
+  // and that XCD runs its query tiles in order, so the resident work-groups
+  // of a unit stream the same K/V tiles nearly together and share them in
+  // the XCD's L2.  Otherwise: t-major, unit-minor.
   int id = blockIdx.x;
   const bool retrieval = id < a.items_r;
   if (!retrieval) id -= a.items_r;
   const int nkind = retrieval ? g.nR : g.nS;
   const int per_t = g.B * nkind * a.n_hc;
-  const int t = a.tiles_max - 1 - id / per_t;
-  int rest = id % per_t;
+  int t, rest;
+  if (per_t % kXcds == 0 && (retrieval || a.items_r % kXcds == 0)) {
+    const int x = id % kXcds, k = id / kXcds, per_x = per_t / kXcds;
+    t = a.tiles_max - 1 - k / per_x;
+    rest = x + kXcds * (k % per_x);
+  } else {
+    t = a.tiles_max - 1 - id / per_t;
+    rest = id % per_t;
+  }
   const int hc = rest % a.n_hc;
   rest /= a.n_hc;
   const int idx = rest % nkind;
@@ -289,9 +306,10 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   u32x4_t kst[(Q8 || ROPE) ? NJ : 1], vst[(Q8 || ROPE) ? NJ : 1];
   uint32_t q8rows = 0;
   int st_k0 = 0;  // first key of the staged tile
-  auto load_tile = [&](int tile, int buf_off) __attribute__((always_inline)) -> bool {  // true: staged, store_tile to follow
+  auto load_tile = [&](int tile, char* kbuf, char* vbuf) __attribute__((always_inline)) -> bool {  // true: staged, store_tile to follow
     const int k0 = tile * kBN;
-    const int dst = buf_off + wave * 1024;
+    char* dst = kbuf + wave * 1024;   // K tile, this wave's 1 KB chunks
+    char* vdst = vbuf + wave * 1024;  // V tile
     // retrieval rows of this tile: row r at (row0 + r) * D of the pool
     const uint16_t* ckr = ck;
     const uint16_t* cvr = cv;
@@ -311,14 +329,14 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) global_to_lds16(kb + j * ROWS_J * D, dst + j * kWaves * 1024);
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) global_to_lds16(vb + j * ROWS_J * D, dst + LD::TILE + j * kWaves * 1024);
+          for (int j = 0; j < NJ; ++j) global_to_lds16(vb + j * ROWS_J * D, vdst + j * kWaves * 1024);
         } else {
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int kp = k0 + r0 + j * ROWS_J;
             const int64_t row = kp <= qmax ? (int64_t)kp : (int64_t)k0;  // k0 <= qmax: same page
             global_to_lds16(ckr + row * D + gK * 8, dst + j * kWaves * 1024);
-            global_to_lds16(cvr + row * D + gV * 8, dst + LD::TILE + j * kWaves * 1024);
+            global_to_lds16(cvr + row * D + gV * 8, vdst + j * kWaves * 1024);
           }
         }
         return false;
@@ -381,7 +399,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
 #pragma unroll
       for (int j = 0; j < NJ; ++j) global_to_lds16(kb + j * ROWS_J * stride, dst + j * kWaves * 1024);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) global_to_lds16(vb + j * ROWS_J * stride, dst + LD::TILE + j * kWaves * 1024);
+      for (int j = 0; j < NJ; ++j) global_to_lds16(vb + j * ROWS_J * stride, vdst + j * kWaves * 1024);
       return false;
     }
 #pragma unroll
@@ -390,12 +408,12 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       bool from_cache;
       row_src(k0 + r0 + j * ROWS_J, off, from_cache);
       global_to_lds16((from_cache ? ckr : a.k) + off + gK * 8, dst + j * kWaves * 1024);
-      global_to_lds16((from_cache ? cvr : a.v) + off + gV * 8, dst + LD::TILE + j * kWaves * 1024);
+      global_to_lds16((from_cache ? cvr : a.v) + off + gV * 8, vdst + j * kWaves * 1024);
     }
     return false;
   };
   // Write a staged tile: int8 granules become code * scale rounded to bf16.
-  auto store_tile = [&](int buf_off) __attribute__((always_inline)) {
+  auto store_tile = [&](char* kbuf, char* vbuf) __attribute__((always_inline)) {
     auto granule = [&](const u32x4_t& x, bool q8) __attribute__((always_inline)) -> u32x4_t {
       if (!q8) return x;
       const float sc = __uint_as_float(x.z);
@@ -407,7 +425,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       }
       return u32x4_t{w[0], w[1], w[2], w[3]};
     };
-    char* dst = prefill_smem + buf_off + wave * 1024 + lane * 16;
+    char* dst = kbuf + wave * 1024 + lane * 16;
+    char* vdst = vbuf + wave * 1024 + lane * 16;
     if constexpr (ROPE) {
       // chunk K rows turned to their positions (every lane takes part: the
       // half-split pairs exchange values across lanes)
@@ -419,7 +438,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
         const uint4 r = rope_apply8<CH>(x, cs, sn, g.rope_half, gK);
         const u32x4_t kr = ((q8rows >> j) & 1u) ? u32x4_t{r.x, r.y, r.z, r.w} : kst[j];
         *reinterpret_cast<u32x4_t*>(dst + j * kWaves * 1024) = kr;
-        *reinterpret_cast<u32x4_t*>(dst + LD::TILE + j * kWaves * 1024) = vst[j];
+        *reinterpret_cast<u32x4_t*>(vdst + j * kWaves * 1024) = vst[j];
       }
       return;
     }
@@ -427,7 +446,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     for (int j = 0; j < NJ; ++j) {
       const bool q8 = (q8rows >> j) & 1u;
       *reinterpret_cast<u32x4_t*>(dst + j * kWaves * 1024) = granule(kst[j], q8);
-      *reinterpret_cast<u32x4_t*>(dst + LD::TILE + j * kWaves * 1024) = granule(vst[j], q8);
+      *reinterpret_cast<u32x4_t*>(vdst + j * kWaves * 1024) = granule(vst[j], q8);
     }
   };
 
@@ -461,7 +480,11 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   auto compute_tile = [&](int kt, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
     const int k0 = tile_of(kt) * kBN;
-    const bool staged = kt + 1 < ntiles && load_tile(tile_of(kt + 1), (cur ^ 1) * LD::BUF);
+    char* const kcur = cur ? lds_k1 : lds_k0;
+    char* const vcur = cur ? lds_v1 : lds_v0;
+    char* const knext = cur ? lds_k0 : lds_k1;
+    char* const vnext = cur ? lds_v0 : lds_v1;
+    const bool staged = kt + 1 < ntiles && load_tile(tile_of(kt + 1), knext, vnext);
 
     // wave-uniform: can the block see a key of this tile, and does any key
     // need a mask (causal diagonal, or outside the streaming band)
@@ -469,13 +492,12 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     if (!retrieval && k0 >= g.S && k0 + kBN - 1 < blo - g.W + 1) live = false;
     const bool need_mask = k0 + kBN - 1 > blo || (!retrieval && k0 + kBN - 1 >= g.S && k0 < bhi - g.W + 1);
     if (live) {
-      constexpr int kb = cur * LD::BUF, vb = kb + LD::TILE;
       f32x16_t sacc[2];
 #pragma unroll
       for (int c = 0; c < QC; ++c)
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
-          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(prefill_smem + kb + k_addr(kb2, c));
+          const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kcur + k_addr(kb2, c));
           sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c], c == 0 ? negm : sacc[kb2], 0, 0, 0);
         }
       // masks: causal on the diagonal, band for streaming heads (branch-free)
@@ -530,21 +552,21 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           const bf16x8_t pb = __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const uint2 lo = lds_read_tr16(vb + v_addr(kb2 * 32 + st * 16, 0, db));
-            const uint2 hi = lds_read_tr16(vb + v_addr(kb2 * 32 + st * 16, 1, db));
+            const uint2 lo = lds_read_tr16(vcur + v_addr(kb2 * 32 + st * 16, 0, db));
+            const uint2 hi = lds_read_tr16(vcur + v_addr(kb2 * 32 + st * 16, 1, db));
             const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, oacc[db], 0, 0, 0);
           }
         }
     }
     if constexpr (Q8 || ROPE) {
-      if (staged) store_tile((cur ^ 1) * LD::BUF);
+      if (staged) store_tile(knext, vnext);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next tile
     __syncthreads();
   };
 
-  if (load_tile(tile_of(0), 0)) store_tile(0);
+  if (load_tile(tile_of(0), lds_k0, lds_v0)) store_tile(lds_k0, lds_v0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int kt = 0; kt < ntiles; kt += 2) {
@@ -577,19 +599,12 @@ int heads_per_group(int G) {
 
 template <int D, bool Q8, bool ROPE>
 hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, Q8, ROPE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Lds<D>::TOTAL);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   a.tq = kWaves * 32 / a.gh;
   a.tiles_max = (max_n + a.tq - 1) / a.tq;
   a.items_r = a.tiles_max * g.B * g.nR * a.n_hc;
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * g.B * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE>), dim3((unsigned)blocks), dim3(kThreads), Lds<D>::TOTAL, s, g, q, a);
+  hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE>), dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
   return hipGetLastError();
 }
 
