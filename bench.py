@@ -90,6 +90,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-steps", type=int, default=128)
     p.add_argument("--no-ceilings", action="store_true")
+    p.add_argument("--legs", default="int8,rope,paged",
+                   help="variant legs to run after the plain step (comma list of int8, rope, paged; empty for none)")
     return p.parse_args()
 
 
@@ -252,16 +254,19 @@ def main():
     # the same step with an int8 retrieval cache (DUO_KV_INT8: smaller, so
     # the bf16 buffers hold it), and with rotary position embedding applied
     # inside the library (base 10000, half-split pairs)
-    _, dec8_ms = variant_phases([dataclasses.replace(c, kv_format=duo.DUO_KV_INT8) for c in cfgs], "int8")
-    pre_r_ms, dec_r_ms = variant_phases(
-        [dataclasses.replace(c, rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF) for c in cfgs], "rope")
+    variants = {}
+    legs = [x for x in args.legs.split(",") if x]
+    if "int8" in legs:
+        variants["int8"] = variant_phases([dataclasses.replace(c, kv_format=duo.DUO_KV_INT8) for c in cfgs], "int8")
+    if "rope" in legs:
+        variants["rope"] = variant_phases(
+            [dataclasses.replace(c, rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF) for c in cfgs], "rope")
     # and with a paged retrieval cache (pages of 1024 positions, a pool just
     # large enough)
     page = 1024
-    pre_p_ms, dec_p_ms = variant_phases(
-        [dataclasses.replace(c, page_tokens=page, num_pages=(t_all + page - 1) // page) for c in cfgs], "paged")
-    bytes8_step = sum(decode_bytes_int8(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
-    dec8_gbs = bytes8_step * args.steps / (dec8_ms * 1e-3) / 1e9
+    if "paged" in legs:
+        variants["paged"] = variant_phases(
+            [dataclasses.replace(c, page_tokens=page, num_pages=(t_all + page - 1) // page) for c in cfgs], "paged")
 
     result = {
         "metric": "decode attn HBM GB/s (% of peak) + prefill TFLOP/s (% MFMA peak), 1 MI355X",
@@ -288,21 +293,6 @@ def main():
                     "frac_of_mfma_peak": round(pre_tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                     "phase_ms_per_step": round(pre_ms / args.steps, 3),
                     "flops_per_step": flops_step},
-        "decode_int8": {"gbs": round(dec8_gbs, 1), "frac_of_hbm_peak": round(dec8_gbs / HBM_PEAK_GBS, 4),
-                        "phase_ms_per_step": round(dec8_ms / args.steps, 3),
-                        "bytes_per_launch": bytes8_step / n_dec,
-                        "decode_time_vs_bf16": round(dec8_ms / dec_ms, 4),
-                        "cache": "retrieval K/V as int8 codes + fp32 row scales (DUO_KV_INT8)"},
-        "rope": {"decode_gbs": round(bytes_step * args.steps / (dec_r_ms * 1e-3) / 1e9, 1),
-                 "prefill_tflops": round(flops_step * args.steps / (pre_r_ms * 1e-3) / 1e12, 1),
-                 "decode_time_vs_plain": round(dec_r_ms / dec_ms, 4),
-                 "prefill_time_vs_plain": round(pre_r_ms / pre_ms, 4),
-                 "embedding": "rotary, base 10000, pairs (i, i + D/2), applied to q and k inside the library"},
-        "paged": {"decode_gbs": round(bytes_step * args.steps / (dec_p_ms * 1e-3) / 1e9, 1),
-                  "prefill_tflops": round(flops_step * args.steps / (pre_p_ms * 1e-3) / 1e12, 1),
-                  "decode_time_vs_contiguous": round(dec_p_ms / dec_ms, 4),
-                  "prefill_time_vs_contiguous": round(pre_p_ms / pre_ms, 4),
-                  "page_tokens": page},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "decode_kernel (one launch per decode call)",
@@ -315,6 +305,29 @@ def main():
                              "mean_launch_ms": round(mean_pre_launch, 4)},
         "wall_s": round(wall, 3),
     }
+    if "int8" in variants:
+        dec8_ms = variants["int8"][1]
+        bytes8_step = sum(decode_bytes_int8(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
+        dec8_gbs = bytes8_step * args.steps / (dec8_ms * 1e-3) / 1e9
+        result["decode_int8"] = {"gbs": round(dec8_gbs, 1), "frac_of_hbm_peak": round(dec8_gbs / HBM_PEAK_GBS, 4),
+                                 "phase_ms_per_step": round(dec8_ms / args.steps, 3),
+                                 "bytes_per_launch": bytes8_step / n_dec,
+                                 "decode_time_vs_bf16": round(dec8_ms / dec_ms, 4),
+                                 "cache": "retrieval K/V as int8 codes + fp32 row scales (DUO_KV_INT8)"}
+    if "rope" in variants:
+        pre_r_ms, dec_r_ms = variants["rope"]
+        result["rope"] = {"decode_gbs": round(bytes_step * args.steps / (dec_r_ms * 1e-3) / 1e9, 1),
+                          "prefill_tflops": round(flops_step * args.steps / (pre_r_ms * 1e-3) / 1e12, 1),
+                          "decode_time_vs_plain": round(dec_r_ms / dec_ms, 4),
+                          "prefill_time_vs_plain": round(pre_r_ms / pre_ms, 4),
+                          "embedding": "rotary, base 10000, pairs (i, i + D/2), applied to q and k inside the library"}
+    if "paged" in variants:
+        pre_p_ms, dec_p_ms = variants["paged"]
+        result["paged"] = {"decode_gbs": round(bytes_step * args.steps / (dec_p_ms * 1e-3) / 1e9, 1),
+                           "prefill_tflops": round(flops_step * args.steps / (pre_p_ms * 1e-3) / 1e12, 1),
+                           "decode_time_vs_contiguous": round(dec_p_ms / dec_ms, 4),
+                           "prefill_time_vs_contiguous": round(pre_p_ms / pre_ms, 4),
+                           "page_tokens": page}
     if not args.no_ceilings:
         result["measured_ceilings"] = measured_ceilings(max(1, int(round(bytes_per_launch / 2**20))))
     if not args.no_cpu_baseline:

@@ -199,8 +199,9 @@ duo_status duo_cache_append(duo_cache* h, const void* k, const void* v,
  * back, sequence b's in rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of
  * k, v: bf16 [cu_seqlens[B]][Hkv][D] (q, out: [cu_seqlens[B]][Hq][D]).
  * cu_seqlens: HOST int32 [B+1], cu_seqlens[0] = 0, nondecreasing; a
- * sequence with no rows is skipped.  Otherwise as duo_cache_append and
- * duo_prefill (INVALID_ARG also for a bad cu_seqlens). */
+ * sequence with no rows is skipped; a call with no rows at all does
+ * nothing and accepts null tensor pointers.  Otherwise as duo_cache_append
+ * and duo_prefill (INVALID_ARG also for a bad cu_seqlens). */
 duo_status duo_cache_append_varlen(duo_cache* h, const void* k, const void* v,
                                    const int32_t* cu_seqlens, void* stream);
 duo_status duo_prefill_varlen(duo_cache* h, const void* q, const void* k, const void* v,

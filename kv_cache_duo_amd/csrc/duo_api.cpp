@@ -382,11 +382,13 @@ duo_status duo_cache_append(duo_cache* h, const void* k, const void* v, const in
 
 duo_status duo_cache_append_varlen(duo_cache* h, const void* k, const void* v, const int32_t* cu_seqlens,
                                    void* stream) {
-  if (h == nullptr || !aligned16(k) || !aligned16(v)) return DUO_ERR_INVALID_ARG;
+  if (h == nullptr) return DUO_ERR_INVALID_ARG;
   duo::Seqs sq;
   int32_t max_n = 0;
   duo_status st = check_varlen(h, cu_seqlens, &sq, &max_n);
   if (st != DUO_OK) return st;
+  if (max_n == 0) return DUO_OK;  // no rows: nothing to do (the pointers may be null)
+  if (!aligned16(k) || !aligned16(v)) return DUO_ERR_INVALID_ARG;
   return append_call(h, sq, max_n, k, v, stream);
 }
 
@@ -403,12 +405,13 @@ duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v
 
 duo_status duo_prefill_varlen(duo_cache* h, const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                               void* out, void* stream) {
-  if (h == nullptr || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return DUO_ERR_INVALID_ARG;
+  if (h == nullptr) return DUO_ERR_INVALID_ARG;
   duo::Seqs sq;
   int32_t max_n = 0;
   duo_status st = check_varlen(h, cu_seqlens, &sq, &max_n);
   if (st != DUO_OK) return st;
+  if (max_n == 0) return DUO_OK;  // no rows: nothing to do (the pointers may be null)
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return DUO_ERR_INVALID_ARG;
   return prefill_call(h, sq, max_n, q, k, v, out, stream);
 }
 

@@ -281,6 +281,10 @@ def test_varlen_validation():
         assert st in (duo.DUO_ERR_INVALID_ARG, duo.DUO_ERR_CAPACITY)
     assert lib.duo_prefill_varlen(c.handle, A, A, A, None, A, None) == duo.DUO_ERR_INVALID_ARG
     assert lib.duo_cache_append_varlen(c.handle, A, None, (ctypes.c_int32 * 3)(0, 1, 2), None) == duo.DUO_ERR_INVALID_ARG
+    # no rows at all: nothing to do, null tensors accepted, nothing enqueued
+    zero = (ctypes.c_int32 * 3)(0, 0, 0)
+    assert lib.duo_prefill_varlen(c.handle, None, None, None, zero, None, None) == duo.DUO_OK
+    assert lib.duo_cache_append_varlen(c.handle, None, None, zero, None) == duo.DUO_OK
     assert c.lengths() == [0, 0]
 
 
