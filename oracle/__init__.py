@@ -19,11 +19,12 @@ pages this project was built from):
   listed in ``mixed_attention`` and ``cache_state``.
 
 Every function here is pinned by ``tests/test_oracle.py`` and
-``tests/test_oracle_quant.py`` and ``tests/test_oracle_rope.py`` against closed forms, a library routine (torch
+``tests/test_oracle_quant.py``, ``tests/test_oracle_rope.py`` and ``tests/test_oracle_fp8.py`` against closed forms, a library routine (torch
 fp64 scaled-dot-product attention), brute force on tiny inputs and
 hand-derived fixtures under ``tests/golden/``.  ``quantized_cache`` adds the
 int8 retrieval cache the pages allude to ("combined with quantization",
-abstract), with the scheme taken as a stated reading; ``rope`` adds rotary
+abstract), with the scheme taken as a stated reading, and ``fp8_cache`` the
+e4m3 alternative; ``rope`` adds rotary
 position embedding on the way into the cache (cited by the pages only, in the
 pith.science reference list), restated from its published definition.
 """
@@ -49,4 +50,11 @@ from .rope import (  # noqa: F401
     rope_frequencies,
     rotated_qk,
     round_bf16,
+)
+from .fp8_cache import (  # noqa: F401
+    dequantize_rows_fp8,
+    e4m3_decode,
+    e4m3_encode,
+    quantize_rows_fp8,
+    seen_rows_fp8,
 )
