@@ -70,8 +70,17 @@ typedef enum duo_status {
  *     even (a zero row: scale 0, codes 0); stored as the byte code + 128.
  *     A call attends to rows stored by earlier calls through code * scale,
  *     and to the rows of its own chunk (or decode token) as given.
- * Streaming heads' caches are bf16 in both formats. */
-typedef enum duo_kv_format { DUO_KV_BF16 = 0, DUO_KV_INT8 = 1 } duo_kv_format;
+ *   DUO_KV_FP8: one OCP E4M3 8-bit float per element (largest finite 448)
+ *     and one power-of-two scale per tensor for the whole cache
+ *     (duo_config.kv_scale_k / kv_scale_v): code = e4m3(x / scale), which
+ *     clamps to [-448, 448] and rounds to nearest even.  Every row a call
+ *     attends to -- its own new rows included, which are stored first -- is
+ *     seen through code * scale.  Retrieval heads' prefill then runs on fp8
+ *     matrix cores: q is rounded to e4m3 (with a power-of-two scale per
+ *     query row) and the softmax weights too, so its results carry fp8
+ *     rounding (about 2^-4 per element) beyond the stored K and V.
+ * Streaming heads' caches are bf16 in every format. */
+typedef enum duo_kv_format { DUO_KV_BF16 = 0, DUO_KV_INT8 = 1, DUO_KV_FP8 = 2 } duo_kv_format;
 
 /* Rotary position embedding applied inside the library (RoFormer, cited in
  * the reference list of the pith.science review page), when
@@ -111,6 +120,9 @@ typedef struct duo_config {
    * (a page holds whole decode row batches and prefill tiles). */
   int32_t page_tokens;
   int64_t num_pages;
+  /* DUO_KV_FP8: the K and V scales, powers of two in [2^-32, 2^32]; 0 = 1 */
+  float kv_scale_k;
+  float kv_scale_v;
 } duo_config;
 
 /* Opaque host-side handle: configuration, head maps, region offsets and the
@@ -127,7 +139,7 @@ typedef struct duo_cache duo_cache;
  * (in increasing k), likewise for streaming heads.
  *   lengths  int32 [B]                     tokens stored per sequence
  *   rk, rv   bf16  [B][nR][max_len][D]     retrieval cache, row = position
- *            (DUO_KV_INT8: uint8 codes, same shape)
+ *            (DUO_KV_INT8: uint8 codes, DUO_KV_FP8: e4m3 codes, same shape)
  *   rks, rvs fp32  [B][nR][max_len]        DUO_KV_INT8 only: row scales
  *            (offset -1 for DUO_KV_BF16)
  *   sk, sv   bf16  [B][nS][sink+recent][D] streaming cache, slot map:
@@ -158,8 +170,9 @@ typedef struct duo_layout {
  * sink < 0, recent < 1, max_len < 1, misaligned dev_buf, scale < 0 or not
  * finite, kv_format not a duo_kv_format, rope_base < 0 or not finite,
  * rope_style not a duo_rope_style, page_tokens not 0 or a power of two in
- * 512..65536, page_tokens > 0 with num_pages < 1), UNSUPPORTED (head_dim,
- * batch, rope_base > 0 with DUO_KV_INT8), BUFFER_TOO_SMALL, HIP. */
+ * 512..65536, page_tokens > 0 with num_pages < 1, kv_scale_k / kv_scale_v
+ * not 0 or a power of two in [2^-32, 2^32]), UNSUPPORTED (head_dim, batch,
+ * rope_base > 0 with DUO_KV_INT8 or DUO_KV_FP8), BUFFER_TOO_SMALL, HIP. */
 duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
                           size_t* required_bytes, duo_cache** out, void* stream);
 

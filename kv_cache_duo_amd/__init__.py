@@ -38,7 +38,7 @@ DUO_ERR_HIP = 5
 DUO_MAX_BATCH = 128
 
 
-DUO_KV_BF16, DUO_KV_INT8 = 0, 1
+DUO_KV_BF16, DUO_KV_INT8, DUO_KV_FP8 = 0, 1, 2
 DUO_ROPE_INTERLEAVED, DUO_ROPE_HALF = 0, 1
 
 
@@ -56,6 +56,7 @@ class _Config(ctypes.Structure):
         ("scale", ctypes.c_float), ("kv_head_is_retrieval", ctypes.POINTER(ctypes.c_uint8)),
         ("kv_format", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
         ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+        ("kv_scale_k", ctypes.c_float), ("kv_scale_v", ctypes.c_float),
     ]
 
 
@@ -147,6 +148,8 @@ class Config:
     rope_style: int = 0     # DUO_ROPE_INTERLEAVED (pairs 2i, 2i+1) or DUO_ROPE_HALF (pairs i, i + D/2)
     page_tokens: int = 0    # > 0: paged retrieval cache, pages of this many positions
     num_pages: int = 0      # paged: pages in the pool
+    kv_scale_k: float = 0.0  # DUO_KV_FP8: power-of-two K scale (0 = 1)
+    kv_scale_v: float = 0.0  # DUO_KV_FP8: power-of-two V scale (0 = 1)
 
     def _c(self):
         mask = (ctypes.c_uint8 * max(len(self.kv_head_is_retrieval), 1))(
@@ -154,7 +157,7 @@ class Config:
         c = _Config(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim, self.max_len,
                     self.sink, self.recent, self.scale,
                     ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)), self.kv_format, self.rope_base,
-                    self.rope_style, self.page_tokens, self.num_pages)
+                    self.rope_style, self.page_tokens, self.num_pages, self.kv_scale_k, self.kv_scale_v)
         return c, mask  # keep the mask alive for the call
 
 
@@ -332,7 +335,7 @@ def cache_views(cache: Cache):
         nbytes *= torch.tensor([], dtype=dtype).element_size()
         return buf[off:off + nbytes].view(dtype).view(*shape)
 
-    rdt = torch.uint8 if lay.kv_format == DUO_KV_INT8 else torch.bfloat16
+    rdt = torch.uint8 if lay.kv_format in (DUO_KV_INT8, DUO_KV_FP8) else torch.bfloat16
     views = {"lengths": region(lay.lengths_offset, (cfg.batch,), torch.int32)}
     if lay.page_tokens > 0:
         # pools, the page table, and copies of every sequence's rows gathered

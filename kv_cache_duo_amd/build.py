@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libduo.so")
 CEILING = os.path.join(HERE, "ceiling")  # measured HBM / MFMA ceilings (standalone)
 
-SOURCES = ["duo_api.cpp", "append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["duo_api.cpp", "append.hip", "decode.hip", "prefill.hip", "prefill_fp8.hip"]
 
 ARCH = "gfx950"
 COMMON = [

@@ -9,7 +9,7 @@
 // Within one call only the last `recent` non-sink positions of a chunk are
 // written to the ring: older ones would be overwritten by the same call.
 // With an int8 retrieval cache (duo_kv_format DUO_KV_INT8) retrieval rows
-// are quantized as they are stored.  With rotary position embedding, K rows
+// are quantized as they are stored (fp8 cache, DUO_KV_FP8: e4m3 codes).  With rotary position embedding, K rows
 // are turned to their position as they are stored (RoFormer, cited in the
 // pith.science review page's reference list).
 #include "device_util.h"
@@ -92,7 +92,10 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
       rope_angles8<D>((int)p, c, g.rope_half, g.rope_rho, cs, sn);
       kx = rope_apply8<CH>(kx, cs, sn, g.rope_half, c);
     }
-    if (retrieval && g.kv_int8) {
+    if (retrieval && g.kv_fp8) {
+      store_fp8_row8(reinterpret_cast<uint8_t*>(g.rk) + rrow * D, kx, c, g.fp8_inv_k);
+      store_fp8_row8(reinterpret_cast<uint8_t*>(g.rv) + rrow * D, vx, c, g.fp8_inv_v);
+    } else if (retrieval && g.kv_int8) {
       // int8 row: the CH lanes of the row agree on its scale (group max)
       store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rk) + rrow * D, g.rks + rrow, kx, c);
       store_int8_row<CH>(reinterpret_cast<uint8_t*>(g.rv) + rrow * D, g.rvs + rrow, vx, c);

@@ -265,9 +265,11 @@ __device__ void merge_records(const Geom& g, const DecodeArgs& a, char* lds, flo
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
-// Q8: the cache's retrieval rows are int8 codes with fp32 row scales
+// FMT: the cache's retrieval rows are bf16 (0), int8 codes with fp32 row
+// scales (1, DUO_KV_INT8) or e4m3 codes with per-tensor power-of-two scales
+// (2, DUO_KV_FP8)
 // (DUO_KV_INT8); streaming units of the same launch stay bf16.
-template <int D, int GC, bool Q8>
+template <int D, int GC, int FMT>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, DecodeArgs a) {
   constexpr int LPR = D / 8;                  // lanes per row (8 bf16 each)
   constexpr int RPW = 64 / LPR;               // rows per wave per load
@@ -481,8 +483,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
                    std::integral_constant<int, ROWS_ITER>());
     }
   };
-  const bool q8 = Q8 && retrieval;
-  if constexpr (Q8) {
+  const bool q8 = FMT != 0 && retrieval;  // 8-bit retrieval rows
+  if constexpr (FMT != 0) {
     if (retrieval) {
       // int8 rows 0..L-1 of the cache; the new token (row L) is scored from
       // the input below.  A row of D codes is read by LPR8 = D/16 lanes with
@@ -494,6 +496,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       // bf16 values stay exact), and the 1024 + 128 offset comes back as one
       // per-lane constant -1152 * sum(q).  V: o += (p * scale_v) * b in fp32,
       // with 128 * sum(p * scale_v) taken off once at the end.
+      // fp8 (FMT 2): K codes become exact f16 pairs (v_cvt_scalef32_pk_f16_fp8)
+      // for the same dot2 with no offset, V codes fp32 values; the two
+      // per-tensor scales fold into the score constant and into p.
       constexpr int LPR8 = D / 16;
       constexpr int RPW8 = 64 / LPR8;
       constexpr int ITER8 = kWaves * RPW8 * kInFlight;
@@ -523,8 +528,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
           q16[gg][e] = __builtin_bit_cast(uint32_t, hq);
           sum += (float)hq.x + (float)hq.y;
         }
-        qoff[gg] = -1152.0f * sum;
-        qsc[gg] = ldexpf(g.scale_log2, ex - 15);
+        qoff[gg] = FMT == 1 ? -1152.0f * sum : 0.f;
+        qsc[gg] = ldexpf(FMT == 1 ? g.scale_log2 : g.scale_log2 * g.fp8_scale_k, ex - 15);
         cacc[gg] = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) o8[gg][e] = 0.f;
@@ -539,15 +544,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       auto load8 = [&](Rows8 (&r)[kInFlight], Rows8 (&)[kInFlight], int base, int64_t r0) __attribute__((always_inline)) {
         const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + r0 * D;
         const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + r0 * D;
-        const float* cks = g.rks + r0;
-        const float* cvs = g.rvs + r0;
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
           const int row = min(row_of8(base, j), Tc - 1);
           r[j].k = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ck8 + (int64_t)row * D) + c8);
           r[j].v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cv8 + (int64_t)row * D) + c8);
-          r[j].ks = cks[row];
-          r[j].vs = cvs[row];
+          if constexpr (FMT == 1) {
+            r[j].ks = g.rks[r0 + row];
+            r[j].vs = g.rvs[r0 + row];
+          }
         }
       };
       auto process8 = [&](const Rows8 (&r)[kInFlight], const Rows8 (&)[kInFlight], int base)
@@ -556,11 +561,16 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
           const bool valid = row_of8(base, j) < Tc;
-          uint32_t kh[8];  // f16 pairs 1024 + b of the 16 codes
+          uint32_t kh[8];  // f16 pairs of the 16 codes: 1024 + b (int8), the e4m3 values (fp8)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            kh[2 * e] = __builtin_amdgcn_perm(0x64646464u, r[j].k[e], 0x04010400u);
-            kh[2 * e + 1] = __builtin_amdgcn_perm(0x64646464u, r[j].k[e], 0x04030402u);
+            if constexpr (FMT == 1) {
+              kh[2 * e] = __builtin_amdgcn_perm(0x64646464u, r[j].k[e], 0x04010400u);
+              kh[2 * e + 1] = __builtin_amdgcn_perm(0x64646464u, r[j].k[e], 0x04030402u);
+            } else {
+              kh[2 * e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].k[e], 1.0f, false));
+              kh[2 * e + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r[j].k[e], 1.0f, true));
+            }
           }
 #pragma unroll
           for (int gg = 0; gg < GC; ++gg) {
@@ -570,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
               acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, kh[e]), __builtin_bit_cast(f16x2_t, q16[gg][e]),
                                            acc, false);
             acc = group_sum<LPR8>(acc);
-            s[j][gg] = valid ? acc * (r[j].ks * qsc[gg]) : -INFINITY;
+            s[j][gg] = valid ? acc * (FMT == 1 ? r[j].ks * qsc[gg] : qsc[gg]) : -INFINITY;
           }
         }
 #pragma unroll
@@ -588,12 +598,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 #pragma unroll
           for (int j = 0; j < kInFlight; ++j) {
             const float p = exp2_fast(s[j][gg] - mu);
-            const float pv = p * r[j].vs;
             l[gg] += p;
-            cacc[gg] += pv;
+            if constexpr (FMT == 1) {
+              const float pv = p * r[j].vs;
+              cacc[gg] += pv;
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-              o8[gg][e] = fmaf(pv, (float)((r[j].v[e >> 2] >> (8 * (e & 3))) & 0xffu), o8[gg][e]);
+              for (int e = 0; e < 16; ++e)
+                o8[gg][e] = fmaf(pv, (float)((r[j].v[e >> 2] >> (8 * (e & 3))) & 0xffu), o8[gg][e]);
+            } else {
+              const float pv = p * g.fp8_scale_v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float2 f0 = fp8_unpack2<false>(r[j].v[e]), f1 = fp8_unpack2<true>(r[j].v[e]);
+                o8[gg][4 * e] = fmaf(pv, f0.x, o8[gg][4 * e]);
+                o8[gg][4 * e + 1] = fmaf(pv, f0.y, o8[gg][4 * e + 1]);
+                o8[gg][4 * e + 2] = fmaf(pv, f1.x, o8[gg][4 * e + 2]);
+                o8[gg][4 * e + 3] = fmaf(pv, f1.y, o8[gg][4 * e + 3]);
+              }
+            }
           }
           m[gg] = mn;
         }
@@ -607,10 +629,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       // wave's state to the 8-dims-per-lane layout of the code below: lane
       // c < LPR takes dims 8c .. 8c+7 (half c mod 2 of lane c/2); the other
       // row groups are left empty
+      if constexpr (FMT == 1) {
 #pragma unroll
-      for (int gg = 0; gg < GC; ++gg)
+        for (int gg = 0; gg < GC; ++gg)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-128.0f, cacc[gg], o8[gg][e]);
+          for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-128.0f, cacc[gg], o8[gg][e]);
+      }
 #pragma unroll
       for (int off = LPR8; off < 64; off <<= 1) {
 #pragma unroll
@@ -656,9 +680,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   if (q8 || g.rope) {
     own_new = split == 0;
     if (own_new) {
-      const uint4 vx = reinterpret_cast<const uint4*>(nv)[c];
+      uint4 vx = reinterpret_cast<const uint4*>(nv)[c];
+      uint4 kx = knew;
+      if (FMT == 2 && retrieval) {  // attended through its stored fp8 value (exact in bf16)
+        kx = fp8_roundtrip8(kx, g.fp8_inv_k, g.fp8_scale_k);
+        vx = fp8_roundtrip8(vx, g.fp8_inv_v, g.fp8_scale_v);
+      }
       const bool mine = wave == 0 && grp == 0;
-      const uint32_t kw[4] = {knew.x, knew.y, knew.z, knew.w}, vw[4] = {vx.x, vx.y, vx.z, vx.w};
+      const uint32_t kw[4] = {kx.x, kx.y, kx.z, kx.w}, vw[4] = {vx.x, vx.y, vx.z, vx.w};
 #pragma unroll
       for (int gg = 0; gg < GC; ++gg) {
         float acc = 0.f;
@@ -718,7 +747,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     const uint4 kx = knew;  // threads 0..LPR-1 hold chunks c = 0..LPR-1
     const uint4 vx = reinterpret_cast<const uint4*>(nv)[threadIdx.x];
     const int64_t row = retrieval ? retrieval_row0(g, b, idx, new_row) + new_row : unit_row0 + new_row;
-    if (q8) {
+    if (q8 && FMT == 2) {
+      store_fp8_row8(reinterpret_cast<uint8_t*>(g.rk) + row * D, kx, threadIdx.x, g.fp8_inv_k);
+      store_fp8_row8(reinterpret_cast<uint8_t*>(g.rv) + row * D, vx, threadIdx.x, g.fp8_inv_v);
+    } else if (q8) {
       store_int8_row<LPR>(reinterpret_cast<uint8_t*>(g.rk) + row * D, g.rks + row, kx, threadIdx.x);
       store_int8_row<LPR>(reinterpret_cast<uint8_t*>(g.rv) + row * D, g.rvs + row, vx, threadIdx.x);
     } else {
@@ -820,10 +852,11 @@ int32_t max_splits_for(int64_t max_len, int32_t slots, int head_chunk) {
 
 DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   DecodePlan p;
-  p.head_chunk = decode_head_chunk(g.G, g.kv_int8 != 0);
+  const bool byte_rows = g.kv_int8 || g.kv_fp8;
+  p.head_chunk = decode_head_chunk(g.G, byte_rows);
   const int n_hc = g.G / p.head_chunk;
   // the larger pair when the retrieval rows are int8 (a multiple of the bf16 one)
-  const int64_t pair = g.kv_int8 ? decode_pair_rows_int8(g.D, p.head_chunk) : decode_pair_rows(g.D, p.head_chunk);
+  const int64_t pair = byte_rows ? decode_pair_rows_int8(g.D, p.head_chunk) : decode_pair_rows(g.D, p.head_chunk);
   int64_t total = 0;
   int32_t tmax = 1;
   for (int b = 0; b < g.B; ++b) {
@@ -835,7 +868,7 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   // kMinPairs pairs each, and few enough work-groups per unit for its records.
   auto round_pair = [&](int64_t x) { return (x + pair - 1) / pair * pair; };
   int64_t ts = round_pair((total + 2047) / 2048);
-  const int min_pairs = g.kv_int8 ? kMinPairsInt8 : kMinPairs;
+  const int min_pairs = byte_rows ? kMinPairsInt8 : kMinPairs;
   if (ts < min_pairs * pair) ts = min_pairs * pair;
   const int64_t ts_cap = round_pair(((int64_t)tmax + g.max_splits - 1) / g.max_splits);
   if (ts < ts_cap) ts = ts_cap;
@@ -856,12 +889,16 @@ template <int DD, int GG>
 hipError_t launch_dg(const Geom& g, const Seqs& q, const DecodeArgs& a, dim3 grid, dim3 block, hipStream_t s) {
   if constexpr (GG <= 4) {
     if (g.kv_int8) {
-      hipLaunchKernelGGL((decode_kernel<DD, GG, true>), grid, block, 0, s, g, q, a);
+      hipLaunchKernelGGL((decode_kernel<DD, GG, 1>), grid, block, 0, s, g, q, a);
+      return hipGetLastError();
+    }
+    if (g.kv_fp8) {
+      hipLaunchKernelGGL((decode_kernel<DD, GG, 2>), grid, block, 0, s, g, q, a);
       return hipGetLastError();
     }
   }
-  if (g.kv_int8) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((decode_kernel<DD, GG, false>), grid, block, 0, s, g, q, a);
+  if (g.kv_int8 || g.kv_fp8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((decode_kernel<DD, GG, 0>), grid, block, 0, s, g, q, a);
   return hipGetLastError();
 }
 

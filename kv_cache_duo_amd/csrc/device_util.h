@@ -89,6 +89,48 @@ __device__ __forceinline__ void store_int8_row(uint8_t* codes, float* scale_out,
   if (c == 0) *scale_out = scale;
 }
 
+// fp8 retrieval cache (duo_kv_format DUO_KV_FP8): OCP E4M3 codes of
+// x / scale, the scale a power of two (so x * (1/scale) is exact).  The
+// conversion instruction rounds to nearest even but turns magnitudes from
+// 465 up into NaN, so values are clamped to +-448 (the largest finite) first.
+__device__ __forceinline__ float fp8_clamp(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
+// Codes of 4 values: bytes 0..3 of the result.
+__device__ __forceinline__ uint32_t fp8_pack4(float a, float b, float c, float d) {
+  uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(a), fp8_clamp(b), 0u, false);
+  return __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(c), fp8_clamp(d), w, true);
+}
+// Store the codes of the 8 bf16 values x (chunk c of a row) at codes + 8c.
+__device__ __forceinline__ void store_fp8_row8(uint8_t* codes, const uint4& x, int c, float inv_scale) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  const uint32_t lo = fp8_pack4(bf16_lo(w[0]) * inv_scale, bf16_hi(w[0]) * inv_scale, bf16_lo(w[1]) * inv_scale,
+                                bf16_hi(w[1]) * inv_scale);
+  const uint32_t hi = fp8_pack4(bf16_lo(w[2]) * inv_scale, bf16_hi(w[2]) * inv_scale, bf16_lo(w[3]) * inv_scale,
+                                bf16_hi(w[3]) * inv_scale);
+  reinterpret_cast<uint2*>(codes)[c] = make_uint2(lo, hi);
+}
+// The two fp32 values of the codes in bytes 2H, 2H+1 of w.
+template <bool H>
+__device__ __forceinline__ float2 fp8_unpack2(uint32_t w) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8(w, H);
+  return make_float2(f.x, f.y);
+}
+
+// The 8 bf16 values x as an fp8 cache stores them: code * scale, which
+// bf16 holds exactly (e4m3 values have 4 significant bits).
+__device__ __forceinline__ uint4 fp8_roundtrip8(const uint4& x, float inv_scale, float scale) {
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t c = __builtin_amdgcn_cvt_pk_fp8_f32(fp8_clamp(bf16_lo(w[e]) * inv_scale),
+                                                       fp8_clamp(bf16_hi(w[e]) * inv_scale), 0u, false);
+    const float2 f = fp8_unpack2<false>(c);
+    o[e] = pack_bf16x2(f.x * scale, f.y * scale);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 // Rotary position embedding (RoFormer): pair i of a head turns by p * theta_i
 // at position p, theta_i = base^(-2i/D) = rho^i, (a, b) -> (a cos - b sin,
 // a sin + b cos).  The angle is formed in fp64 revolutions (p * theta_i / 2 pi)

@@ -45,14 +45,21 @@ duo_status check_config(const duo_config* c) {
   if (c->sink < 0 || c->recent < 1 || c->max_len < 1) return DUO_ERR_INVALID_ARG;
   if (!(c->scale >= 0.f) || !std::isfinite(c->scale)) return DUO_ERR_INVALID_ARG;
   if (c->kv_head_is_retrieval == nullptr) return DUO_ERR_INVALID_ARG;
-  if (c->kv_format != DUO_KV_BF16 && c->kv_format != DUO_KV_INT8) return DUO_ERR_INVALID_ARG;
+  if (c->kv_format != DUO_KV_BF16 && c->kv_format != DUO_KV_INT8 && c->kv_format != DUO_KV_FP8)
+    return DUO_ERR_INVALID_ARG;
+  for (float sc : {c->kv_scale_k, c->kv_scale_v}) {
+    if (sc == 0.f) continue;
+    int e = 0;
+    if (!std::isfinite(sc) || !(sc > 0.f) || std::frexp(sc, &e) != 0.5f || e - 1 < -32 || e - 1 > 32)
+      return DUO_ERR_INVALID_ARG;
+  }
   if (!(c->rope_base >= 0.f) || !std::isfinite(c->rope_base)) return DUO_ERR_INVALID_ARG;
   if (c->rope_base > 0.f && c->rope_style != DUO_ROPE_INTERLEAVED && c->rope_style != DUO_ROPE_HALF)
     return DUO_ERR_INVALID_ARG;
   if (c->head_dim != 64 && c->head_dim != 128) return DUO_ERR_UNSUPPORTED;
   if (c->batch > DUO_MAX_BATCH || c->num_kv_heads > duo::kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
   if (c->max_len > kMaxLen || (int64_t)c->sink + c->recent > kMaxLen) return DUO_ERR_UNSUPPORTED;
-  if (c->rope_base > 0.f && c->kv_format == DUO_KV_INT8) return DUO_ERR_UNSUPPORTED;
+  if (c->rope_base > 0.f && c->kv_format != DUO_KV_BF16) return DUO_ERR_UNSUPPORTED;
   if (c->page_tokens != 0) {
     const int32_t p = c->page_tokens;
     if (p < 512 || p > 65536 || (p & (p - 1)) != 0) return DUO_ERR_INVALID_ARG;
@@ -86,12 +93,25 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   g->nR = nr;
   g->nS = ns;
   g->kv_int8 = c->kv_format == DUO_KV_INT8;
+  g->kv_fp8 = c->kv_format == DUO_KV_FP8;
+  {
+    const float sk = c->kv_scale_k > 0.f ? c->kv_scale_k : 1.f, sv = c->kv_scale_v > 0.f ? c->kv_scale_v : 1.f;
+    int ek = 0, ev = 0;
+    std::frexp(sk, &ek);
+    std::frexp(sv, &ev);
+    g->fp8_exp_k = ek - 1;
+    g->fp8_exp_v = ev - 1;
+    g->fp8_scale_k = sk;
+    g->fp8_scale_v = sv;
+    g->fp8_inv_k = 1.f / sk;  // exact: powers of two
+    g->fp8_inv_v = 1.f / sv;
+  }
   g->rope = c->rope_base > 0.f;
   g->rope_half = g->rope && c->rope_style == DUO_ROPE_HALF;
   g->rope_rho = g->rope ? std::pow((double)c->rope_base, -2.0 / c->head_dim) : 0.0;
-  g->max_splits = duo::max_splits_for(c->max_len, g->slots, duo::decode_head_chunk(g->G, g->kv_int8 != 0));
+  g->max_splits = duo::max_splits_for(c->max_len, g->slots, duo::decode_head_chunk(g->G, g->kv_int8 || g->kv_fp8));
 
-  const int gc = duo::decode_head_chunk(g->G, g->kv_int8 != 0);
+  const int gc = duo::decode_head_chunk(g->G, g->kv_int8 || g->kv_fp8);
   const int64_t units = (int64_t)g->B * g->Hkv * (g->G / gc);
   int64_t off = 0;
   L->lengths_offset = off;
@@ -118,7 +138,7 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   off = align_up(off + 4 * units * g->max_splits * gc * (g->D + 2));
   L->work_bytes = off - L->work_offset;
   const int64_t row = 2 * (int64_t)g->D;
-  const int64_t rrow = g->kv_int8 ? (int64_t)g->D : row;  // retrieval row bytes
+  const int64_t rrow = (g->kv_int8 || g->kv_fp8) ? (int64_t)g->D : row;  // retrieval row bytes
   L->kv_format = c->kv_format;
   L->rk_offset = off;
   off = align_up(off + pool_rows * nr * rrow);
@@ -143,7 +163,7 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
 
 void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   char* base = static_cast<char*>(buf);
-  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / duo::decode_head_chunk(g->G, g->kv_int8 != 0));
+  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / duo::decode_head_chunk(g->G, g->kv_int8 || g->kv_fp8));
   g->lengths = reinterpret_cast<int32_t*>(base + L.lengths_offset);
   g->tickets = reinterpret_cast<uint32_t*>(base + L.work_offset);
   g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units * g->tickets_per_unit));
@@ -307,15 +327,18 @@ duo_status prefill_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const 
   // retrieval rows are stored (rotated) first and the attention reads every
   // retrieval key from the cache; streaming heads rotate their chunk rows
   // as they load them.
+  // An fp8 cache stores the retrieval rows first as well: its prefill reads
+  // every retrieval key and value as stored.
   hipError_t e = hipSuccess;
-  if (h->geom.rope) {
+  const bool store_first = h->geom.rope || h->geom.kv_fp8;
+  if (store_first) {
     e = duo::launch_append(h->geom, sq, kk, vv, max_n, s, duo::kAppendRetrieval);
     if (e != hipSuccess) return DUO_ERR_HIP;
   }
   e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), kk, vv, max_n, static_cast<uint16_t*>(out), s);
   if (e != hipSuccess) return DUO_ERR_HIP;
   e = duo::launch_append(h->geom, sq, kk, vv, max_n, s,
-                         h->geom.rope ? duo::kAppendStreaming : duo::kAppendRetrieval | duo::kAppendStreaming);
+                         store_first ? duo::kAppendStreaming : duo::kAppendRetrieval | duo::kAppendStreaming);
   if (e != hipSuccess) return DUO_ERR_HIP;
   for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += sq.n[b];
   return DUO_OK;

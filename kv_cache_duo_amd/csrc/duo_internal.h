@@ -18,6 +18,9 @@ struct Geom {
   int32_t S, W, slots;        // sink, recent, sink+recent
   int32_t nR, nS;             // retrieval / streaming KV heads
   int32_t kv_int8;            // retrieval rows stored as int8 codes + fp32 scales
+  int32_t kv_fp8;             // retrieval rows stored as e4m3 codes, per-tensor power-of-two scales
+  int32_t fp8_exp_k, fp8_exp_v;  // log2 of the K / V scales
+  float fp8_scale_k, fp8_scale_v, fp8_inv_k, fp8_inv_v;
   int64_t max_len;
   float scale_log2;           // softmax scale * log2(e): scores in base-2 units
   int32_t rope;               // rotary position embedding applied to q and k
@@ -107,6 +110,11 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q);
 hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p,
                          const uint16_t* qin, const uint16_t* kin, const uint16_t* vin,
                          uint16_t* out, hipStream_t s);
+
+// Retrieval heads of an fp8 cache (DUO_KV_FP8), on fp8 matrix cores; the
+// chunk's retrieval rows must be stored first.
+hipError_t launch_prefill_fp8(const Geom& g, const Seqs& q, const uint16_t* qin, int32_t max_n, uint16_t* out,
+                              hipStream_t s);
 
 hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, const uint16_t* kin,
                           const uint16_t* vin, int32_t max_n, uint16_t* out, hipStream_t s);

@@ -598,10 +598,11 @@ int heads_per_group(int G) {
 }
 
 template <int D, bool Q8, bool ROPE>
-hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s) {
+hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s,
+                    bool streaming_only = false) {
   a.tq = kWaves * 32 / a.gh;
   a.tiles_max = (max_n + a.tq - 1) / a.tq;
-  a.items_r = a.tiles_max * g.B * g.nR * a.n_hc;
+  a.items_r = streaming_only ? 0 : a.tiles_max * g.B * g.nR * a.n_hc;
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * g.B * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE>), dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
@@ -623,7 +624,13 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   // int8 retrieval rows are only read from a stored prefix
   bool prefix = false;
   for (int b = 0; b < g.B; ++b) prefix = prefix || (q.n[b] > 0 && q.len[b] > 0);
-  if (g.rope)  // never with an int8 cache (rejected by the configuration check)
+  if (g.kv_fp8) {  // retrieval heads on fp8 matrix cores, streaming heads here
+    hipError_t e = launch_prefill_fp8(g, q, qin, max_n, out, s);
+    if (e != hipSuccess) return e;
+    return g.D == 128 ? launch_t<128, false, false>(g, q, a, max_n, s, true)
+                      : launch_t<64, false, false>(g, q, a, max_n, s, true);
+  }
+  if (g.rope)  // never with an 8-bit cache (rejected by the configuration check)
     return g.D == 128 ? launch_t<128, false, true>(g, q, a, max_n, s) : launch_t<64, false, true>(g, q, a, max_n, s);
   if (g.kv_int8 && g.nR > 0 && prefix)
     return g.D == 128 ? launch_t<128, true, false>(g, q, a, max_n, s) : launch_t<64, true, false>(g, q, a, max_n, s);

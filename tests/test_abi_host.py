@@ -152,8 +152,41 @@ def test_int8_layout():
     r16 = (bf.sk_offset - bf.rk_offset)
     assert r8 < r16 * 0.6
     with pytest.raises(duo.DuoError) as e:
-        duo.required_bytes(_cfg(kv_format=2))
+        duo.required_bytes(_cfg(kv_format=3))
     assert e.value.status == duo.DUO_ERR_INVALID_ARG
+
+
+def test_fp8_layout():
+    """DUO_KV_FP8: retrieval rows of D bytes, no scale regions (one scale per
+    tensor, in the configuration); streaming regions stay bf16."""
+    cfg = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], kv_format=duo.DUO_KV_FP8, kv_scale_k=0.5, kv_scale_v=2.0)
+    c = _attach(cfg, [5, 7])
+    lay = c.layout()
+    assert lay.kv_format == duo.DUO_KV_FP8 and lay.rks_offset == -1 and lay.rvs_offset == -1
+    assert lay.rv_offset - lay.rk_offset >= cfg.batch * 2 * cfg.max_len * cfg.head_dim
+    assert lay.sk_offset - lay.rv_offset >= cfg.batch * 2 * cfg.max_len * cfg.head_dim
+    bf = _attach(_cfg(kv_head_is_retrieval=[0, 1, 1, 0]), [5, 7]).layout()
+    assert (lay.sk_offset - lay.rk_offset) * 2 <= (bf.sk_offset - bf.rk_offset) + 2 * 256
+    assert lay.sv_offset - lay.sk_offset == bf.sv_offset - bf.sk_offset
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kv_format=2, kv_scale_k=0.3), duo.DUO_ERR_INVALID_ARG),            # not a power of two
+    (dict(kv_format=2, kv_scale_v=-2.0), duo.DUO_ERR_INVALID_ARG),
+    (dict(kv_format=2, kv_scale_k=float("inf")), duo.DUO_ERR_INVALID_ARG),
+    (dict(kv_format=2, kv_scale_k=2.0 ** 40), duo.DUO_ERR_INVALID_ARG),       # outside [2^-32, 2^32]
+    (dict(kv_format=2, rope_base=10000.0), duo.DUO_ERR_UNSUPPORTED),          # rotary + fp8 cache
+])
+def test_fp8_invalid_configs(kw, status):
+    with pytest.raises(duo.DuoError) as e:
+        duo.required_bytes(_cfg(**kw))
+    assert e.value.status == status
+
+
+def test_fp8_scale_zero_means_one():
+    a = duo.required_bytes(_cfg(kv_format=duo.DUO_KV_FP8, kv_scale_k=0.0, kv_scale_v=0.0))
+    b = duo.required_bytes(_cfg(kv_format=duo.DUO_KV_FP8, kv_scale_k=0.25, kv_scale_v=8.0))
+    assert a == b > 0
 
 
 def _raw(c):
