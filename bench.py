@@ -19,6 +19,9 @@ Inputs are resident in HBM before the timed region.  Reported:
   rope       the same step with rotary position embedding applied inside the
              library (same algorithmic counts; rotation work is overhead)
   paged      the same step over a paged retrieval cache (1024-position pages)
+  fp8        the same step over an fp8 (e4m3) retrieval cache: retrieval
+             heads' prefill on fp8 matrix cores (priced against the 5 PF
+             dense fp8 peak), decode over D-byte rows
   cpu_baseline  the fp64 oracle on a bounded sample of the same decode work
 Algorithmic counts: each K/V byte once per (sequence, KV head) plus q, out
 and the appended token; flops = 4*D per allowed (query, key) pair per query
@@ -38,6 +41,7 @@ import time
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
@@ -70,7 +74,8 @@ def measured_ceilings(decode_mib: int):
     import subprocess
     exe = os.path.join(ROOT, "kv_cache_duo_amd", "ceiling")
     out = {}
-    for args in (["stream_read_rotating", str(decode_mib), "8"], ["stream_read", "4096"], ["mfma"], ["mfma_random"]):
+    for args in (["stream_read_rotating", str(decode_mib), "8"], ["stream_read", "4096"], ["mfma"], ["mfma_random"],
+                 ["mfma_fp8_random"]):
         r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=120)
         if r.returncode != 0:
             raise RuntimeError(f"{exe} {' '.join(args)} failed: {r.stderr}")
@@ -90,8 +95,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-steps", type=int, default=128)
     p.add_argument("--no-ceilings", action="store_true")
-    p.add_argument("--legs", default="int8,rope,paged",
-                   help="variant legs to run after the plain step (comma list of int8, rope, paged; empty for none)")
+    p.add_argument("--legs", default="int8,rope,paged,fp8",
+                   help="variant legs to run after the plain step (comma list of int8, rope, paged, fp8; "
+                        "empty for none)")
     return p.parse_args()
 
 
@@ -128,6 +134,21 @@ def decode_bytes_int8(w, mask, ctx: int) -> float:
     kv = 2 * w.batch * (nr * (ctx * row8 + row + row8) + ns * row * min(ctx + 1, w.sink + w.recent))
     qo = 2 * row * w.batch * w.num_q_heads
     append = 2 * row * w.batch * ns  # streaming heads' new token stored as bf16
+    return float(kv + qo + append)
+
+
+def decode_bytes_fp8(w, mask, ctx: int) -> float:
+    """Algorithmic bytes of one decode call with an fp8 retrieval cache: each
+    stored retrieval row once as D codes for K and for V (one scale per
+    tensor, a kernel argument), the new token read (bf16) and stored (fp8),
+    streaming rows as bf16, q/out."""
+    nr = int(sum(mask))
+    ns = w.num_kv_heads - nr
+    row = 2 * w.head_dim
+    row8 = w.head_dim
+    kv = 2 * w.batch * (nr * (ctx * row8 + row + row8) + ns * row * min(ctx + 1, w.sink + w.recent))
+    qo = 2 * row * w.batch * w.num_q_heads
+    append = 2 * row * w.batch * ns
     return float(kv + qo + append)
 
 
@@ -264,6 +285,8 @@ def main():
     # and with a paged retrieval cache (pages of 1024 positions, a pool just
     # large enough)
     page = 1024
+    if "fp8" in legs:
+        variants["fp8"] = variant_phases([dataclasses.replace(c, kv_format=duo.DUO_KV_FP8) for c in cfgs], "fp8")
     if "paged" in legs:
         variants["paged"] = variant_phases(
             [dataclasses.replace(c, page_tokens=page, num_pages=(t_all + page - 1) // page) for c in cfgs], "paged")
@@ -328,6 +351,19 @@ def main():
                            "decode_time_vs_contiguous": round(dec_p_ms / dec_ms, 4),
                            "prefill_time_vs_contiguous": round(pre_p_ms / pre_ms, 4),
                            "page_tokens": page}
+    if "fp8" in variants:
+        pre_f_ms, dec_f_ms = variants["fp8"]
+        bytesf_step = sum(decode_bytes_fp8(w, m, w.prefill + s) for m in masks for s in range(w.decode_steps))
+        decf_gbs = bytesf_step * args.steps / (dec_f_ms * 1e-3) / 1e9
+        pref_tflops = flops_step * args.steps / (pre_f_ms * 1e-3) / 1e12
+        result["fp8"] = {"decode_gbs": round(decf_gbs, 1), "decode_frac_of_hbm_peak": round(decf_gbs / HBM_PEAK_GBS, 4),
+                         "decode_bytes_per_launch": bytesf_step / n_dec,
+                         "decode_time_vs_bf16": round(dec_f_ms / dec_ms, 4),
+                         "prefill_tflops": round(pref_tflops, 1),
+                         "prefill_frac_of_fp8_mfma_peak": round(pref_tflops / FP8_MFMA_PEAK_TFLOPS, 4),
+                         "prefill_phase_ms_per_step": round(pre_f_ms / args.steps, 3),
+                         "prefill_time_vs_bf16": round(pre_f_ms / pre_ms, 4),
+                         "cache": "retrieval K/V as e4m3 codes, one power-of-two scale per tensor (DUO_KV_FP8)"}
     if not args.no_ceilings:
         result["measured_ceilings"] = measured_ceilings(max(1, int(round(bytes_per_launch / 2**20))))
     if not args.no_cpu_baseline:

@@ -4,6 +4,8 @@
 //   ceiling stream_read_rotating <MiB> <n> -- the same over n buffers in turn
 //   ceiling mfma               -- back-to-back v_mfma_f32_32x32x16_bf16
 //   ceiling mfma_random        -- the same with changing pseudo-random operands
+//   ceiling mfma_fp8_random    -- v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit
+//                                 scales) with changing pseudo-random operands
 // Standalone executable (not part of the C ABI); prints one JSON line.
 #include <hip/hip_runtime.h>
 
@@ -99,6 +101,41 @@ __global__ __launch_bounds__(256) void mfma_loop_random(float* out, int iters) {
   if (s == 1234.5f) out[blockIdx.x] = s;
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+// The same rounds on e4m3 operands (pseudo-random values in [-2, 2) as
+// codes), through the scaled fp8 instruction with unit scales (E8M0 127).
+__device__ __forceinline__ int fp8_word(unsigned seed) {
+  const unsigned w = __builtin_amdgcn_cvt_pk_fp8_f32(hash_unit(seed), hash_unit(seed + 1), 0u, false);
+  return (int)__builtin_amdgcn_cvt_pk_fp8_f32(hash_unit(seed + 2), hash_unit(seed + 3), w, true);
+}
+#define FP8_MFMA(A, B, C) __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(A, B, C, 0, 0, 0, 127, 0, 127)
+__global__ __launch_bounds__(256) void mfma_loop_fp8_random(float* out, int iters) {
+  i32x8 a[4], b[4];
+  const unsigned seed = (blockIdx.x * 256u + threadIdx.x) * 512u;
+#pragma unroll
+  for (int f = 0; f < 4; ++f)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      a[f][j] = fp8_word(seed + f * 32 + 4 * j);
+      b[f][j] = fp8_word(seed + 256 + f * 32 + 4 * j);
+    }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  for (int i = 0; i < iters; i += 4) {
+    c0 = FP8_MFMA(a[0], b[0], c0); c1 = FP8_MFMA(a[1], b[1], c1);
+    c2 = FP8_MFMA(a[2], b[2], c2); c3 = FP8_MFMA(a[3], b[3], c3);
+    c0 = FP8_MFMA(a[1], b[2], c0); c1 = FP8_MFMA(a[2], b[3], c1);
+    c2 = FP8_MFMA(a[3], b[0], c2); c3 = FP8_MFMA(a[0], b[1], c3);
+    c0 = FP8_MFMA(a[2], b[0], c0); c1 = FP8_MFMA(a[3], b[1], c1);
+    c2 = FP8_MFMA(a[0], b[2], c2); c3 = FP8_MFMA(a[1], b[3], c3);
+    c0 = FP8_MFMA(a[3], b[3], c0); c1 = FP8_MFMA(a[0], b[0], c1);
+    c2 = FP8_MFMA(a[1], b[1], c2); c3 = FP8_MFMA(a[2], b[2], c3);
+  }
+  float s = 0.f;
+  for (int r = 0; r < 16; ++r) s += c0[r] + c1[r] + c2[r] + c3[r];
+  if (s == 1234.5f) out[blockIdx.x] = s;
+}
+#undef FP8_MFMA
+
 bool ok(hipError_t e, const char* what) {
   if (e != hipSuccess) fprintf(stderr, "%s: %s\n", what, hipGetErrorString(e));
   return e == hipSuccess;
@@ -167,7 +204,8 @@ int run_stream_read_rotating(size_t mib, int nbuf) {
   return 0;
 }
 
-int run_mfma(bool random) {
+// mode 0: bf16 constant operands, 1: bf16 random operands, 2: fp8 random
+int run_mfma(int mode) {
   int dev = 0, cus = 0;
   if (!ok(hipGetDevice(&dev), "device") ||
       !ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "attr"))
@@ -178,7 +216,7 @@ int run_mfma(bool random) {
   if (!ok(hipMalloc(&out, blocks * 4), "hipMalloc")) return 1;
   hipEvent_t a, b;
   if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return 1;
-  auto kernel = random ? mfma_loop_random : mfma_loop;
+  auto kernel = mode == 2 ? mfma_loop_fp8_random : mode == 1 ? mfma_loop_random : mfma_loop;
   hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, 0, out, iters);
   (void)hipEventRecord(a, 0);
   const int reps = 5;
@@ -187,9 +225,11 @@ int run_mfma(bool random) {
   if (!ok(hipEventSynchronize(b), "sync")) return 1;
   float ms = 0.f;
   (void)hipEventElapsedTime(&ms, a, b);
-  const double flop = (double)reps * blocks * 4 /*waves*/ * iters * 4 /*mfma*/ * 32768.0;
-  printf("{\"ceiling\": \"%s\", \"cus\": %d, \"tflops\": %.1f}\n",
-         random ? "mfma_bf16_32x32x16_random_operands" : "mfma_bf16_32x32x16", cus, flop / (ms * 1e-3) / 1e12);
+  const double per_mfma = mode == 2 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16;
+  const double flop = (double)reps * blocks * 4 /*waves*/ * iters * 4 /*mfma*/ * per_mfma;
+  const char* name = mode == 2 ? "mfma_fp8_32x32x64_random_operands"
+                     : mode == 1 ? "mfma_bf16_32x32x16_random_operands" : "mfma_bf16_32x32x16";
+  printf("{\"ceiling\": \"%s\", \"cus\": %d, \"tflops\": %.1f}\n", name, cus, flop / (ms * 1e-3) / 1e12);
   return 0;
 }
 
@@ -200,9 +240,10 @@ int main(int argc, char** argv) {
     return run_stream_read(argc >= 3 ? (size_t)std::atoll(argv[2]) : 4096);
   if (argc >= 2 && std::strcmp(argv[1], "stream_read_rotating") == 0)
     return run_stream_read_rotating(argc >= 3 ? (size_t)std::atoll(argv[2]) : 132, argc >= 4 ? std::atoi(argv[3]) : 8);
-  if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma(false);
-  if (argc >= 2 && std::strcmp(argv[1], "mfma_random") == 0) return run_mfma(true);
+  if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma(0);
+  if (argc >= 2 && std::strcmp(argv[1], "mfma_random") == 0) return run_mfma(1);
+  if (argc >= 2 && std::strcmp(argv[1], "mfma_fp8_random") == 0) return run_mfma(2);
   fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling stream_read_rotating <MiB> <buffers> | ceiling mfma"
-                  " | ceiling mfma_random\n");
+                  " | ceiling mfma_random | ceiling mfma_fp8_random\n");
   return 2;
 }

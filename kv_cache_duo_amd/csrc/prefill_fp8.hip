@@ -14,9 +14,12 @@
 //     scale operands, so S^T = K Q^T comes out in base-2 units;
 //   * the softmax weights rounded to e4m3 as 2^(s - mu + 7) (at most
 //     2^(7 + 1.75) < 448 with the reference mu moved whenever a tile max
-//     exceeds it by more than 1.75; weights down to 2^-16 stay representable),
-//     their fp32 sum l kept unrounded;
-//   * O^T += V^T P^T with the V scale as the instruction's A scale.
+//     exceeds it by more than 1.75; weights down to 2^-16 stay representable);
+//   * O^T += V^T P^T with the V scale as the instruction's A scale, and the
+//     weights' sum l from the same rounded weights through one more matrix
+//     instruction with an all-ones A operand, so that the output is exactly a
+//     convex combination of V rows (and the vector ALUs, which bound this
+//     kernel, are spared 31 adds per tile).
 // v_mfma_scale_f32_32x32x64_f8f6f4: 32x32 outputs per 64-deep contraction,
 // the C layout of the bf16 32x32 instructions; per 64-key tile a wave issues
 // 4 (D = 128) QK and 4 PV instructions instead of 16 + 16 bf16 ones.
@@ -75,9 +78,10 @@ __device__ __forceinline__ i32x2_t lds_read_tr8(const char* lds) {
   typedef __attribute__((address_space(3))) i32x2_t lds_i32x2_t;
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)lds);
 }
-// e4m3 codes of 4 values known to lie within +-448.
+// e4m3 codes of 4 values known to lie within +-448 (both halves of the word
+// are written, so its old contents are left unspecified).
 __device__ __forceinline__ uint32_t pack4_in_range(float a, float b, float c, float d) {
-  const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0u, false);
+  const uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, __builtin_nondeterministic_value(0u), false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -207,7 +211,12 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY, mu = 0.f, thr = -INFINITY, l_run = 0.f;
+  f32x16_t lacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
+  const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  float m_run = -INFINITY, mu = 0.f, thr = -INFINITY;
   f32x16_t negm;
 #pragma unroll
   for (int r = 0; r < 16; ++r) negm[r] = kPOffset;
@@ -256,7 +265,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
         m_run = m_new;
         mu = mu_new;
         thr = m_new == -INFINITY ? -INFINITY : kSlack;
-        l_run *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -277,9 +287,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
         for (int w4 = 0; w4 < 4; ++w4) {
           const float p0 = exp2_fast(sacc[kb2][4 * w4]), p1 = exp2_fast(sacc[kb2][4 * w4 + 1]);
           const float p2 = exp2_fast(sacc[kb2][4 * w4 + 2]), p3 = exp2_fast(sacc[kb2][4 * w4 + 3]);
-          l_run += (p0 + p1) + (p2 + p3);
           pb[4 * kb2 + w4] = (int)pack4_in_range(p0, p1, p2, p3);
         }
+      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, 127, 0, 127);
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         i32x8_t va;
@@ -305,9 +315,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
   }
 
   // ---- normalise and store this lane's query row
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (my_i <= i_hi) {
-    const float inv = 1.0f / l_tot;
+    const float inv = 1.0f / lacc[0];  // every row of the ones product holds the sum
     uint16_t* dst = a.out + (((int64_t)sq.off[b] + my_i) * g.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
