@@ -16,13 +16,18 @@
 //     2^(7 + 1.75) < 448 with the reference mu moved whenever a tile max
 //     exceeds it by more than 1.75; weights down to 2^-16 stay representable);
 //   * O^T += V^T P^T with the V scale as the instruction's A scale, and the
-//     weights' sum l from the same rounded weights through one more matrix
-//     instruction with an all-ones A operand, so that the output is exactly a
-//     convex combination of V rows (and the vector ALUs, which bound this
-//     kernel, are spared 31 adds per tile).
+//     weights' sum l from the same rounded weights through one more (16x16x128)
+//     matrix instruction whose A operand selects each query's weights, so
+//     that the output is exactly a convex combination of V rows (and the
+//     vector ALUs are spared 31 adds per tile).
 // v_mfma_scale_f32_32x32x64_f8f6f4: 32x32 outputs per 64-deep contraction,
 // the C layout of the bf16 32x32 instructions; per 64-key tile a wave issues
 // 4 (D = 128) QK and 4 PV instructions instead of 16 + 16 bf16 ones.
+// Three waves per SIMD (at most 168 VGPRs at D = 128): the MFMA C operand
+// that carries 7 - mu and the row-sum selector are built right before use,
+// so that neither stays live across the tile loop.  A third wave hides more
+// of each wave's dependency stalls (MFMA results, LDS reads, the end-of-tile
+// barrier) than the software pipelining within a wave that was tried.
 //
 // Tiles (64 keys, D bytes per row) go global -> LDS directly (16 bytes per
 // lane), double-buffered in four distinct LDS objects.  Operand reads:
@@ -49,6 +54,7 @@ namespace {
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef int i32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
@@ -86,7 +92,7 @@ __device__ __forceinline__ uint32_t pack4_in_range(float a, float b, float c, fl
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs sq, Fp8Args a) {
+__global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs sq, Fp8Args a) {
   constexpr int TILE = kBN * D;           // bytes of a K or V tile
   __shared__ __attribute__((aligned(16))) char lds_k0[TILE];
   __shared__ __attribute__((aligned(16))) char lds_v0[TILE];
@@ -211,15 +217,18 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  f32x16_t lacc;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) lacc[r] = 0.f;
-  const i32x8_t ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
+  // Row sums through v_mfma_scale_f32_16x16x128_f8f6f4 with the weights as
+  // its B operand: lane l holds column l % 16 and contraction group l / 16,
+  // so groups 0 and 2 carry query l % 16 (both halves of the keys) and
+  // groups 1 and 3 query l % 16 + 16.  A row 0 of ones over groups 0, 2 and
+  // a row 1 of ones over groups 1, 3 give the two queries' sums in
+  // registers 0 and 1 of lanes 0..15.
+  f32x4_t lacc = {0.f, 0.f, 0.f, 0.f};
+  const int sel_row = lane & 15, sel_grp = (lane >> 4) & 1;
+  const int one_w = (sel_row == sel_grp && sel_row < 2) ? 0x38383838 : 0;  // e4m3 1.0
+
   float m_run = -INFINITY, mu = 0.f, thr = -INFINITY;
-  f32x16_t negm;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) negm[r] = kPOffset;
+  float negm_s = kPOffset;
 
   auto compute_tile = [&](int kt, auto cur_c) __attribute__((always_inline)) {
     constexpr int cur = decltype(cur_c)::value;
@@ -232,6 +241,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
     const bool live = bhi >= blo && k0 <= bhi;
     if (live) {
       f32x16_t sacc[2];
+      f32x16_t negm;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[r] = negm_s;
 #pragma unroll
       for (int c = 0; c < KS; ++c)
 #pragma unroll
@@ -265,8 +277,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
         m_run = m_new;
         mu = mu_new;
         thr = m_new == -INFINITY ? -INFINITY : kSlack;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) lacc[r] *= alpha;
+        {  // lane c < 16 holds the sums of queries c (register 0) and c + 16 (register 1)
+          const float alpha_hi = __shfl(alpha, (lane & 15) + 16);
+          lacc[0] *= alpha;
+          lacc[1] *= alpha_hi;
+        }
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -275,8 +290,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) sacc[kb2][r] -= delta;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) negm[r] = kPOffset - mu;
+        negm_s = kPOffset - mu;
       }
       // weights 2^(s - mu + 7) as the B operand of O^T += V^T P^T: byte
       // j = 16 kb2 + r holds register r of block kb2
@@ -289,7 +303,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
           const float p2 = exp2_fast(sacc[kb2][4 * w4 + 2]), p3 = exp2_fast(sacc[kb2][4 * w4 + 3]);
           pb[4 * kb2 + w4] = (int)pack4_in_range(p0, p1, p2, p3);
         }
-      lacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb, lacc, 0, 0, 0, 127, 0, 127);
+      {
+        const i32x8_t ones = {one_w, one_w, one_w, one_w, one_w, one_w, one_w, one_w};
+        lacc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ones, pb, lacc, 0, 0, 0, 127, 0, 127);
+      }
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         i32x8_t va;
@@ -315,8 +332,11 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_fp8_kernel(Geom g, Seqs s
   }
 
   // ---- normalise and store this lane's query row
+  // query col's sum: register (col >= 16) of lane col % 16
+  const float l_a = __shfl(lacc[0], col & 15), l_b = __shfl(lacc[1], col & 15);
+  const float l_tot = col < 16 ? l_a : l_b;
   if (my_i <= i_hi) {
-    const float inv = 1.0f / lacc[0];  // every row of the ones product holds the sum
+    const float inv = 1.0f / l_tot;
     uint16_t* dst = a.out + (((int64_t)sq.off[b] + my_i) * g.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
