@@ -199,3 +199,78 @@ def test_fp8_first_token_decode():
     q, k, v = qkv(1, 5, 4, 2, 64, 95, "cuda")
     cache = new_cache_fp8(1, 4, 2, 64, 8, 2, 4, mask)
     run_fp8(cache, q, k, v, mask, [], 5, 1.0, 1.0, "empty")
+
+
+def test_fp8_paged_chunked_prefill_and_decode():
+    """fp8 rows in pages (P = 512): chunked prefill across page boundaries (the
+    fp8 prefill looks up the page of every 64-row tile), then decode steps
+    that open new pages; codes read back through the page table."""
+    require_gpu()
+    _say("paged chunked")
+    mask = [1, 0, 1, 1]
+    t = 1700
+    q, k, v = qkv(2, t, 8, 4, 128, 96, "cuda")
+    cache = new_cache_fp8(2, 8, 4, 128, t, 4, 64, mask, page_tokens=512, num_pages=8)
+    run_fp8(cache, q, k, v, mask, [[700, 300], [600, 1000], [380, 390]], 6, 1.0, 1.0, "paged")
+
+
+def test_fp8_paged_equals_contiguous():
+    """The same calls into a paged and a contiguous fp8 cache give bitwise
+    equal prefill outputs and stored codes."""
+    require_gpu()
+    _say("paged == contiguous")
+    mask = [1, 1, 0, 1]
+    t = 2600
+    q, k, v = qkv(2, t, 16, 4, 128, 97, "cuda")
+    chunks = [[1500, 900], [1100, 1700]]
+    paged = new_cache_fp8(2, 16, 4, 128, t, 64, 256, mask, page_tokens=1024, num_pages=6)
+    flat = new_cache_fp8(2, 16, 4, 128, t, 64, 256, mask)
+    op, _, _ = run_sequence(paged, q, k, v, chunks, 0)
+    fp, _, _ = run_sequence(flat, q, k, v, chunks, 0)
+    assert torch.equal(op.view(torch.int16), fp.view(torch.int16))
+    a, b = duo.cache_views(paged), duo.cache_views(flat)
+    for name in ("rk", "rv"):  # the paged view holds whole pages: compare the stored rows
+        assert torch.equal(a[name][:, :, :t], b[name][:, :, :t]), name
+
+
+def test_fp8_varlen_equals_padded():
+    """Packed rows with cu_seqlens into an fp8 cache give the padded call's
+    prefill outputs and cache bit for bit (including an empty sequence)."""
+    require_gpu()
+    _say("varlen == padded")
+    mask = [0, 1, 1, 0]
+    lens = [300, 0, 1029, 64]
+    b_n, c = 4, max(lens)
+    q, k, v = qkv(b_n, c, 8, 4, 128, 98, "cuda")
+    pad = new_cache_fp8(b_n, 8, 4, 128, 2048, 8, 32, mask)
+    packed = new_cache_fp8(b_n, 8, 4, 128, 2048, 8, 32, mask)
+    out_pad = torch.zeros_like(q)
+    duo.duo_prefill(pad, q, k, v, lens, out_pad)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    qp = torch.cat([q[b, :lens[b]] for b in range(b_n)]).contiguous()
+    kp = torch.cat([k[b, :lens[b]] for b in range(b_n)]).contiguous()
+    vp = torch.cat([v[b, :lens[b]] for b in range(b_n)]).contiguous()
+    out_p = torch.zeros_like(qp)
+    duo.duo_prefill_varlen(packed, qp, kp, vp, cu, out_p)
+    torch.cuda.synchronize()
+    for b in range(b_n):
+        assert torch.equal(out_p[cu[b]:cu[b + 1]].view(torch.int16), out_pad[b, :lens[b]].view(torch.int16)), f"b{b}"
+    a, bb = duo.cache_views(pad), duo.cache_views(packed)
+    for name in ("rk", "rv"):
+        assert torch.equal(a[name], bb[name]), name
+    for name in ("sk", "sv"):
+        assert torch.equal(a[name].view(torch.int16), bb[name].view(torch.int16)), name
+    assert pad.lengths() == packed.lengths() == lens
+    qn, kn, vn = to_np32(q), to_np32(k), to_np32(v)
+    ref = oracle_fp8(qn, kn, vn, mask, 8, 32, {b: list(range(lens[b])) for b in range(b_n)}, 1.0, 1.0)
+    g = 2
+    for b in range(b_n):
+        if lens[b]:
+            got = to_np32(out_p[cu[b]:cu[b + 1]])
+            retr = [h for h in range(8) if mask[h // g]]
+            strm = [h for h in range(8) if not mask[h // g]]
+            vmax = [np.abs(seen_rows_fp8(vn[b, :lens[b], h // g], True, 1.0)).max() for h in retr]
+            assert_fp8_close(got[:, retr], ref[b][:, retr], vmax, f"varlen b{b}")
+            assert_close(got[:, strm], ref[b][:, strm], f"varlen streaming b{b}")
