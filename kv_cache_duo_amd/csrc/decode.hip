@@ -850,7 +850,7 @@ int32_t max_splits_for(int64_t max_len, int32_t slots, int head_chunk) {
   return (int32_t)(s < cap ? s : cap);
 }
 
-DecodePlan plan_decode(const Geom& g, const Seqs& q) {
+DecodePlan plan_decode(const Geom& g, const Seqs& q, int32_t num_cus) {
   DecodePlan p;
   const bool byte_rows = g.kv_int8 || g.kv_fp8;
   p.head_chunk = decode_head_chunk(g.G, byte_rows);
@@ -869,6 +869,21 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q) {
   auto round_pair = [&](int64_t x) { return (x + pair - 1) / pair * pair; };
   int64_t ts = round_pair((total + 2047) / 2048);
   const int min_pairs = byte_rows ? kMinPairsInt8 : kMinPairs;
+  // One query head per work-group: a work-group scores each row it reads
+  // once and keeps 64 KB of loads in flight, as much as one CU's share of
+  // HBM bandwidth needs, so the call gets about one work-group per CU.  More
+  // work-groups only add split records to merge and stretch the end of the
+  // stream (the last claimed pair of a unit runs on a CU shared with other
+  // work-groups); on the 32K MHA layer one per CU beats the ~2000-work-group
+  // rule by 6%.  With several query heads per work-group each row costs
+  // several dot products, and the ~2000-work-group rule stays (the 8-by-128K
+  // GQA batch runs 9% slower at half as many work-groups).
+  if (p.head_chunk == 1 && g.nR > 0) {
+    const int64_t units_r = (int64_t)g.B * g.nR * n_hc;
+    const int64_t wg_s = (int64_t)g.B * g.nS * n_hc;  // about one per streaming unit
+    const int64_t per_unit = ((int64_t)num_cus - wg_s) / units_r;
+    if (per_unit >= 1) ts = round_pair(((int64_t)tmax + per_unit - 1) / per_unit);
+  }
   if (ts < min_pairs * pair) ts = min_pairs * pair;
   const int64_t ts_cap = round_pair(((int64_t)tmax + g.max_splits - 1) / g.max_splits);
   if (ts < ts_cap) ts = ts_cap;

@@ -27,6 +27,7 @@ struct duo_cache {
   // pages of every sequence in position order (host mirror of page_table)
   std::vector<int32_t> free_pages;
   std::vector<std::vector<int32_t>> seq_pages;
+  int32_t num_cus;  // compute units of the current device when the handle was made (decode split planning)
 };
 
 namespace {
@@ -35,6 +36,18 @@ constexpr int64_t kAlign = 256;
 constexpr int64_t kMaxLen = int64_t(1) << 30;
 
 int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Compute units of the current device, or 256 (an MI355X) when no device
+// answers: the count only shapes how decode splits its rows.
+int32_t device_compute_units() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                              hipSuccess || cus <= 0) {
+    (void)hipGetLastError();  // clear the error the query left
+    return 256;
+  }
+  return cus;
+}
 
 bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -202,6 +215,7 @@ duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int6
   if (lengths != nullptr)
     for (int b = 0; b < cfg->batch; ++b) h->len[b] = lengths[b];
   h->buf_words = static_cast<int32_t*>(buf);
+  h->num_cus = device_compute_units();
   h->seq_pages.assign(cfg->batch, {});
   if (h->geom.paged) {
     h->free_pages.resize((size_t)cfg->num_pages);
@@ -454,7 +468,7 @@ duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v,
   if (st != DUO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (take_pages(h, sq, s) != hipSuccess) return DUO_ERR_HIP;
-  const duo::DecodePlan p = duo::plan_decode(h->geom, sq);
+  const duo::DecodePlan p = duo::plan_decode(h->geom, sq, h->num_cus);
   hipError_t e = duo::launch_decode(h->geom, sq, p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                                     static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), s);
   if (e != hipSuccess) return DUO_ERR_HIP;

@@ -106,7 +106,8 @@ struct DecodePlan {
   int32_t splits_s;          // max splits over streaming units
   int32_t head_chunk;        // query heads handled per work-group (divides G)
 };
-DecodePlan plan_decode(const Geom& g, const Seqs& q);
+// num_cus: compute units of the device (work-groups per call are sized to it)
+DecodePlan plan_decode(const Geom& g, const Seqs& q, int32_t num_cus);
 hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p,
                          const uint16_t* qin, const uint16_t* kin, const uint16_t* vin,
                          uint16_t* out, hipStream_t s);
