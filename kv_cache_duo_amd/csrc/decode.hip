@@ -69,6 +69,7 @@ __device__ __forceinline__ float2 load_agent2(const float* p) {  // p 8-byte ali
 
 __device__ __forceinline__ float max_or_zero(float m) { return m == -INFINITY ? 0.f : m; }
 
+
 __device__ __forceinline__ uint4 load_nt(const uint4* p) {
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -327,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   // `rows` - 1 read row rows - 1): a paged retrieval cache keeps a pair in
   // one page; other units are contiguous.
   auto pair_row0 = [&](int base, int rows) __attribute__((always_inline)) -> int64_t {
-    return (retrieval && g.paged) ? retrieval_row0(g, b, idx, min(base, rows - 1)) : unit_row0;
+    return (retrieval && g.paged) ? retrieval_row0_uniform(g, b, idx, min(base, rows - 1)) : unit_row0;
   };
   const uint16_t* nk = a.k + ((int64_t)b * g.Hkv + kvh) * D;
   const uint16_t* nv = a.v + ((int64_t)b * g.Hkv + kvh) * D;

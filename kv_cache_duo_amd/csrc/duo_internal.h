@@ -64,6 +64,23 @@ __device__ __forceinline__ int64_t retrieval_row0(const Geom& g, int b, int idx,
   return ((page * g.nR + idx) << g.page_shift) - ((int64_t)j << g.page_shift);
 }
 
+// The same for arguments that are uniform across the work-group: the
+// page-table entry comes through the scalar cache and is waited for in
+// place.  A vector load there would make its wait also wait for every load
+// the kernel has in flight.  (Page tables are written by earlier launches;
+// each launch starts with the scalar cache invalidated.)
+__device__ __forceinline__ int32_t load_uniform_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ int64_t retrieval_row0_uniform(const Geom& g, int b, int idx, int p_page) {
+  if (!g.paged) return ((int64_t)b * g.nR + idx) * g.max_len;
+  const int j = p_page >> g.page_shift;
+  const int64_t page = load_uniform_i32(g.page_table + (int64_t)b * g.max_pages + j);
+  return ((page * g.nR + idx) << g.page_shift) - ((int64_t)j << g.page_shift);
+}
+
 // KV head of unit u.  Read as a 32-bit word of the kernel argument: for a
 // work-group-uniform u that is a scalar load, where a byte load of the
 // argument would be a vector memory round trip.

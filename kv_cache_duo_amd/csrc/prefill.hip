@@ -315,7 +315,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     const uint16_t* cvr = cv;
     int64_t row0 = 0;
     if (retrieval) {
-      row0 = retrieval_row0(g, b, idx, k0);
+      row0 = retrieval_row0_uniform(g, b, idx, k0);
       ckr = g.rk + row0 * D;
       cvr = g.rv + row0 * D;
     }

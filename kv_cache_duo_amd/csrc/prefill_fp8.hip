@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs s
   const int gV = pch ^ v_swz<D>(r0);
   auto load_tile = [&](int tile, char* kbuf, char* vbuf) __attribute__((always_inline)) {
     const int k0 = tile * kBN;
-    const int64_t row0 = retrieval_row0(g, b, idx, k0);
+    const int64_t row0 = retrieval_row0_uniform(g, b, idx, k0);
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(g.rk) + row0 * D;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(g.rv) + row0 * D;
 #pragma unroll
