@@ -111,7 +111,7 @@ typedef struct duo_config {
   int32_t kv_format;    /* duo_kv_format of the retrieval cache */
   float rope_base;      /* 0: no rotary embedding; > 0: its base (e.g. 10000) */
   int32_t rope_style;   /* duo_rope_style (read when rope_base > 0) */
-  /* Paged retrieval cache (0 = contiguous [B][nR][max_len] rows).  With
+  /* Paged retrieval cache (0 = contiguous rows, see duo_layout).  With
    * page_tokens > 0 the retrieval rows live in a pool of num_pages pages of
    * page_tokens positions each, shared by all sequences; a sequence takes
    * pages as it grows (one page covers page_tokens positions of every
@@ -138,10 +138,14 @@ typedef struct duo_cache duo_cache;
  * KV head k is stored at index head_index[k] among the retrieval heads
  * (in increasing k), likewise for streaming heads.
  *   lengths  int32 [B]                     tokens stored per sequence
- *   rk, rv   bf16  [B][nR][max_len][D]     retrieval cache, row = position
+ *   rk, rv   bf16  [B][nR][max_len][D]     retrieval cache, row = position,
+ *            when max_len <= 1024 (block_tokens = 0); longer contiguous caches
+ *            hold [B][nblk][nR][block_tokens][D] with block_tokens = 1024 and
+ *            nblk = ceil(max_len / 1024): block j of sequence b holds
+ *            positions [1024 j, 1024 (j+1)) of each retrieval head in turn
  *            (DUO_KV_INT8: uint8 codes, DUO_KV_FP8: e4m3 codes, same shape)
- *   rks, rvs fp32  [B][nR][max_len]        DUO_KV_INT8 only: row scales
- *            (offset -1 for DUO_KV_BF16)
+ *   rks, rvs fp32  the rows' scales, same layout without D
+ *            (DUO_KV_INT8 only; offset -1 otherwise)
  *   sk, sv   bf16  [B][nS][sink+recent][D] streaming cache, slot map:
  *            slot(p) = p for p < sink, else sink + (p - sink) mod recent
  *   work     uint32 split counters and fp32 split-K partial results of
@@ -159,6 +163,7 @@ typedef struct duo_layout {
   int64_t page_table_offset;        /* -1 for a contiguous cache */
   int32_t page_tokens, max_pages_per_seq;
   int64_t num_pages;
+  int32_t block_tokens;             /* contiguous cache: 1024 if its rows are blocked, else 0 (also when paged) */
 } duo_layout;
 
 /* Lay out a new, empty cache in `dev_buf`.

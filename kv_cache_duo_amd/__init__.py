@@ -71,6 +71,7 @@ class Layout(ctypes.Structure):
         ("rks_offset", ctypes.c_int64), ("rvs_offset", ctypes.c_int64),
         ("page_table_offset", ctypes.c_int64), ("page_tokens", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int64),
+        ("block_tokens", ctypes.c_int32),
     ]
 
 
@@ -322,7 +323,9 @@ def cache_views(cache: Cache):
     """Typed views of the regions of a cache's device buffer (for tests and
     checkpointing): lengths int32 [B], rk/rv [B,nR,max_len,D] (bf16, or uint8
     codes with rks/rvs fp32 [B,nR,max_len] row scales for DUO_KV_INT8), sk/sv
-    [B,nS,sink+recent,D] as bf16."""
+    [B,nS,sink+recent,D] as bf16.  rk/rv (rks/rvs) are views of the buffer
+    for an unblocked contiguous cache and reordered copies for a blocked or
+    paged one (whose raw regions are *_blocks or *_pool)."""
     cfg, lay, buf = cache.cfg, cache.layout(), cache.buf
     if buf is None:
         raise ValueError("cache has no torch buffer attached")
@@ -356,6 +359,22 @@ def cache_views(cache: Cache):
                 for j, page in enumerate(pages):
                     g[b, :, j * pt:(j + 1) * pt] = pool[page]
             views[name] = g
+    elif lay.block_tokens > 0:
+        # blocked contiguous rows [B][nblk][nR][block][D]: copies reordered to
+        # rk/rv [B, nR, max_len, D] (rks/rvs [B, nR, max_len]); the raw
+        # regions as *_blocks
+        bt = lay.block_tokens
+        nblk = (cfg.max_len + bt - 1) // bt
+        bshape = (cfg.batch, nblk, lay.n_retrieval, bt, d)
+        names = [("rk", lay.rk_offset, bshape, rdt), ("rv", lay.rv_offset, bshape, rdt)]
+        if lay.kv_format == DUO_KV_INT8:
+            names += [("rks", lay.rks_offset, bshape[:4], torch.float32),
+                      ("rvs", lay.rvs_offset, bshape[:4], torch.float32)]
+        for name, off, shape, dt in names:
+            blocks = region(off, shape, dt)
+            views[name + "_blocks"] = blocks
+            flat = blocks.transpose(1, 2).reshape((cfg.batch, lay.n_retrieval, nblk * bt) + tuple(shape[4:]))
+            views[name] = flat[:, :, :cfg.max_len].contiguous()
     else:
         rshape = (cfg.batch, lay.n_retrieval, cfg.max_len, d)
         views["rk"] = region(lay.rk_offset, rshape, rdt)

@@ -322,13 +322,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   const int kvh = kv_head_of_unit(g, retrieval ? idx : g.nR + idx);
   const int64_t unit_rows = retrieval ? g.max_len : (int64_t)g.slots;
   const int64_t unit_row0 = ((int64_t)b * nkind + idx) * unit_rows;  // contiguous rows of the unit
-  uint16_t* ck = (retrieval ? g.rk : g.sk) + unit_row0 * D;          // (streaming units)
-  uint16_t* cv = (retrieval ? g.rv : g.sv) + unit_row0 * D;
   // Row base of the pair of batches starting at row `base` (rows past
-  // `rows` - 1 read row rows - 1): a paged retrieval cache keeps a pair in
-  // one page; other units are contiguous.
+  // `rows` - 1 read row rows - 1): a page or block of the retrieval cache
+  // holds whole pairs; streaming units are contiguous.
   auto pair_row0 = [&](int base, int rows) __attribute__((always_inline)) -> int64_t {
-    return (retrieval && g.paged) ? retrieval_row0_uniform(g, b, idx, min(base, rows - 1)) : unit_row0;
+    return retrieval ? retrieval_row0_uniform(g, b, idx, min(base, rows - 1)) : unit_row0;
   };
   const uint16_t* nk = a.k + ((int64_t)b * g.Hkv + kvh) * D;
   const uint16_t* nv = a.v + ((int64_t)b * g.Hkv + kvh) * D;

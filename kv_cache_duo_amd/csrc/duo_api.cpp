@@ -132,7 +132,12 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   // paged: page table right after the lengths (word indices stay small)
   L->page_table_offset = -1;
   g->paged = c->page_tokens > 0;
-  int64_t pool_rows = (int64_t)g->B * g->max_len;  // retrieval rows per head
+  // retrieval rows per head: max_len per sequence, or whole blocks of
+  // 2^kBlockShift positions when longer than one block
+  const int64_t blk = int64_t(1) << duo::kBlockShift;
+  g->nblk = g->max_len > blk ? (int32_t)((g->max_len + blk - 1) / blk) : 1;
+  L->block_tokens = g->nblk > 1 ? (int32_t)blk : 0;
+  int64_t pool_rows = g->nblk > 1 ? (int64_t)g->B * g->nblk * blk : (int64_t)g->B * g->max_len;
   if (g->paged) {
     int shift = 0;
     while ((1 << shift) < c->page_tokens) ++shift;
@@ -144,6 +149,8 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
     L->page_table_offset = off;
     off = align_up(off + 4 * (int64_t)g->B * g->max_pages);
     pool_rows = c->num_pages * c->page_tokens;
+    g->nblk = 1;
+    L->block_tokens = 0;
   }
   L->work_offset = off;  // merge tickets, then the split records
   g->tickets_per_unit = duo::tickets_per_unit(g->max_splits);

@@ -51,12 +51,31 @@ def test_required_bytes_for_workloads(name):
     req = duo.required_bytes(cfg)
     nr = int(mask.sum())
     ns = w.num_kv_heads - nr
-    kv_bytes = 2 * 2 * w.batch * w.head_dim * (nr * cfg.max_len + ns * (w.sink + w.recent))
+    kv_bytes = 2 * 2 * w.batch * w.head_dim * (nr * _rows(cfg.max_len) + ns * (w.sink + w.recent))
     assert req >= kv_bytes
     # the rest (lengths, tickets, split-K partials, alignment) stays small
     assert req - kv_bytes <= max(64 << 20, kv_bytes // 4)
-    bigger = duo.Config(**{**cfg.__dict__, "max_len": cfg.max_len + 1})
-    assert duo.required_bytes(bigger) >= req + 2 * 2 * w.batch * nr * w.head_dim - 4096
+    for extra in (1, 1024):
+        m = cfg.max_len + extra
+        bigger = duo.Config(**{**cfg.__dict__, "max_len": m})
+        grow = 2 * 2 * w.batch * nr * w.head_dim * (_rows(m) - _rows(cfg.max_len))
+        assert duo.required_bytes(bigger) >= req + grow - 4096
+
+
+def _rows(max_len):
+    """Retrieval rows per (sequence, head) of a contiguous cache: max_len, or
+    whole 1024-position blocks past one block."""
+    return max_len if max_len <= 1024 else -(-max_len // 1024) * 1024
+
+
+def test_blocked_layout_reported():
+    """Contiguous caches longer than 1024 positions report 1024-position
+    blocks; shorter ones and paged ones report none."""
+    assert _attach(_cfg(max_len=1024), [0, 0]).layout().block_tokens == 0
+    lay = _attach(_cfg(max_len=1025), [0, 0]).layout()
+    assert lay.block_tokens == 1024
+    c = _cfg(max_len=5000)
+    assert duo.required_bytes(c) >= 2 * 2 * c.batch * sum(c.kv_head_is_retrieval) * c.head_dim * 5120
 
 
 @pytest.mark.parametrize("kw,status", [
