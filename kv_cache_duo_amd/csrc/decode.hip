@@ -39,8 +39,10 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxMergeRecords = 1024;  // (m, l) pairs the merge stages in LDS
-// pairs of batches per work-group, at least, on average (bf16 rows; int8
-// rows, whose pairs hold twice the rows): measured best on the 32K MHA layer
+// Pairs of batches per work-group, at least, on average (bf16 rows; 8-bit
+// rows, whose pairs hold twice the rows), under the ~2048-work-group rule of
+// plan_decode for work-groups that serve several query heads (a sweep on the
+// 32K MHA layer picked these before that layer moved to one work-group per CU)
 constexpr int kMinPairs = 3, kMinPairsInt8 = 2;
 
 struct DecodeArgs {
