@@ -495,8 +495,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       // two codes) and meet q in v_dot2_f32_f16; q is held in f16 scaled by a
       // power of two (2^(15 - e), amax = m 2^e over the head: no overflow,
       // bf16 values stay exact), and the 1024 + 128 offset comes back as one
-      // per-lane constant -1152 * sum(q).  V: o += (p * scale_v) * b in fp32,
-      // with 128 * sum(p * scale_v) taken off once at the end.
+      // per-lane constant -1152 * sum(q).  V: the same f16 values 1024 + b
+      // meet p * scale_v (fp32) in mixed-precision FMAs (fp32 accumulate),
+      // with 1152 * sum(p * scale_v) taken off once at the end.
       // fp8 (FMT 2): K codes become exact f16 pairs (v_cvt_scalef32_pk_f16_fp8)
       // for the same dot2 with no offset, V codes fp32 values; the two
       // per-tensor scales fold into the score constant and into p.
@@ -601,11 +602,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
             const float p = exp2_fast(s[j][gg] - mu);
             l[gg] += p;
             if constexpr (FMT == 1) {
+              // the codes as the exact f16 values 1024 + b, two per v_perm
+              // (as on the K side), into mixed-precision FMAs with p in
+              // fp32; 1152 * sum(p * scale_v) comes off once at the end
               const float pv = p * r[j].vs;
               cacc[gg] += pv;
 #pragma unroll
-              for (int e = 0; e < 16; ++e)
-                o8[gg][e] = fmaf(pv, (float)((r[j].v[e >> 2] >> (8 * (e & 3))) & 0xffu), o8[gg][e]);
+              for (int e = 0; e < 4; ++e) {
+                const f16x2_t lo = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, r[j].v[e], 0x04010400u));
+                const f16x2_t hi = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, r[j].v[e], 0x04030402u));
+                o8[gg][4 * e] = fmaf(pv, (float)lo.x, o8[gg][4 * e]);
+                o8[gg][4 * e + 1] = fmaf(pv, (float)lo.y, o8[gg][4 * e + 1]);
+                o8[gg][4 * e + 2] = fmaf(pv, (float)hi.x, o8[gg][4 * e + 2]);
+                o8[gg][4 * e + 3] = fmaf(pv, (float)hi.y, o8[gg][4 * e + 3]);
+              }
             } else {
               const float pv = p * g.fp8_scale_v;
 #pragma unroll
@@ -634,7 +644,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 #pragma unroll
         for (int gg = 0; gg < GC; ++gg)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-128.0f, cacc[gg], o8[gg][e]);
+          for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-1152.0f, cacc[gg], o8[gg][e]);
       }
 #pragma unroll
       for (int off = LPR8; off < 64; off <<= 1) {
