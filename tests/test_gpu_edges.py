@@ -1,7 +1,8 @@
 """GPU parity at the limits of the boundary: the largest batch (128
 sequences), the largest number of KV heads (256), calls that add nothing,
-and a cache filled to exactly max_len.  All through the C ABI against the
-fp64 oracle; cache buffers start as NaN bytes."""
+a cache filled to exactly max_len, and caches one position longer than a
+1024-position row block.  All through the C ABI against the fp64 oracle;
+cache buffers start as NaN bytes."""
 
 from __future__ import annotations
 
@@ -10,7 +11,7 @@ import pytest
 import torch
 
 import kv_cache_duo_amd as duo
-from parity_util import assert_close, check_cache_bits, new_cache, oracle_rows, require_gpu, to_np32
+from parity_util import assert_close, check_cache_bits, new_cache, oracle_rows, require_gpu, run_sequence, to_np32
 from workloads import qkv
 
 pytestmark = pytest.mark.gpu
@@ -142,3 +143,35 @@ def test_exactly_full_cache():
     torch.cuda.synchronize()
     assert cache.lengths() == [n] and torch.equal(cache.buf, before)
     check_cache_bits(cache, k, v, mask, [n])
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "int8", "fp8"])
+def test_block_boundary(fmt):
+    """A contiguous cache one position longer than a 1024-position block (two
+    blocks, the second nearly empty): chunked prefill to 1020 rows, then
+    decode steps that cross into the second block; outputs against each
+    format's oracle, cache read back through the reordered views."""
+    require_gpu()
+    _say(f"block boundary {fmt}")
+    mask = [1, 0, 1, 1]
+    t, pre, steps = 1025, 1020, 5
+    q, k, v = qkv(2, t, 8, 4, 128, 86, "cuda")
+    kw = {"bf16": {}, "int8": dict(kv_format=duo.DUO_KV_INT8), "fp8": dict(kv_format=duo.DUO_KV_FP8)}[fmt]
+    cfg = duo.Config(2, 8, 4, 128, t, 4, 32, mask, **kw)
+    cache = duo.duo_cache_init(cfg, torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda"))
+    assert cache.layout().block_tokens == 1024
+    chunks = [[700, 1000], [320, 20]]
+    if fmt == "bf16":
+        outp, outd, done = run_sequence(cache, q, k, v, chunks, steps)
+        qn, kn, vn = to_np32(q), to_np32(k), to_np32(v)
+        ref = oracle_rows(qn, kn, vn, mask, 4, 32, {b: list(range(pre + steps)) for b in range(2)})
+        for b in range(2):
+            assert_close(to_np32(outp[b, :pre]), ref[b][:pre], f"prefill b{b}")
+            assert_close(to_np32(outd[:, b]), ref[b][pre:], f"decode b{b}")
+        check_cache_bits(cache, k, v, mask, done)
+    elif fmt == "int8":
+        from test_gpu_int8 import run_q8
+        run_q8(cache, q, k, v, chunks, steps, mask)
+    else:
+        from test_gpu_fp8 import run_fp8
+        run_fp8(cache, q, k, v, mask, chunks, steps, 1.0, 1.0, "block boundary")
