@@ -180,22 +180,30 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs s
   const int scale_k = 127 + g.fp8_exp_k;       // K tensor scale
   const int scale_v = 127 + g.fp8_exp_v;       // V tensor scale
 
-  // ---- tile loader
+  // ---- tile loader: a lane's byte offsets inside a tile are fixed; the
+  // tile's base address is uniform (scalar registers)
   const int r0 = wave * RPC + lane / CH;
   const int pch = lane % CH;
-  const int gK = pch ^ k_swz<D>(r0);  // rows r0 + j ROWS_J swizzle like r0
-  const int gV = pch ^ v_swz<D>(r0);
+  const uint32_t koff = (uint32_t)(r0 * D + (pch ^ k_swz<D>(r0)) * 16);  // rows r0 + j ROWS_J swizzle like r0
+  const uint32_t voff = (uint32_t)(r0 * D + (pch ^ v_swz<D>(r0)) * 16);
   auto load_tile = [&](int tile, char* kbuf, char* vbuf) __attribute__((always_inline)) {
     const int k0 = tile * kBN;
-    const int64_t row0 = retrieval_row0_uniform(g, b, idx, k0);
+    const int64_t row0 = retrieval_row0_uniform(g, b, idx, k0) + k0;  // row of position k0
     const uint8_t* kb = reinterpret_cast<const uint8_t*>(g.rk) + row0 * D;
     const uint8_t* vb = reinterpret_cast<const uint8_t*>(g.rv) + row0 * D;
+    if (k0 + kBN - 1 <= qmax) {
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int kp = k0 + r0 + j * ROWS_J;
-      const int64_t row = kp <= qmax ? (int64_t)kp : (int64_t)k0;  // past qmax: a stored row of the same page
-      g2l16(kb + row * D + gK * 16, kbuf + (j * kWaves + wave) * 1024);
-      g2l16(vb + row * D + gV * 16, vbuf + (j * kWaves + wave) * 1024);
+      for (int j = 0; j < NJ; ++j) {
+        g2l16(kb + j * ROWS_J * D + koff, kbuf + (j * kWaves + wave) * 1024);
+        g2l16(vb + j * ROWS_J * D + voff, vbuf + (j * kWaves + wave) * 1024);
+      }
+    } else {  // last tile: rows past qmax read the last granule of row qmax instead
+      const uint32_t lim = (uint32_t)(qmax - k0 + 1) * D - 16;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        g2l16(kb + min(koff + j * ROWS_J * D, lim), kbuf + (j * kWaves + wave) * 1024);
+        g2l16(vb + min(voff + j * ROWS_J * D, lim), vbuf + (j * kWaves + wave) * 1024);
+      }
     }
   };
 
