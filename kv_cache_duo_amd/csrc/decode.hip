@@ -452,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   __shared__ int sm_claim[2];
   bool own_new = false;  // this work-group's rows hold the new token
   auto stream_pairs = [&](auto& ka, auto& va, auto& kb, auto& vb, auto&& ld, auto&& pr, int rows, int npr,
-                          auto pair_c, auto iter_c) __attribute__((always_inline)) {
+                          auto pair_c, auto iter_c, auto order_c) __attribute__((always_inline)) {
     constexpr int P = decltype(pair_c)::value, IT = decltype(iter_c)::value;  // rows per pair, per batch
     int base = split * P;
     const int64_t r0 = pair_row0(base, rows);
@@ -470,6 +470,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       const int64_t nr0 = pair_row0(nbase, rows);  // page lookup: in flight while this pair is scored
       pr(ka, va, base);
       ld(ka, va, nbase, nr0);
+      // 8-bit rows: keep these loads ahead of the second batch's work (left
+      // to itself the compiler sinks them below it, and every pair then
+      // waits out its whole load latency)
+      if constexpr (decltype(order_c)::value) __builtin_amdgcn_sched_barrier(0);
       pr(kb, vb, base + IT);
       ld(kb, vb, nbase + IT, nr0);
       own_new = own_new || (new_row >= base && new_row < base + P);
@@ -481,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     if (Tst > 0) {
       uint4 ka[kInFlight], va[kInFlight], kb[kInFlight], vb[kInFlight];
       stream_pairs(ka, va, kb, vb, load, process, Tst, (Tst + PAIR - 1) / PAIR, std::integral_constant<int, PAIR>(),
-                   std::integral_constant<int, ROWS_ITER>());
+                   std::integral_constant<int, ROWS_ITER>(), std::false_type());
     }
   };
   const bool q8 = FMT != 0 && retrieval;  // 8-bit retrieval rows
@@ -634,7 +638,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       if (Tc > 0) {
         Rows8 ra[kInFlight], rb[kInFlight];
         stream_pairs(ra, ra, rb, rb, load8, process8, Tc, (Tc + PAIR8 - 1) / PAIR8,
-                     std::integral_constant<int, PAIR8>(), std::integral_constant<int, ITER8>());
+                     std::integral_constant<int, PAIR8>(), std::integral_constant<int, ITER8>(), std::true_type());
       }
       // merge the row groups of the wave (16 dims per lane), then hand the
       // wave's state to the 8-dims-per-lane layout of the code below: lane
