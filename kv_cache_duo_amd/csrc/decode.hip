@@ -547,17 +547,24 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       auto row_of8 = [&](int base, int j) __attribute__((always_inline)) {
         return base + (j * kWaves + wave) * RPW8 + grp8;
       };
+      // rows of a batch from a uniform base row (the batch's first row, or
+      // the last stored row when the batch starts past it) plus a lane
+      // offset, clamped to the last stored row
+      const int lane_row8 = wave * RPW8 + grp8;
       auto load8 = [&](Rows8 (&r)[kInFlight], Rows8 (&)[kInFlight], int base, int64_t r0) __attribute__((always_inline)) {
-        const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + r0 * D;
-        const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + r0 * D;
+        const int bb = min(base, Tc - 1);
+        const uint8_t* kb = reinterpret_cast<const uint8_t*>(g.rk) + (r0 + bb) * D;
+        const uint8_t* vb = reinterpret_cast<const uint8_t*>(g.rv) + (r0 + bb) * D;
+        const char* ksb = reinterpret_cast<const char*>(g.rks + r0 + bb);
+        const char* vsb = reinterpret_cast<const char*>(g.rvs + r0 + bb);
 #pragma unroll
         for (int j = 0; j < kInFlight; ++j) {
-          const int row = min(row_of8(base, j), Tc - 1);
-          r[j].k = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(ck8 + (int64_t)row * D) + c8);
-          r[j].v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(cv8 + (int64_t)row * D) + c8);
+          const uint32_t rel = (uint32_t)min(lane_row8 + j * (kWaves * RPW8) + (base - bb), Tc - 1 - bb);
+          r[j].k = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kb + (rel * D + c8 * 16)));
+          r[j].v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vb + (rel * D + c8 * 16)));
           if constexpr (FMT == 1) {
-            r[j].ks = g.rks[r0 + row];
-            r[j].vs = g.rvs[r0 + row];
+            r[j].ks = *reinterpret_cast<const float*>(ksb + 4 * rel);
+            r[j].vs = *reinterpret_cast<const float*>(vsb + 4 * rel);
           }
         }
       };
