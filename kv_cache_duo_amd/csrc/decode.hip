@@ -99,6 +99,9 @@ constexpr int merge_lds_bytes() { return kMaxMergeRecords * 8 + kThreads * 8 + 2
 // ticket.  Records of GC*D floats are read as GC*D/2 float2 chunks; KL
 // records are summed in parallel.
 constexpr int kSingleLoads = 36;
+// Units of at most this many splits skip the group counters: their
+// arrivals go straight to the unit's counter.
+constexpr int kDirectArrivals = 32;
 template <int D, int GC>
 constexpr int single_merge_max() {
   return GC * D / 2 > kThreads ? 0 : (kThreads / (GC * D / 2)) * kSingleLoads;
@@ -844,8 +847,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   };
   if constexpr (single_merge_max<D, GC>() > 0) {
     if (ns <= single_merge_max<D, GC>()) {
-      if (ng > 1 && !last_arrival(t_group, gsz)) return;
-      if (!last_arrival(t_unit, ng > 1 ? ng : ns)) return;
+      // a few dozen arrivals go straight to the unit's counter (one atomic
+      // round trip less for the last one)
+      const bool grouped = ns > kDirectArrivals;
+      if (grouped && !last_arrival(t_group, gsz)) return;
+      if (!last_arrival(t_unit, grouped ? ng : ns)) return;
       reset_claims();
       merge_single<D, GC>(g, a, sm_raw, rec_o, rec_ml, ns, b, h0);
       return;
