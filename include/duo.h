@@ -92,7 +92,10 @@ typedef enum duo_kv_format { DUO_KV_BF16 = 0, DUO_KV_INT8 = 1, DUO_KV_FP8 = 2 } 
  * every key is attended through that stored value; q is rotated at its
  * position before the product; V is not rotated.  Angles are formed in fp64
  * and reduced before the fp32 sine and cosine, so positions in the millions
- * keep their accuracy.  Not combined with DUO_KV_INT8 (UNSUPPORTED).
+ * keep their accuracy.  With an 8-bit format the rotated bf16 K row is what
+ * gets encoded; DUO_KV_INT8 still attends the call's own rows through their
+ * (rotated) bf16 values and stored rows through their codes, DUO_KV_FP8 every
+ * retrieval row through its codes.
  *   DUO_ROPE_INTERLEAVED: pair i = dims (2i, 2i+1) (the RoFormer form);
  *   DUO_ROPE_HALF: pair i = dims (i, i + head_dim/2). */
 typedef enum duo_rope_style { DUO_ROPE_INTERLEAVED = 0, DUO_ROPE_HALF = 1 } duo_rope_style;
@@ -177,7 +180,8 @@ typedef struct duo_layout {
  * rope_style not a duo_rope_style, page_tokens not 0 or a power of two in
  * 512..65536, page_tokens > 0 with num_pages < 1, kv_scale_k / kv_scale_v
  * not 0 or a power of two in [2^-32, 2^32]), UNSUPPORTED (head_dim, batch,
- * rope_base > 0 with DUO_KV_INT8 or DUO_KV_FP8), BUFFER_TOO_SMALL, HIP. */
+ * num_kv_heads, max_len or sink + recent beyond the library's limits),
+ * BUFFER_TOO_SMALL, HIP. */
 duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,
                           size_t* required_bytes, duo_cache** out, void* stream);
 

@@ -521,7 +521,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 #pragma unroll
       for (int gg = 0; gg < GC; ++gg) {
         const uint4* src = reinterpret_cast<const uint4*>(a.q + ((int64_t)b * g.Hq + h0 + gg) * D) + 2 * c8;
-        const uint4 x0 = src[0], x1 = src[1];
+        uint4 x0, x1;
+        if (g.rope) {  // the rotated q of the 8-dims-per-lane layout: its chunks 2 c8 and 2 c8 + 1
+          auto from = [&](int src_lane) __attribute__((always_inline)) {
+            return make_uint4((uint32_t)__shfl((int)qw[gg][0], src_lane), (uint32_t)__shfl((int)qw[gg][1], src_lane),
+                              (uint32_t)__shfl((int)qw[gg][2], src_lane), (uint32_t)__shfl((int)qw[gg][3], src_lane));
+          };
+          x0 = from(2 * c8);
+          x1 = from(2 * c8 + 1);
+        } else {
+          x0 = src[0];
+          x1 = src[1];
+        }
         const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
         float amax = 0.f;
 #pragma unroll

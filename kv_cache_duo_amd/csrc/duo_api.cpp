@@ -72,7 +72,6 @@ duo_status check_config(const duo_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return DUO_ERR_UNSUPPORTED;
   if (c->batch > DUO_MAX_BATCH || c->num_kv_heads > duo::kMaxKvHeads) return DUO_ERR_UNSUPPORTED;
   if (c->max_len > kMaxLen || (int64_t)c->sink + c->recent > kMaxLen) return DUO_ERR_UNSUPPORTED;
-  if (c->rope_base > 0.f && c->kv_format != DUO_KV_BF16) return DUO_ERR_UNSUPPORTED;
   if (c->page_tokens != 0) {
     const int32_t p = c->page_tokens;
     if (p < 512 || p > 65536 || (p & (p - 1)) != 0) return DUO_ERR_INVALID_ARG;

@@ -120,11 +120,12 @@ __device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
 // Q8: the retrieval cache holds int8 rows (DUO_KV_INT8) and some sequence
 // has a stored prefix; tiles with stored retrieval rows are then staged
 // through registers and dequantized into the bf16 LDS layout.
-// ROPE: rotary position embedding (never together with Q8).
+// ROPE: rotary position embedding.  With Q8 as well (an int8 cache with
+// rotary embedding, prefix or not) every retrieval tile is staged: stored
+// rows dequantized, the chunk's rows turned to their positions.
 template <int D, bool Q8, bool ROPE>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
-  static_assert(!(Q8 && ROPE), "rotary embedding with an int8 cache is not supported");
   // The K and V tiles of the two pipeline stages are four distinct LDS
   // objects: the compiler then knows that the next tile's direct-to-LDS
   // loads cannot alias the transposing reads of the current one, and does
@@ -301,10 +302,11 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // kst / vst (bit j of q8rows: row j holds codes + scale in .x .y .z).
   // (the retrieval pointers are set per tile: a paged cache keeps a tile's
   // 64 rows in one page)
-  // ROPE: a staged streaming tile's rows wait in kst / vst as bf16 granules
-  // (bit j of q8rows: row j is a chunk row whose K is turned in store_tile).
+  // ROPE: a staged tile's chunk rows wait in kst / vst as bf16 granules
+  // (bit j of rotrows: row j is a chunk row whose K is turned in store_tile).
+  // Both: retrieval tiles mix stored int8 rows and chunk rows to be turned.
   u32x4_t kst[(Q8 || ROPE) ? NJ : 1], vst[(Q8 || ROPE) ? NJ : 1];
-  uint32_t q8rows = 0;
+  uint32_t q8rows = 0, rotrows = 0;
   int st_k0 = 0;  // first key of the staged tile
   auto load_tile = [&](int tile, char* kbuf, char* vbuf) __attribute__((always_inline)) -> bool {  // true: staged, store_tile to follow
     const int k0 = tile * kBN;
@@ -319,7 +321,36 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       ckr = g.rk + row0 * D;
       cvr = g.rv + row0 * D;
     }
-    if constexpr (ROPE) {
+    if constexpr (Q8 && ROPE) {
+      if (retrieval) {
+        // stored rows (kp < L) as int8 codes + scale, the chunk's rows from
+        // the input (turned in store_tile), rows past qmax chunk row 0
+        const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + row0 * D;
+        const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + row0 * D;
+        st_k0 = k0;
+        q8rows = 0;
+        rotrows = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int kp = k0 + r0 + j * ROWS_J;
+          if (kp < L) {
+            const u32x2_t kc = *reinterpret_cast<const u32x2_t*>(ck8 + (int64_t)kp * D + gK * 8);
+            const u32x2_t vc = *reinterpret_cast<const u32x2_t*>(cv8 + (int64_t)kp * D + gV * 8);
+            kst[j] = u32x4_t{kc.x, kc.y, __float_as_uint(g.rks[row0 + kp]), 0u};
+            vst[j] = u32x4_t{vc.x, vc.y, __float_as_uint(g.rvs[row0 + kp]), 0u};
+            q8rows |= 1u << j;
+          } else {
+            const bool in = kp <= qmax;
+            const int64_t off = in ? in_base + (int64_t)(kp - L) * in_stride : in_base;
+            kst[j] = *reinterpret_cast<const u32x4_t*>(a.k + off + gK * 8);
+            vst[j] = *reinterpret_cast<const u32x4_t*>(a.v + off + gV * 8);
+            if (in) rotrows |= 1u << j;
+          }
+        }
+        return true;
+      }
+    }
+    if constexpr (ROPE && !Q8) {
       if (retrieval) {
         // every key row is in the cache (this chunk's rows were stored,
         // rotated, before the kernel); rows past qmax read row 0 instead
@@ -341,9 +372,11 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
         }
         return false;
       }
+    }
+    if constexpr (ROPE) {
       if (k0 + kBN - 1 >= L) {  // a streaming tile with chunk rows: stage it
         st_k0 = k0;
-        q8rows = 0;
+        rotrows = 0;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
           // row_src for a streaming head, written out (a second call of
@@ -357,7 +390,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           const int64_t off = !ok ? in_base : in_chunk ? in_base + (int64_t)(kp - L) * in_stride : cache_row * D;
           kst[j] = *reinterpret_cast<const u32x4_t*>((from_cache ? ck : a.k) + off + gK * 8);
           vst[j] = *reinterpret_cast<const u32x4_t*>((from_cache ? cv : a.v) + off + gV * 8);
-          if (!from_cache && kp >= L && kp <= qmax) q8rows |= 1u << j;
+          if (!from_cache && kp >= L && kp <= qmax) rotrows |= 1u << j;
         }
         return true;
       }
@@ -436,9 +469,10 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
         rope_angles8<D>(st_k0 + r0 + j * ROWS_J, gK, g.rope_half, g.rope_rho, cs, sn);
         const uint4 x = make_uint4(kst[j].x, kst[j].y, kst[j].z, kst[j].w);
         const uint4 r = rope_apply8<CH>(x, cs, sn, g.rope_half, gK);
-        const u32x4_t kr = ((q8rows >> j) & 1u) ? u32x4_t{r.x, r.y, r.z, r.w} : kst[j];
-        *reinterpret_cast<u32x4_t*>(dst + j * kWaves * 1024) = kr;
-        *reinterpret_cast<u32x4_t*>(vdst + j * kWaves * 1024) = vst[j];
+        const u32x4_t kr = ((rotrows >> j) & 1u) ? u32x4_t{r.x, r.y, r.z, r.w} : kst[j];
+        const bool q8 = Q8 && ((q8rows >> j) & 1u);
+        *reinterpret_cast<u32x4_t*>(dst + j * kWaves * 1024) = granule(kr, q8);
+        *reinterpret_cast<u32x4_t*>(vdst + j * kWaves * 1024) = granule(vst[j], q8);
       }
       return;
     }
@@ -627,10 +661,15 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   if (g.kv_fp8) {  // retrieval heads on fp8 matrix cores, streaming heads here
     hipError_t e = launch_prefill_fp8(g, q, qin, max_n, out, s);
     if (e != hipSuccess) return e;
+    if (g.rope)
+      return g.D == 128 ? launch_t<128, false, true>(g, q, a, max_n, s, true)
+                        : launch_t<64, false, true>(g, q, a, max_n, s, true);
     return g.D == 128 ? launch_t<128, false, false>(g, q, a, max_n, s, true)
                       : launch_t<64, false, false>(g, q, a, max_n, s, true);
   }
-  if (g.rope)  // never with an 8-bit cache (rejected by the configuration check)
+  if (g.rope && g.kv_int8 && g.nR > 0)  // stored rows as int8, the chunk's rows turned from the input
+    return g.D == 128 ? launch_t<128, true, true>(g, q, a, max_n, s) : launch_t<64, true, true>(g, q, a, max_n, s);
+  if (g.rope)
     return g.D == 128 ? launch_t<128, false, true>(g, q, a, max_n, s) : launch_t<64, false, true>(g, q, a, max_n, s);
   if (g.kv_int8 && g.nR > 0 && prefix)
     return g.D == 128 ? launch_t<128, true, false>(g, q, a, max_n, s) : launch_t<64, true, false>(g, q, a, max_n, s);

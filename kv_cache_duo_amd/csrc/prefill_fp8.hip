@@ -146,22 +146,70 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs s
   const int ntiles = qmax / kBN + 1;
 
   // ---- Q operand (B of S^T = K Q^T): query `col`, dims 64c + 32 half + 0..31
+  // (rotated to the query's position first with rotary embedding)
   i32x8_t qreg[KS];
   int eq = 0;
   {
     const bool ok = my_i <= i_hi;
     const uint4* src = reinterpret_cast<const uint4*>(a.q + (((int64_t)sq.off[b] + (ok ? my_i : i_lo)) * g.Hq + h) * D);
-    uint4 x[KS][4];
-    float amax = 0.f;
+    float x[KS][4][8];  // x[c][u]: dims 64c + 32 half + 8u + 0..7, the row's 8-dim chunk 8c + 4 half + u
 #pragma unroll
     for (int c = 0; c < KS; ++c)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        x[c][u] = src[(64 * c + 32 * half) / 8 + u];
-        const uint32_t w[4] = {x[c][u].x, x[c][u].y, x[c][u].z, x[c][u].w};
+        const uint4 t = src[(64 * c + 32 * half) / 8 + u];
+        const uint32_t w[4] = {t.x, t.y, t.z, t.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fmaxf(fabsf(bf16_lo(w[e])), fabsf(bf16_hi(w[e]))));
+        for (int e = 0; e < 4; ++e) {
+          x[c][u][2 * e] = bf16_lo(w[e]);
+          x[c][u][2 * e + 1] = bf16_hi(w[e]);
+        }
       }
+    if (g.rope) {
+      float cs[8], sn[8];
+      if (!g.rope_half) {  // pairs (2i, 2i + 1) inside a chunk
+#pragma unroll
+        for (int c = 0; c < KS; ++c)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            rope_angles8<D>(my_q, 8 * c + 4 * half + u, false, g.rope_rho, cs, sn);
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+              const float p0 = x[c][u][e], p1 = x[c][u][e + 1];
+              x[c][u][e] = fmaf(p0, cs[e], -p1 * sn[e]);
+              x[c][u][e + 1] = fmaf(p0, sn[e], p1 * cs[e]);
+            }
+          }
+      } else if constexpr (KS >= 2) {  // pairs (d, d + D/2): c = 0 with c = 1 (D = 128), same lane
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          rope_angles8<D>(my_q, 4 * half + u, true, g.rope_rho, cs, sn);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float p0 = x[0][u][e], p1 = x[1][u][e];
+            x[0][u][e] = fmaf(p0, cs[e], -p1 * sn[e]);
+            x[1][u][e] = fmaf(p0, sn[e], p1 * cs[e]);
+          }
+        }
+      } else {  // D = 64: pairs (d, d + 32) join the two halves, lanes l and l ^ 32
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          rope_angles8<D>(my_q, 4 * half + u, true, g.rope_rho, cs, sn);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float mine = x[0][u][e], other = __shfl_xor(mine, 32);
+            x[0][u][e] = half == 0 ? fmaf(mine, cs[e], -other * sn[e]) : fmaf(other, sn[e], mine * cs[e]);
+          }
+        }
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int c = 0; c < KS; ++c)
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(x[c][u][e]));
     amax = fmaxf(amax, __shfl_xor(amax, 32)) * g.scale_log2;  // the whole row (both halves)
     if (amax > 0.f) frexpf(amax * (1.0f / 448.0f), &eq);      // amax 2^-eq in [224, 448)
     eq = min(max(eq, -126), 127);                              // an E8M0 scale byte (255 is NaN)
@@ -170,10 +218,9 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs s
     for (int c = 0; c < KS; ++c)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t w[4] = {x[c][u].x, x[c][u].y, x[c][u].z, x[c][u].w};
-        qreg[c][2 * u] = (int)fp8_pack4(bf16_lo(w[0]) * s, bf16_hi(w[0]) * s, bf16_lo(w[1]) * s, bf16_hi(w[1]) * s);
-        qreg[c][2 * u + 1] =
-            (int)fp8_pack4(bf16_lo(w[2]) * s, bf16_hi(w[2]) * s, bf16_lo(w[3]) * s, bf16_hi(w[3]) * s);
+        const float* y = x[c][u];
+        qreg[c][2 * u] = (int)fp8_pack4(y[0] * s, y[1] * s, y[2] * s, y[3] * s);
+        qreg[c][2 * u + 1] = (int)fp8_pack4(y[4] * s, y[5] * s, y[6] * s, y[7] * s);
       }
   }
   const int scale_q = 127 + eq;                // E8M0: 2^eq back onto the query column

@@ -93,7 +93,6 @@ def test_blocked_layout_reported():
     (dict(rope_base=-1.0), duo.DUO_ERR_INVALID_ARG),
     (dict(rope_base=float("inf")), duo.DUO_ERR_INVALID_ARG),
     (dict(rope_base=10000.0, rope_style=2), duo.DUO_ERR_INVALID_ARG),
-    (dict(rope_base=10000.0, kv_format=1), duo.DUO_ERR_UNSUPPORTED),  # rotary + int8 cache
     (dict(page_tokens=256, num_pages=8), duo.DUO_ERR_INVALID_ARG),     # pages below 512 positions
     (dict(page_tokens=1000, num_pages=8), duo.DUO_ERR_INVALID_ARG),    # not a power of two
     (dict(page_tokens=131072, num_pages=8), duo.DUO_ERR_INVALID_ARG),  # above 65536
@@ -194,12 +193,18 @@ def test_fp8_layout():
     (dict(kv_format=2, kv_scale_v=-2.0), duo.DUO_ERR_INVALID_ARG),
     (dict(kv_format=2, kv_scale_k=float("inf")), duo.DUO_ERR_INVALID_ARG),
     (dict(kv_format=2, kv_scale_k=2.0 ** 40), duo.DUO_ERR_INVALID_ARG),       # outside [2^-32, 2^32]
-    (dict(kv_format=2, rope_base=10000.0), duo.DUO_ERR_UNSUPPORTED),          # rotary + fp8 cache
 ])
 def test_fp8_invalid_configs(kw, status):
     with pytest.raises(duo.DuoError) as e:
         duo.required_bytes(_cfg(**kw))
     assert e.value.status == status
+
+
+@pytest.mark.parametrize("fmt", [duo.DUO_KV_INT8, duo.DUO_KV_FP8])
+def test_rope_with_8bit_formats_needs_no_extra_bytes(fmt):
+    plain = duo.required_bytes(_cfg(kv_format=fmt))
+    for style in (duo.DUO_ROPE_INTERLEAVED, duo.DUO_ROPE_HALF):
+        assert duo.required_bytes(_cfg(kv_format=fmt, rope_base=10000.0, rope_style=style)) == plain
 
 
 def test_fp8_scale_zero_means_one():
