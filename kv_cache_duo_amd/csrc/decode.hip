@@ -27,7 +27,6 @@
 // and the new K row are turned to position L once, in the prologue, and the
 // new token is scored outside the row loop (by work-group 0 of the unit).
 #include <cfloat>
-#include <cstdlib>
 #include <type_traits>
 
 #include "device_util.h"
@@ -926,11 +925,6 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q, int32_t num_cus) {
   if (ts < min_pairs * pair) ts = min_pairs * pair;
   const int64_t ts_cap = round_pair(((int64_t)tmax + g.max_splits - 1) / g.max_splits);
   if (ts < ts_cap) ts = ts_cap;
-  static const int64_t env_ts = [] {
-    const char* e = getenv("DUO_DECODE_SPLIT_TOKENS");
-    return e ? (int64_t)atoll(e) : (int64_t)0;
-  }();
-  if (env_ts > 0 && env_ts % pair == 0 && env_ts >= ts_cap) ts = env_ts;
   p.split_tokens = (int32_t)ts;
   p.splits_r = (int32_t)((tmax + ts - 1) / ts);
   const int32_t smax = tmax < g.slots ? tmax : g.slots;
