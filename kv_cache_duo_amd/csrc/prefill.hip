@@ -463,10 +463,22 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     if constexpr (ROPE) {
       // chunk K rows turned to their positions (every lane takes part: the
       // half-split pairs exchange values across lanes)
+      // the angles of row r0 from fp64 turns; rows r0 + j ROWS_J by complex
+      // multiplication with the angles of ROWS_J positions (NJ - 1 fp32
+      // steps, a few 1e-7 on cos and sin, far below the bf16 rounding of K)
+      float cs[8], sn[8], cd[8], sd[8];
+      rope_angles8<D>(st_k0 + r0, gK, g.rope_half, g.rope_rho, cs, sn);
+      if constexpr (NJ > 1) rope_angles8<D>(ROWS_J, gK, g.rope_half, g.rope_rho, cd, sd);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        float cs[8], sn[8];
-        rope_angles8<D>(st_k0 + r0 + j * ROWS_J, gK, g.rope_half, g.rope_rho, cs, sn);
+        if (j > 0) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float c2 = fmaf(cs[e], cd[e], -sn[e] * sd[e]);
+            sn[e] = fmaf(sn[e], cd[e], cs[e] * sd[e]);
+            cs[e] = c2;
+          }
+        }
         const uint4 x = make_uint4(kst[j].x, kst[j].y, kst[j].z, kst[j].w);
         const uint4 r = rope_apply8<CH>(x, cs, sn, g.rope_half, gK);
         const u32x4_t kr = ((rotrows >> j) & 1u) ? u32x4_t{r.x, r.y, r.z, r.w} : kst[j];
