@@ -69,7 +69,7 @@ __device__ __forceinline__ int64_t retrieval_row0(const Geom& g, int b, int idx,
   if (!g.paged) {
     if (g.nblk == 1) return ((int64_t)b * g.nR + idx) * g.max_len;
     const int j = p_page >> kBlockShift;  // blocked contiguous layout: blocks of sequence b in order
-    return (((int64_t)b * g.nblk + j) * g.nR + idx << kBlockShift) - ((int64_t)j << kBlockShift);
+    return ((((int64_t)b * g.nblk + j) * g.nR + idx) << kBlockShift) - ((int64_t)j << kBlockShift);
   }
   const int j = p_page >> g.page_shift;
   const int64_t page = g.page_table[(int64_t)b * g.max_pages + j];
