@@ -1,7 +1,8 @@
 """GPU parity at the limits of the boundary: the largest batch (128
 sequences), the largest number of KV heads (256), calls that add nothing,
-a cache filled to exactly max_len, and caches one position longer than a
-1024-position row block.  All through the C ABI against the fp64 oracle;
+a cache filled to exactly max_len, caches one position longer than a
+1024-position row block, and decode at the split count where the merge's
+arrival counting changes.  All through the C ABI against the fp64 oracle;
 cache buffers start as NaN bytes."""
 
 from __future__ import annotations
@@ -175,3 +176,29 @@ def test_block_boundary(fmt):
     else:
         from test_gpu_fp8 import run_fp8
         run_fp8(cache, q, k, v, mask, chunks, steps, 1.0, 1.0, "block boundary")
+
+
+@pytest.mark.parametrize("stored", [12287, 12288])
+def test_decode_split_count_boundary(stored):
+    """One retrieval and one streaming KV head: decode splits a unit's rows
+    into ~384-row pieces, so 12288 and 12289 rows give 32 and 33 work-groups
+    on a 256-CU device: the last arrival counts on the unit's counter alone
+    at 32, through the group counters at 33.  Three steps cross from one
+    side to the other and back into a fresh call."""
+    require_gpu()
+    _say(f"split-count boundary, {stored} stored rows")
+    mask = [1, 0]
+    steps = 3
+    t = stored + steps
+    q, k, v = qkv(1, t, 2, 2, 128, 83, "cuda")
+    cache = new_cache(1, 2, 2, 128, t, 64, 256, mask)
+    duo.duo_cache_append(cache, k[:, :stored].contiguous(), v[:, :stored].contiguous(), [stored])
+    qn, kn, vn = to_np32(q), to_np32(k), to_np32(v)
+    for s in range(steps):
+        p = stored + s
+        o1 = torch.empty(1, 2, 128, dtype=torch.bfloat16, device="cuda")
+        duo.duo_decode(cache, q[:, p].contiguous(), k[:, p].contiguous(), v[:, p].contiguous(), o1)
+        ref = oracle_rows(qn, kn, vn, mask, 64, 256, {0: [p]})[0]
+        assert_close(to_np32(o1), ref, f"decode at {p}")
+    torch.cuda.synchronize()
+    check_cache_bits(cache, k, v, mask, [t])
