@@ -449,12 +449,15 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   auto store_tile = [&](char* kbuf, char* vbuf) __attribute__((always_inline)) {
     auto granule = [&](const u32x4_t& x, bool q8) __attribute__((always_inline)) -> u32x4_t {
       if (!q8) return x;
+      // (b - 128) sc as one fma of b, sc and -128 sc (exact): the same
+      // single rounding as the product
       const float sc = __uint_as_float(x.z);
+      const float off = -128.0f * sc;
       uint32_t w[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint32_t cw = x[e >> 1] >> (16 * (e & 1));
-        w[e] = pack_bf16x2(((float)(cw & 0xffu) - 128.0f) * sc, ((float)((cw >> 8) & 0xffu) - 128.0f) * sc);
+        w[e] = pack_bf16x2(fmaf((float)(cw & 0xffu), sc, off), fmaf((float)((cw >> 8) & 0xffu), sc, off));
       }
       return u32x4_t{w[0], w[1], w[2], w[3]};
     };
