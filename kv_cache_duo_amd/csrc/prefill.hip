@@ -134,6 +134,9 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_v0[Lds<D>::TILE];
   __shared__ __attribute__((aligned(16))) char lds_k1[Lds<D>::TILE];
   __shared__ __attribute__((aligned(16))) char lds_v1[Lds<D>::TILE];
+  // ROPE: cos (first D) and sin (next D) of the turn of the ROWS_J positions
+  // between the rows a lane stages, per dim
+  __shared__ __attribute__((aligned(16))) float lds_step[ROPE ? 2 * D : 4];
   using LD = Lds<D>;
   constexpr int CH = D / 8;                 // 16-byte granules per row
   constexpr int RPC = 64 / CH;              // rows per 1 KB wave load (4 or 8)
@@ -471,7 +474,13 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       // steps, a few 1e-7 on cos and sin, far below the bf16 rounding of K)
       float cs[8], sn[8], cd[8], sd[8];
       rope_angles8<D>(st_k0 + r0, gK, g.rope_half, g.rope_rho, cs, sn);
-      if constexpr (NJ > 1) rope_angles8<D>(ROWS_J, gK, g.rope_half, g.rope_rho, cd, sd);
+      if constexpr (NJ > 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          cd[e] = lds_step[8 * gK + e];
+          sd[e] = lds_step[D + 8 * gK + e];
+        }
+      }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         if (j > 0) {
@@ -615,6 +624,18 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     __syncthreads();
   };
 
+  if constexpr (ROPE && NJ > 1) {  // the turn of ROWS_J positions, per dim: the same for every staged tile
+    if (threadIdx.x < D / 8) {
+      float cs[8], sn[8];
+      rope_angles8<D>(ROWS_J, threadIdx.x, g.rope_half, g.rope_rho, cs, sn);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        lds_step[8 * threadIdx.x + e] = cs[e];
+        lds_step[D + 8 * threadIdx.x + e] = sn[e];
+      }
+    }
+    __syncthreads();
+  }
   if (load_tile(tile_of(0), lds_k0, lds_v0)) store_tile(lds_k0, lds_v0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
