@@ -281,3 +281,62 @@ def test_rope_8bit_first_token_decode(fmt):
     cache = new_cache(fmt, 1, 4, 2, 64, 8, 2, 4, mask, INTERLEAVED)
     run = run_int8 if fmt == duo.DUO_KV_INT8 else run_fp8
     run(cache, q, k, v, mask, [], 6, INTERLEAVED)
+
+
+@pytest.mark.parametrize("fmt", [duo.DUO_KV_INT8, duo.DUO_KV_FP8])
+def test_rope_8bit_paged_varlen_equals_padded(fmt):
+    """Rotary embedding, an 8-bit paged cache and a stored prefix together:
+    a packed (cu_seqlens) prefill gives the padded call's outputs and cache
+    bytes bit for bit, and both match the oracle."""
+    require_gpu()
+    _say(f"paged varlen == padded fmt={fmt}")
+    mask = [1, 0, 1, 1]
+    b_n = 3
+    pre, lens = [700, 0, 90], [300, 520, 0]
+    t = max(p + n for p, n in zip(pre, lens))
+    q, k, v = qkv(b_n, t, 8, 4, 64, 67, "cuda")
+
+    def fresh():
+        return new_cache(fmt, b_n, 8, 4, 64, t, 8, 32, mask, HALF, page_tokens=512, num_pages=b_n * 2)
+
+    pad, packed = fresh(), fresh()
+    for cache in (pad, packed):
+        duo.duo_cache_append(cache, k[:, :max(pre)].contiguous(), v[:, :max(pre)].contiguous(), pre)
+    c = max(lens)
+    qc, kc, vc = (torch.zeros(b_n, c, x.shape[2], 64, dtype=torch.bfloat16, device="cuda") for x in (q, k, v))
+    for b in range(b_n):
+        qc[b, :lens[b]], kc[b, :lens[b]], vc[b, :lens[b]] = (x[b, pre[b]:pre[b] + lens[b]] for x in (q, k, v))
+    out_pad = torch.zeros_like(qc)
+    duo.duo_prefill(pad, qc, kc, vc, lens, out_pad)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    qp, kp, vp = (torch.cat([x[b, :lens[b]] for b in range(b_n)]).contiguous() for x in (qc, kc, vc))
+    out_p = torch.zeros_like(qp)
+    duo.duo_prefill_varlen(packed, qp, kp, vp, cu, out_p)
+    torch.cuda.synchronize()
+    for b in range(b_n):
+        assert torch.equal(out_p[cu[b]:cu[b + 1]].view(torch.int16), out_pad[b, :lens[b]].view(torch.int16)), f"b{b}"
+    va, vb_ = duo.cache_views(pad), duo.cache_views(packed)
+    names = ("rk", "rv", "sk", "sv") + (("rks", "rvs") if fmt == duo.DUO_KV_INT8 else ())
+    for name in names:
+        assert torch.equal(va[name].view(torch.uint8), vb_[name].view(torch.uint8)), name
+    done = [pre[b] + lens[b] for b in range(b_n)]
+    assert pad.lengths() == packed.lengths() == done
+    qn, kn, vn = to_np32(q), to_np32(k), to_np32(v)
+    rows = {b: list(range(pre[b], done[b])) for b in range(b_n)}
+    ref = oracle(fmt, qn, kn, vn, mask, 8, 32, rows, pre, BASE, HALF)
+    g = 2
+    for b in range(b_n):
+        if not lens[b]:
+            continue
+        got = to_np32(out_p[cu[b]:cu[b + 1]])
+        if fmt == duo.DUO_KV_INT8:
+            assert_close(got, ref[b], f"int8 varlen b{b}")
+        else:
+            retr = [h for h in range(8) if mask[h // g]]
+            strm = [h for h in range(8) if not mask[h // g]]
+            vmax = [np.abs(seen_rows_fp8(vn[b, :done[b], h // g], True, 1.0)).max() for h in retr]
+            assert_fp8_close(got[:, retr], ref[b][:, retr], vmax, f"fp8 varlen b{b}")
+            assert_close(got[:, strm], ref[b][:, strm], f"fp8 varlen streaming b{b}")
+    check_cache(packed, fmt, k, v, mask, done, BASE, HALF)
