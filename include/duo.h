@@ -34,7 +34,13 @@
  *     Calls only enqueue work on it and never synchronise; DUO_OK means the
  *     work was enqueued.  Results are visible after the caller synchronises.
  *   - All arguments are validated before anything is enqueued; a call that
- *     returns an error leaves the device buffer and the handle unchanged.
+ *     returns a validation error (INVALID_ARG, UNSUPPORTED, BUFFER_TOO_SMALL,
+ *     CAPACITY) leaves the device buffer and the handle unchanged.  A call
+ *     that returns DUO_ERR_HIP (a launch failed) leaves the handle unchanged
+ *     -- stored lengths, and in a paged cache every page's owner -- but
+ *     kernels launched before the failing one may have written device memory
+ *     that no stored length covers (rows past a sequence's length, page-table
+ *     entries of pages it does not hold); nothing a later call reads.
  *   - A handle is not thread-safe; use one stream per handle, calls in order.
  *   - No exception crosses the ABI and nothing aborts.
  */

@@ -101,12 +101,31 @@ _SIGNATURES = {
 _lib = None
 
 
+def _check_build_record() -> None:
+    """Refuse a libduo.so built from other sources than the ones in the tree
+    (the build writes a digest of its sources beside the library)."""
+    import json
+
+    from kv_cache_duo_amd.build import BUILD_RECORD, source_digest
+    try:
+        with open(BUILD_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        raise RuntimeError(f"{LIB_PATH} has no build record ({BUILD_RECORD}): rebuild with "
+                           "`python -m kv_cache_duo_amd.build`") from None
+    if rec.get("sources_sha256") != source_digest():
+        raise RuntimeError(f"{LIB_PATH} was built from other sources than kv_cache_duo_amd/csrc and "
+                           "include/duo.h hold now: rebuild with `python -m kv_cache_duo_amd.build`")
+
+
 def load_library() -> ctypes.CDLL:
-    """Load libduo.so (built by ``kv_cache_duo_amd.build``); raise if absent."""
+    """Load libduo.so (built by ``kv_cache_duo_amd.build``); raise if it is
+    absent or stale."""
     global _lib
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is not built: run `python -m kv_cache_duo_amd.build`")
+        _check_build_record()
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             fn = getattr(lib, name)

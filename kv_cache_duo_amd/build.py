@@ -36,6 +36,26 @@ COMMON = [
 ]
 
 
+# What a built library was made from: written beside libduo.so by build(),
+# checked by the binding before it loads the library.
+BUILD_RECORD = os.path.join(HERE, "libduo.build.json")
+
+
+def source_digest() -> str:
+    """sha256 over the library's sources, its headers and the compile flags."""
+    import hashlib
+    h = hashlib.sha256()
+    h.update(" ".join(COMMON).encode())
+    names = sorted(SOURCES + [f for f in os.listdir(CSRC) if f.endswith(".h")])
+    for name in names:
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    with open(os.path.join(INCLUDE, "duo.h"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()
+
+
 def hipcc() -> str:
     rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
     path = os.path.join(rocm, "bin", "hipcc")
@@ -67,6 +87,10 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
+    import json
+    with open(BUILD_RECORD + ".tmp", "w") as f:
+        json.dump({"sources_sha256": source_digest(), "arch": ARCH}, f)
+    os.replace(BUILD_RECORD + ".tmp", BUILD_RECORD)
     cmd = [hipcc(), *COMMON, "-x", "hip", os.path.join(CSRC, "ceiling.hip"), "-o", CEILING + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -5,7 +5,9 @@
 // synthetic data (sourcepulse card, "How It Works"); here they are an input.
 // Retrieval KV heads get a full contiguous cache, streaming KV heads a
 // constant-length sink + ring cache (DuoAttention abstract).  Every check
-// runs before anything is enqueued, so a failing call changes nothing.
+// runs before anything is enqueued, so a call that fails validation changes
+// nothing; a call whose launch fails (DUO_ERR_HIP) keeps the handle's
+// lengths and pages as they were.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -294,7 +296,34 @@ duo_status check_pages(const duo_cache* h, const duo::Seqs& sq) {
   return need <= (int64_t)h->free_pages.size() ? DUO_OK : DUO_ERR_CAPACITY;
 }
 
+// Page ownership before a call, to undo take_pages when a later launch of
+// the same call fails: the handle then keeps its pages and lengths.
+struct PageMark {
+  std::vector<size_t> held;  // seq_pages[b].size() before the call
+};
+PageMark mark_pages(const duo_cache* h) {
+  PageMark m;
+  if (h->geom.paged) {
+    m.held.resize(h->seq_pages.size());
+    for (size_t b = 0; b < h->seq_pages.size(); ++b) m.held[b] = h->seq_pages[b].size();
+  }
+  return m;
+}
+// Give back the pages taken since `m`, restoring the free list's order
+// (take_pages popped them from its back in sequence order).
+void rollback_pages(duo_cache* h, const PageMark& m) {
+  if (!h->geom.paged) return;
+  for (size_t b = h->seq_pages.size(); b-- > 0;)
+    while (h->seq_pages[b].size() > m.held[b]) {
+      h->free_pages.push_back(h->seq_pages[b].back());
+      h->seq_pages[b].pop_back();
+    }
+}
+
 // Take the pages (check_pages passed) and enqueue the page-table writes.
+// On a failed launch the caller rolls the host state back (rollback_pages);
+// table entries already written name positions past the stored lengths,
+// whose entries are unspecified.
 hipError_t take_pages(duo_cache* h, const duo::Seqs& sq, hipStream_t s) {
   if (!h->geom.paged) return hipSuccess;
   const int64_t p = h->cfg.page_tokens;
@@ -325,10 +354,14 @@ duo_status append_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const v
   duo_status st = check_pages(h, sq);
   if (st != DUO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (take_pages(h, sq, s) != hipSuccess) return DUO_ERR_HIP;
-  hipError_t e = duo::launch_append(h->geom, sq, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v),
-                                    max_n, s);
-  if (e != hipSuccess) return DUO_ERR_HIP;
+  const PageMark mark = mark_pages(h);
+  hipError_t e = take_pages(h, sq, s);
+  if (e == hipSuccess)
+    e = duo::launch_append(h->geom, sq, static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), max_n, s);
+  if (e != hipSuccess) {
+    rollback_pages(h, mark);
+    return DUO_ERR_HIP;
+  }
   for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += sq.n[b];
   return DUO_OK;
 }
@@ -339,7 +372,12 @@ duo_status prefill_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const 
   duo_status st = check_pages(h, sq);
   if (st != DUO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (take_pages(h, sq, s) != hipSuccess) return DUO_ERR_HIP;
+  const PageMark mark = mark_pages(h);
+  hipError_t e = take_pages(h, sq, s);
+  if (e != hipSuccess) {
+    rollback_pages(h, mark);
+    return DUO_ERR_HIP;
+  }
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   // Streaming heads read ring slots that this chunk's append overwrites, so
@@ -349,17 +387,18 @@ duo_status prefill_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const 
   // as they load them.
   // An fp8 cache stores the retrieval rows first as well: its prefill reads
   // every retrieval key and value as stored.
-  hipError_t e = hipSuccess;
   const bool store_first = h->geom.rope || h->geom.kv_fp8;
-  if (store_first) {
-    e = duo::launch_append(h->geom, sq, kk, vv, max_n, s, duo::kAppendRetrieval);
-    if (e != hipSuccess) return DUO_ERR_HIP;
+  if (store_first) e = duo::launch_append(h->geom, sq, kk, vv, max_n, s, duo::kAppendRetrieval);
+  if (e == hipSuccess)
+    e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), kk, vv, max_n, static_cast<uint16_t*>(out),
+                            s);
+  if (e == hipSuccess)
+    e = duo::launch_append(h->geom, sq, kk, vv, max_n, s,
+                           store_first ? duo::kAppendStreaming : duo::kAppendRetrieval | duo::kAppendStreaming);
+  if (e != hipSuccess) {
+    rollback_pages(h, mark);
+    return DUO_ERR_HIP;
   }
-  e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), kk, vv, max_n, static_cast<uint16_t*>(out), s);
-  if (e != hipSuccess) return DUO_ERR_HIP;
-  e = duo::launch_append(h->geom, sq, kk, vv, max_n, s,
-                         store_first ? duo::kAppendStreaming : duo::kAppendRetrieval | duo::kAppendStreaming);
-  if (e != hipSuccess) return DUO_ERR_HIP;
   for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += sq.n[b];
   return DUO_OK;
 }
@@ -473,11 +512,17 @@ duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v,
   duo_status st = check_pages(h, sq);
   if (st != DUO_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (take_pages(h, sq, s) != hipSuccess) return DUO_ERR_HIP;
-  const duo::DecodePlan p = duo::plan_decode(h->geom, sq, h->num_cus);
-  hipError_t e = duo::launch_decode(h->geom, sq, p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                                    static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), s);
-  if (e != hipSuccess) return DUO_ERR_HIP;
+  const PageMark mark = mark_pages(h);
+  hipError_t e = take_pages(h, sq, s);
+  if (e == hipSuccess) {
+    const duo::DecodePlan p = duo::plan_decode(h->geom, sq, h->num_cus);
+    e = duo::launch_decode(h->geom, sq, p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), s);
+  }
+  if (e != hipSuccess) {
+    rollback_pages(h, mark);
+    return DUO_ERR_HIP;
+  }
   for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += 1;
   return DUO_OK;
 }

@@ -351,3 +351,43 @@ def test_release_checks_its_arguments():
     assert lib.duo_cache_release(None, 0, None) == duo.DUO_ERR_INVALID_ARG
     assert lib.duo_cache_release(c.handle, 2, None) == duo.DUO_ERR_INVALID_ARG
     assert lib.duo_cache_release(c.handle, -1, None) == duo.DUO_ERR_INVALID_ARG
+
+
+def test_failed_launch_keeps_pages_and_lengths():
+    """A call whose kernel launch fails (DUO_ERR_HIP) gives back the pages it
+    took and keeps every length.  Forced from the host: on a machine without
+    a HIP device every launch fails, so the call gets past validation and
+    fails at its first launch (the page-table write).  Where a device exists
+    the launch would really write through the fake buffer address, so the
+    test only runs without one."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("needs a host without a HIP device (every launch must fail)")
+    lib = duo.load_library()
+    cfg = _cfg(max_len=4096, page_tokens=512, num_pages=8)
+    c = _attach(cfg, [0, 0])
+    before = [c.pages(b) for b in range(cfg.batch)]
+    n = (ctypes.c_int32 * 2)(600, 100)
+    fake = ctypes.c_void_p(FAKE)
+    assert lib.duo_cache_append(c.handle, fake, fake, n, 600, None) == duo.DUO_ERR_HIP
+    assert lib.duo_prefill(c.handle, fake, fake, fake, n, 600, fake, None) == duo.DUO_ERR_HIP
+    assert lib.duo_decode(c.handle, fake, fake, fake, fake, None) == duo.DUO_ERR_HIP
+    assert [c.pages(b) for b in range(cfg.batch)] == before == [([], 8), ([], 8)]
+    assert c.lengths() == [0, 0]
+
+
+def test_stale_library_is_refused(tmp_path, monkeypatch):
+    """load_library() checks the digest the build recorded against the
+    sources in the tree and refuses a library built from other sources."""
+    import json
+
+    import kv_cache_duo_amd.build as b
+    rec = tmp_path / "libduo.build.json"
+    rec.write_text(json.dumps({"sources_sha256": "0" * 64, "arch": "gfx950"}))
+    monkeypatch.setattr(b, "BUILD_RECORD", str(rec))
+    monkeypatch.setattr(duo, "_lib", None)
+    with pytest.raises(RuntimeError, match="other sources"):
+        duo.load_library()
+    monkeypatch.setattr(b, "BUILD_RECORD", str(tmp_path / "missing.json"))
+    with pytest.raises(RuntimeError, match="no build record"):
+        duo.load_library()

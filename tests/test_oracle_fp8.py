@@ -70,3 +70,17 @@ def test_scaled_rows_and_seen_values():
         assert np.array_equal(seen_rows_fp8(x, False, scale), x)
     with pytest.raises(ValueError):
         quantize_rows_fp8(x, 0.3)
+
+
+def test_golden_scaled_codes_and_seen_values():
+    """Hand-derived scaled cases (tests/golden/e4m3.json, scaled_cases): the
+    code of x / scale and the stored value code * scale, through every
+    scaled entry of the oracle.  A scale applied in the wrong direction, or
+    not at all on decode, fails them."""
+    for c in GOLDEN["scaled_cases"]:
+        x, scale, code, seen = c["x"], c["scale"], int(c["code"], 16), c["seen"]
+        got = quantize_rows_fp8(np.array([[x]]), scale)
+        assert int(got[0, 0]) == code, (c, hex(int(got[0, 0])))
+        assert dequantize_rows_fp8(np.array([[code]], dtype=np.uint8), scale)[0, 0] == seen, c
+        assert seen_rows_fp8(np.array([[x]]), True, scale)[0, 0] == seen, c
+        assert seen_rows_fp8(np.array([[x]]), False, scale)[0, 0] == x, c
