@@ -26,7 +26,10 @@ from typing import Sequence
 import torch  # noqa: F401  -- load torch's HIP runtime before libduo.so binds to it
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libduo.so")
+# DUO_LIBRARY names another build of the same sources (the host-sanitized
+# one of kv_cache_duo_amd.build.build_host_sanitized); default: the in-tree
+# library.
+LIB_PATH = os.environ.get("DUO_LIBRARY") or os.path.join(_HERE, "libduo.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "duo.h")
 
 DUO_OK = 0
@@ -106,12 +109,13 @@ def _check_build_record() -> None:
     (the build writes a digest of its sources beside the library)."""
     import json
 
-    from kv_cache_duo_amd.build import BUILD_RECORD, source_digest
+    from kv_cache_duo_amd.build import RECORD_NAME, source_digest
+    record = os.path.join(os.path.dirname(LIB_PATH), RECORD_NAME)
     try:
-        with open(BUILD_RECORD) as f:
+        with open(record) as f:
             rec = json.load(f)
     except (OSError, ValueError):
-        raise RuntimeError(f"{LIB_PATH} has no build record ({BUILD_RECORD}): rebuild with "
+        raise RuntimeError(f"{LIB_PATH} has no build record ({record}): rebuild with "
                            "`python -m kv_cache_duo_amd.build`") from None
     if rec.get("sources_sha256") != source_digest():
         raise RuntimeError(f"{LIB_PATH} was built from other sources than kv_cache_duo_amd/csrc and "

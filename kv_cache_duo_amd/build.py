@@ -38,7 +38,8 @@ COMMON = [
 
 # What a built library was made from: written beside libduo.so by build(),
 # checked by the binding before it loads the library.
-BUILD_RECORD = os.path.join(HERE, "libduo.build.json")
+RECORD_NAME = "libduo.build.json"
+BUILD_RECORD = os.path.join(HERE, RECORD_NAME)
 
 
 def source_digest() -> str:
@@ -54,6 +55,13 @@ def source_digest() -> str:
     with open(os.path.join(INCLUDE, "duo.h"), "rb") as f:
         h.update(f.read())
     return h.hexdigest()
+
+
+def write_record(path: str) -> None:
+    import json
+    with open(path + ".tmp", "w") as f:
+        json.dump({"sources_sha256": source_digest(), "arch": ARCH}, f)
+    os.replace(path + ".tmp", path)
 
 
 def hipcc() -> str:
@@ -87,10 +95,7 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
-    import json
-    with open(BUILD_RECORD + ".tmp", "w") as f:
-        json.dump({"sources_sha256": source_digest(), "arch": ARCH}, f)
-    os.replace(BUILD_RECORD + ".tmp", BUILD_RECORD)
+    write_record(BUILD_RECORD)
     cmd = [hipcc(), *COMMON, "-x", "hip", os.path.join(CSRC, "ceiling.hip"), "-o", CEILING + ".tmp"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -99,6 +104,46 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB} and {CEILING}")
     return LIB
+
+
+def sanitizer_runtime() -> str:
+    """The compiler's AddressSanitizer runtime (it carries the
+    UndefinedBehaviorSanitizer handlers too), to preload into a process that
+    loads a sanitized host library."""
+    import glob
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    found = sorted(glob.glob(os.path.join(rocm, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    if not found:
+        raise RuntimeError("clang AddressSanitizer runtime not found under ROCM_PATH")
+    return found[-1]
+
+
+def build_host_sanitized(out_dir: str) -> str:
+    """libduo.so with its host code (duo_api.cpp: validation, layout, page
+    bookkeeping) built with AddressSanitizer and UndefinedBehaviorSanitizer.
+    Device code is not instrumented (each -fsanitize= applies to the host
+    pass only); the kernels' objects come from the last build().  Load it
+    with sanitizer_runtime() preloaded.  Returns the library's path."""
+    os.makedirs(out_dir, exist_ok=True)
+    objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES if s != "duo_api.cpp"]
+    if not all(os.path.exists(o) for o in objs):
+        build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    flags = [f for f in COMMON if f != "-O3"]
+    api = os.path.join(out_dir, "duo_api_san.o")
+    cmd = [hipcc(), *flags, "-O1", "-g", *san, "-x", "hip", "-c", os.path.join(CSRC, "duo_api.cpp"), "-o", api]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized host build:\n{' '.join(cmd)}\n{r.stderr}")
+    lib = os.path.join(out_dir, "libduo.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *san, api, *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed for the sanitized host build:\n{' '.join(cmd)}\n{r.stderr}")
+    write_record(os.path.join(out_dir, RECORD_NAME))
+    return lib
 
 
 if __name__ == "__main__":

@@ -381,13 +381,12 @@ def test_stale_library_is_refused(tmp_path, monkeypatch):
     sources in the tree and refuses a library built from other sources."""
     import json
 
-    import kv_cache_duo_amd.build as b
-    rec = tmp_path / "libduo.build.json"
-    rec.write_text(json.dumps({"sources_sha256": "0" * 64, "arch": "gfx950"}))
-    monkeypatch.setattr(b, "BUILD_RECORD", str(rec))
+    lib = tmp_path / "libduo.so"
+    lib.write_bytes(b"not loaded: the record is checked first")
+    monkeypatch.setattr(duo, "LIB_PATH", str(lib))
     monkeypatch.setattr(duo, "_lib", None)
-    with pytest.raises(RuntimeError, match="other sources"):
-        duo.load_library()
-    monkeypatch.setattr(b, "BUILD_RECORD", str(tmp_path / "missing.json"))
     with pytest.raises(RuntimeError, match="no build record"):
+        duo.load_library()
+    (tmp_path / "libduo.build.json").write_text(json.dumps({"sources_sha256": "0" * 64, "arch": "gfx950"}))
+    with pytest.raises(RuntimeError, match="other sources"):
         duo.load_library()
