@@ -81,12 +81,35 @@ typedef enum duo_status {
  *     (duo_config.kv_scale_k / kv_scale_v): code = e4m3(x / scale), which
  *     clamps to [-448, 448] and rounds to nearest even.  Every row a call
  *     attends to -- its own new rows included, which are stored first -- is
- *     seen through code * scale.  Retrieval heads' prefill then runs on fp8
- *     matrix cores: q is rounded to e4m3 (with a power-of-two scale per
- *     query row) and the softmax weights too, so its results carry fp8
- *     rounding (about 2^-4 per element) beyond the stored K and V.
+ *     seen through code * scale.  How retrieval heads' prefill computes over
+ *     those values is duo_fp8_prefill.
  * Streaming heads' caches are bf16 in every format. */
 typedef enum duo_kv_format { DUO_KV_BF16 = 0, DUO_KV_INT8 = 1, DUO_KV_FP8 = 2 } duo_kv_format;
+
+/* Retrieval heads' prefill over a DUO_KV_FP8 cache.
+ *   DUO_FP8_PREFILL_EXACT: every stored e4m3 value times its power-of-two
+ *     scale is decoded to bf16 -- exactly: an e4m3 value has 4 significant
+ *     bits -- and the products run on the bf16 matrix cores, so the only
+ *     rounding beyond the stored K and V is that of the bf16 path (q, the
+ *     softmax weights, the output).
+ *   DUO_FP8_PREFILL_MFMA: the products run on the fp8 matrix cores at twice
+ *     the bf16 rate; q is rounded to e4m3 (with a power-of-two scale per
+ *     query row) and the softmax weights too, so results carry fp8 rounding
+ *     (up to 2^-4 relative per rounded element) beyond the stored K and V. */
+typedef enum duo_fp8_prefill { DUO_FP8_PREFILL_EXACT = 0, DUO_FP8_PREFILL_MFMA = 1 } duo_fp8_prefill;
+
+/* How a decode call splits a retrieval head's rows over work-groups.
+ *   DUO_DECODE_STATIC: work-group s of a (sequence, KV head) takes the fixed
+ *     row batches s, s + n, s + 2n, ... (n work-groups), and the partial
+ *     results are merged in work-group order: two runs on the same inputs
+ *     give bitwise equal outputs.
+ *   DUO_DECODE_DYNAMIC: after its first batch a work-group claims the next
+ *     unclaimed one from a counter, so work-groups that get less memory
+ *     bandwidth take fewer rows; which work-group sums which rows, and so
+ *     the fp32 summation order, then depends on timing, and two runs may
+ *     differ in the last bits (within the fp32 rounding of the softmax sums,
+ *     a few units of the bf16 output's last place at most). */
+typedef enum duo_decode_split { DUO_DECODE_STATIC = 0, DUO_DECODE_DYNAMIC = 1 } duo_decode_split;
 
 /* Rotary position embedding applied inside the library (RoFormer, cited in
  * the reference list of the pith.science review page), when
@@ -132,6 +155,8 @@ typedef struct duo_config {
   /* DUO_KV_FP8: the K and V scales, powers of two in [2^-32, 2^32]; 0 = 1 */
   float kv_scale_k;
   float kv_scale_v;
+  int32_t fp8_prefill;  /* duo_fp8_prefill (read with DUO_KV_FP8) */
+  int32_t decode_split; /* duo_decode_split */
 } duo_config;
 
 /* Opaque host-side handle: configuration, head maps, region offsets and the
@@ -173,6 +198,9 @@ typedef struct duo_layout {
   int32_t page_tokens, max_pages_per_seq;
   int64_t num_pages;
   int32_t block_tokens;             /* contiguous cache: 1024 if its rows are blocked, else 0 (also when paged) */
+  int64_t work_records_offset;      /* decoding's split-K partial results, up to work_offset + work_bytes
+                                       (written by a decode call before it reads them; their contents
+                                       between calls are unspecified) */
 } duo_layout;
 
 /* Lay out a new, empty cache in `dev_buf`.
@@ -185,7 +213,8 @@ typedef struct duo_layout {
  * finite, kv_format not a duo_kv_format, rope_base < 0 or not finite,
  * rope_style not a duo_rope_style, page_tokens not 0 or a power of two in
  * 512..65536, page_tokens > 0 with num_pages < 1, kv_scale_k / kv_scale_v
- * not 0 or a power of two in [2^-32, 2^32]), UNSUPPORTED (head_dim, batch,
+ * not 0 or a power of two in [2^-32, 2^32], fp8_prefill not a
+ * duo_fp8_prefill, decode_split not a duo_decode_split), UNSUPPORTED (head_dim, batch,
  * num_kv_heads, max_len or sink + recent beyond the library's limits),
  * BUFFER_TOO_SMALL, HIP. */
 duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,

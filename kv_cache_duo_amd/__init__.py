@@ -43,6 +43,8 @@ DUO_MAX_BATCH = 128
 
 DUO_KV_BF16, DUO_KV_INT8, DUO_KV_FP8 = 0, 1, 2
 DUO_ROPE_INTERLEAVED, DUO_ROPE_HALF = 0, 1
+DUO_FP8_PREFILL_EXACT, DUO_FP8_PREFILL_MFMA = 0, 1
+DUO_DECODE_STATIC, DUO_DECODE_DYNAMIC = 0, 1
 
 
 class DuoError(RuntimeError):
@@ -60,6 +62,7 @@ class _Config(ctypes.Structure):
         ("kv_format", ctypes.c_int32), ("rope_base", ctypes.c_float), ("rope_style", ctypes.c_int32),
         ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int64),
         ("kv_scale_k", ctypes.c_float), ("kv_scale_v", ctypes.c_float),
+        ("fp8_prefill", ctypes.c_int32), ("decode_split", ctypes.c_int32),
     ]
 
 
@@ -74,7 +77,7 @@ class Layout(ctypes.Structure):
         ("rks_offset", ctypes.c_int64), ("rvs_offset", ctypes.c_int64),
         ("page_table_offset", ctypes.c_int64), ("page_tokens", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int64),
-        ("block_tokens", ctypes.c_int32),
+        ("block_tokens", ctypes.c_int32), ("work_records_offset", ctypes.c_int64),
     ]
 
 
@@ -174,6 +177,8 @@ class Config:
     num_pages: int = 0      # paged: pages in the pool
     kv_scale_k: float = 0.0  # DUO_KV_FP8: power-of-two K scale (0 = 1)
     kv_scale_v: float = 0.0  # DUO_KV_FP8: power-of-two V scale (0 = 1)
+    fp8_prefill: int = 0     # DUO_FP8_PREFILL_EXACT (bf16 matrix cores) or DUO_FP8_PREFILL_MFMA (fp8 ones)
+    decode_split: int = 0    # DUO_DECODE_STATIC (bitwise reproducible) or DUO_DECODE_DYNAMIC
 
     def _c(self):
         mask = (ctypes.c_uint8 * max(len(self.kv_head_is_retrieval), 1))(
@@ -181,7 +186,8 @@ class Config:
         c = _Config(self.batch, self.num_q_heads, self.num_kv_heads, self.head_dim, self.max_len,
                     self.sink, self.recent, self.scale,
                     ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)), self.kv_format, self.rope_base,
-                    self.rope_style, self.page_tokens, self.num_pages, self.kv_scale_k, self.kv_scale_v)
+                    self.rope_style, self.page_tokens, self.num_pages, self.kv_scale_k, self.kv_scale_v,
+                    self.fp8_prefill, self.decode_split)
         return c, mask  # keep the mask alive for the call
 
 

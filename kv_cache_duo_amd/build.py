@@ -46,7 +46,7 @@ def source_digest() -> str:
     """sha256 over the library's sources, its headers and the compile flags."""
     import hashlib
     h = hashlib.sha256()
-    h.update(" ".join(COMMON).encode())
+    h.update(" ".join(f for f in COMMON if not f.startswith("-I")).encode())  # paths differ between machines
     names = sorted(SOURCES + [f for f in os.listdir(CSRC) if f.endswith(".h")])
     for name in names:
         h.update(name.encode())

@@ -9,8 +9,13 @@
 // its rows are the cache rows (retrieval: positions 0..L; streaming: the
 // min(L+1, sink+recent) occupied slots), cut into pairs of batches.  Every
 // unit gets ns work-groups.  Work-group `split` of a unit takes pair `split`
-// first, then claims further pairs from the unit's counter (one claim
-// ahead of use), so work-groups that get less bandwidth take fewer rows.
+// first.  With the static split (the default) it then takes pairs split +
+// ns, split + 2 ns, ...: which rows a work-group sums, and in what order, is
+// fixed, and the records are merged in work-group order, so outputs are
+// bitwise reproducible.  With the dynamic split it claims further pairs
+// from the unit's counter (one claim ahead of use), so work-groups that get
+// less bandwidth take fewer rows, at the price of a timing-dependent fp32
+// summation order.
 // The new token's row is read from the input and stored to the cache by the
 // work-group whose pair holds it; no other work-group reads that row.  Each
 // work-group streams its rows with coalesced 16-byte loads (a row of D bf16
@@ -338,15 +343,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   const int64_t pu = ((int64_t)b * g.Hkv + kvh) * n_hc + hc;
   uint32_t* t_unit = g.tickets + pu * g.tickets_per_unit;  // line 0: arrivals, line 1: pair claims
   uint32_t* t_claim = t_unit + kTicketStride;
-  // Wave 0 claims for the work-group: lane 0 adds 1, the other lanes 0, so
-  // lane 0's value is the claim however the lanes' atomics are combined.
-  // The claim for the second pair goes out before anything else.
-  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  // Dynamic split: thread 0 claims for the work-group, one atomic per pair;
+  // the claim for the second pair goes out before anything else.
   auto claim = [&]() {
     return __hip_atomic_fetch_add(t_claim, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   uint32_t claimed = 0;
-  if (threadIdx.x == 0) claimed = claim();
+  const bool dynamic = g.decode_dynamic != 0;
+  if (dynamic && threadIdx.x == 0) claimed = claim();
 
   // ---- queries of the GC heads: this lane's 8 dims of each
   uint32_t qw[GC][4];
@@ -444,29 +448,36 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     }
   };
 
-  // ---- stream the pairs: pair `split`, then claimed pairs ns, ns+1, ...
-  // While a pair's two batches are processed, the next pair's loads go out
-  // batch by batch, and the claim for the pair after it is in flight.  The
-  // claim reaches the other waves through a double-buffered LDS slot (one
-  // barrier per pair).  `rows` bounds the streamed rows, `npr` the pairs;
-  // past the last pair the loads re-read the last row (cached):
-  // unconditional loads keep the outstanding-load count static.
+  // ---- stream the pairs: pair `split`, then (static split) pairs
+  // split + ns, split + 2 ns, ..., or (dynamic split) claimed pairs ns,
+  // ns+1, ...  While a pair's two batches are processed, the next pair's
+  // loads go out batch by batch.  A dynamic claim for the pair after it is
+  // in flight meanwhile and reaches the other waves through a
+  // double-buffered LDS slot (one barrier per pair).  `rows` bounds the
+  // streamed rows, `npr` the pairs; past the last pair the loads re-read the
+  // last row (cached): unconditional loads keep the outstanding-load count
+  // static.
   __shared__ int sm_claim[2];
   bool own_new = false;  // this work-group's rows hold the new token
   auto stream_pairs = [&](auto& ka, auto& va, auto& kb, auto& vb, auto&& ld, auto&& pr, int rows, int npr,
                           auto pair_c, auto iter_c, auto order_c) __attribute__((always_inline)) {
     constexpr int P = decltype(pair_c)::value, IT = decltype(iter_c)::value;  // rows per pair, per batch
     int base = split * P;
+    int pair = split;
     const int64_t r0 = pair_row0(base, rows);
     ld(ka, va, base, r0);
     ld(kb, vb, base + IT, r0);
     for (int it = 0;; it ^= 1) {
-      if (threadIdx.x == 0) {
-        sm_claim[it] = ns + (int)claimed;
-        claimed = claim();
+      int p_next = pair + ns;
+      if (dynamic) {
+        if (threadIdx.x == 0) {
+          sm_claim[it] = ns + (int)claimed;
+          claimed = claim();
+        }
+        __syncthreads();
+        p_next = __builtin_amdgcn_readfirstlane(sm_claim[it]);
       }
-      __syncthreads();
-      const int p_next = __builtin_amdgcn_readfirstlane(sm_claim[it]);
+      pair = p_next;
       const bool more = p_next < npr;
       const int nbase = more ? p_next * P : rows;
       const int64_t nr0 = pair_row0(nbase, rows);  // page lookup: in flight while this pair is scored
@@ -823,7 +834,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     }
   }
   if (ns == 1) {  // the only claimer of this unit
-    if (threadIdx.x == 0) __hip_atomic_store(t_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dynamic && threadIdx.x == 0) __hip_atomic_store(t_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
@@ -853,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
     return sm_flag != 0;
   };
   auto reset_claims = [&]() {
-    if (threadIdx.x == 0) __hip_atomic_store(t_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (dynamic && threadIdx.x == 0) __hip_atomic_store(t_claim, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   if constexpr (single_merge_max<D, GC>() > 0) {
     if (ns <= single_merge_max<D, GC>()) {

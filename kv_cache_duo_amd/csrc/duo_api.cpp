@@ -68,6 +68,8 @@ duo_status check_config(const duo_config* c) {
     if (!std::isfinite(sc) || !(sc > 0.f) || std::frexp(sc, &e) != 0.5f || e - 1 < -32 || e - 1 > 32)
       return DUO_ERR_INVALID_ARG;
   }
+  if (c->fp8_prefill != DUO_FP8_PREFILL_EXACT && c->fp8_prefill != DUO_FP8_PREFILL_MFMA) return DUO_ERR_INVALID_ARG;
+  if (c->decode_split != DUO_DECODE_STATIC && c->decode_split != DUO_DECODE_DYNAMIC) return DUO_ERR_INVALID_ARG;
   if (!(c->rope_base >= 0.f) || !std::isfinite(c->rope_base)) return DUO_ERR_INVALID_ARG;
   if (c->rope_base > 0.f && c->rope_style != DUO_ROPE_INTERLEAVED && c->rope_style != DUO_ROPE_HALF)
     return DUO_ERR_INVALID_ARG;
@@ -108,6 +110,8 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   g->nS = ns;
   g->kv_int8 = c->kv_format == DUO_KV_INT8;
   g->kv_fp8 = c->kv_format == DUO_KV_FP8;
+  g->fp8_mfma = g->kv_fp8 && c->fp8_prefill == DUO_FP8_PREFILL_MFMA;
+  g->decode_dynamic = c->decode_split == DUO_DECODE_DYNAMIC;
   {
     const float sk = c->kv_scale_k > 0.f ? c->kv_scale_k : 1.f, sv = c->kv_scale_v > 0.f ? c->kv_scale_v : 1.f;
     int ek = 0, ev = 0;
@@ -156,6 +160,7 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   L->work_offset = off;  // merge tickets, then the split records
   g->tickets_per_unit = duo::tickets_per_unit(g->max_splits);
   off = align_up(off + 4 * units * g->tickets_per_unit);
+  L->work_records_offset = off;
   off = align_up(off + 4 * units * g->max_splits * gc * (g->D + 2));
   L->work_bytes = off - L->work_offset;
   const int64_t row = 2 * (int64_t)g->D;
@@ -184,10 +189,9 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
 
 void bind_device(duo::Geom* g, const duo_layout& L, void* buf) {
   char* base = static_cast<char*>(buf);
-  const int64_t units = (int64_t)g->B * g->Hkv * (g->G / duo::decode_head_chunk(g->G, g->kv_int8 || g->kv_fp8));
   g->lengths = reinterpret_cast<int32_t*>(base + L.lengths_offset);
   g->tickets = reinterpret_cast<uint32_t*>(base + L.work_offset);
-  g->partials = reinterpret_cast<float*>(base + align_up(L.work_offset + 4 * units * g->tickets_per_unit));
+  g->partials = reinterpret_cast<float*>(base + L.work_records_offset);
   g->rk = reinterpret_cast<uint16_t*>(base + L.rk_offset);
   g->rv = reinterpret_cast<uint16_t*>(base + L.rv_offset);
   g->rks = L.rks_offset >= 0 ? reinterpret_cast<float*>(base + L.rks_offset) : nullptr;

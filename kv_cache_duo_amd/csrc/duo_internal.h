@@ -26,6 +26,8 @@ struct Geom {
   int32_t nR, nS;             // retrieval / streaming KV heads
   int32_t kv_int8;            // retrieval rows stored as int8 codes + fp32 scales
   int32_t kv_fp8;             // retrieval rows stored as e4m3 codes, per-tensor power-of-two scales
+  int32_t fp8_mfma;           // kv_fp8: retrieval prefill on fp8 matrix cores (else exact bf16 decoding)
+  int32_t decode_dynamic;     // decode work-groups claim row batches from a counter (else a fixed stride)
   int32_t fp8_exp_k, fp8_exp_v;  // log2 of the K / V scales
   float fp8_scale_k, fp8_scale_v, fp8_inv_k, fp8_inv_v;
   int64_t max_len;

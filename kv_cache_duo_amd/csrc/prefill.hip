@@ -123,7 +123,14 @@ __device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
 // ROPE: rotary position embedding.  With Q8 as well (an int8 cache with
 // rotary embedding, prefix or not) every retrieval tile is staged: stored
 // rows dequantized, the chunk's rows turned to their positions.
-template <int D, bool Q8, bool ROPE>
+// F8: the retrieval cache holds e4m3 rows (DUO_KV_FP8, exact prefill); the
+// call's own rows are stored first, so every retrieval tile is staged from
+// the cache: codes through registers, decoded at unit scale -- exactly, an
+// e4m3 value has 4 significant bits -- into the bf16 LDS layout.  The K
+// scale joins q's pre-multiplication and the V scale the final
+// normalisation; both are powers of two, so the result is the bf16 tile
+// engine's over the stored values, bit for bit.
+template <int D, bool Q8, bool ROPE, bool F8 = false>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // The K and V tiles of the two pipeline stages are four distinct LDS
@@ -214,7 +221,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
 
   // ---- Q operand (B of S^T = K Q^T), scaled by scale * log2 e: lane holds
   // row `col`, k slice `half`
-  const float c2 = g.scale_log2;
+  const float c2 = (F8 && retrieval) ? g.scale_log2 * g.fp8_scale_k : g.scale_log2;
   bf16x8_t qreg[QC];
   {
     const bool ok = my_i <= i_hi;
@@ -308,7 +315,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // ROPE: a staged tile's chunk rows wait in kst / vst as bf16 granules
   // (bit j of rotrows: row j is a chunk row whose K is turned in store_tile).
   // Both: retrieval tiles mix stored int8 rows and chunk rows to be turned.
-  u32x4_t kst[(Q8 || ROPE) ? NJ : 1], vst[(Q8 || ROPE) ? NJ : 1];
+  // F8: a staged retrieval tile's e4m3 granules wait in kst / vst (.x .y).
+  u32x4_t kst[(Q8 || ROPE || F8) ? NJ : 1], vst[(Q8 || ROPE || F8) ? NJ : 1];
   uint32_t q8rows = 0, rotrows = 0;
   int st_k0 = 0;  // first key of the staged tile
   auto load_tile = [&](int tile, char* kbuf, char* vbuf) __attribute__((always_inline)) -> bool {  // true: staged, store_tile to follow
@@ -323,6 +331,24 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       row0 = retrieval_row0_uniform(g, b, idx, k0);
       ckr = g.rk + row0 * D;
       cvr = g.rv + row0 * D;
+    }
+    if constexpr (F8) {
+      if (retrieval) {
+        // every row up to qmax is stored; rows past it read row k0 (<= qmax,
+        // the same page), whose scores are masked
+        const uint8_t* ck8 = reinterpret_cast<const uint8_t*>(g.rk) + row0 * D;
+        const uint8_t* cv8 = reinterpret_cast<const uint8_t*>(g.rv) + row0 * D;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int kp = k0 + r0 + j * ROWS_J;
+          const int64_t row = kp <= qmax ? (int64_t)kp : (int64_t)k0;
+          const u32x2_t kc = *reinterpret_cast<const u32x2_t*>(ck8 + row * D + gK * 8);
+          const u32x2_t vc = *reinterpret_cast<const u32x2_t*>(cv8 + row * D + gV * 8);
+          kst[j] = u32x4_t{kc.x, kc.y, 0u, 0u};
+          vst[j] = u32x4_t{vc.x, vc.y, 0u, 0u};
+        }
+        return true;
+      }
     }
     if constexpr (Q8 && ROPE) {
       if (retrieval) {
@@ -466,6 +492,22 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     };
     char* dst = kbuf + wave * 1024 + lane * 16;
     char* vdst = vbuf + wave * 1024 + lane * 16;
+    if constexpr (F8) {
+      if (retrieval) {  // e4m3 codes -> bf16 at unit scale (exact)
+        auto dec = [](const u32x4_t& x) __attribute__((always_inline)) -> u32x4_t {
+          return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, false)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.x, 1.0f, true)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, false)),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x.y, 1.0f, true))};
+        };
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          *reinterpret_cast<u32x4_t*>(dst + j * kWaves * 1024) = dec(kst[j]);
+          *reinterpret_cast<u32x4_t*>(vdst + j * kWaves * 1024) = dec(vst[j]);
+        }
+        return;
+      }
+    }
     if constexpr (ROPE) {
       // chunk K rows turned to their positions (every lane takes part: the
       // half-split pairs exchange values across lanes)
@@ -617,7 +659,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           }
         }
     }
-    if constexpr (Q8 || ROPE) {
+    if constexpr (Q8 || ROPE || F8) {
       if (staged) store_tile(knext, vnext);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next tile
@@ -647,7 +689,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // ---- normalise and store this lane's query row
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (my_i <= i_hi) {
-    const float inv = 1.0f / l_tot;
+    float inv = 1.0f / l_tot;
+    if (F8 && retrieval) inv *= g.fp8_scale_v;  // a power of two: exact
     uint16_t* dst = a.out + (((int64_t)sq.off[b] + my_i) * g.Hq + h) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -667,7 +710,7 @@ int heads_per_group(int G) {
   return 1;
 }
 
-template <int D, bool Q8, bool ROPE>
+template <int D, bool Q8, bool ROPE, bool F8 = false>
 hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s,
                     bool streaming_only = false) {
   a.tq = kWaves * 32 / a.gh;
@@ -675,7 +718,7 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
   a.items_r = streaming_only ? 0 : a.tiles_max * g.B * g.nR * a.n_hc;
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * g.B * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
-  hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE>), dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
+  hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE, F8>), dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
   return hipGetLastError();
 }
 
@@ -694,6 +737,13 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   // int8 retrieval rows are only read from a stored prefix
   bool prefix = false;
   for (int b = 0; b < g.B; ++b) prefix = prefix || (q.n[b] > 0 && q.len[b] > 0);
+  if (g.kv_fp8 && !g.fp8_mfma) {  // stored e4m3 rows decoded exactly, bf16 matrix cores, one launch
+    if (g.rope)
+      return g.D == 128 ? launch_t<128, false, true, true>(g, q, a, max_n, s)
+                        : launch_t<64, false, true, true>(g, q, a, max_n, s);
+    return g.D == 128 ? launch_t<128, false, false, true>(g, q, a, max_n, s)
+                      : launch_t<64, false, false, true>(g, q, a, max_n, s);
+  }
   if (g.kv_fp8) {  // retrieval heads on fp8 matrix cores, streaming heads here
     hipError_t e = launch_prefill_fp8(g, q, qin, max_n, out, s);
     if (e != hipSuccess) return e;

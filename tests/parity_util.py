@@ -145,3 +145,29 @@ def run_sequence(cache, q, k, v, chunks, decode_steps, out_fill=0.0):
         done = [p + 1 for p in pos]
     torch.cuda.synchronize()
     return outp, (torch.stack(outd) if outd else None), done
+
+
+def poison_decode_records(cache):
+    """Fill the cache's decode split records with NaN bytes (0xFF): a decode
+    call that read a record before writing it in the same call would produce
+    a non-finite output."""
+    lay = cache.layout()
+    cache.buf[lay.work_records_offset:lay.work_offset + lay.work_bytes].fill_(0xFF)
+
+
+def decode_steps_poisoned(cache, q, k, v, start, steps):
+    """`steps` decode calls of tokens start[b] + s of q/k/v [B,T,H,D] (bf16,
+    cuda), with the split records poisoned before each call.  Returns
+    [steps, B, Hq, D]."""
+    b_n = cache.cfg.batch
+    outs = []
+    for s in range(steps):
+        q1 = torch.stack([q[b, start[b] + s] for b in range(b_n)]).contiguous()
+        k1 = torch.stack([k[b, start[b] + s] for b in range(b_n)]).contiguous()
+        v1 = torch.stack([v[b, start[b] + s] for b in range(b_n)]).contiguous()
+        o1 = torch.empty_like(q1)
+        poison_decode_records(cache)
+        duo.duo_decode(cache, q1, k1, v1, o1)
+        outs.append(o1)
+    torch.cuda.synchronize()
+    return torch.stack(outs)

@@ -1,34 +1,44 @@
 """GPU parity of the benchmark's variant legs at full size: the
-llama2_7b_mha_32k layer (32 heads, D = 128, 8 retrieval heads, one-shot
-32768-token prefill, 256 decode steps) exactly as the benchmark launches it,
-with
+llama3_8b_gqa_b8_128k layer (32 query / 8 KV heads, D = 128, 4 retrieval KV
+heads, 8 sequences, one-shot 131072-token prefill, 128 decode steps) exactly
+as the benchmark launches it, with
 
   * an int8 retrieval cache (DUO_KV_INT8),
   * rotary position embedding (base 10000, half-split pairs),
   * a paged retrieval cache (1024-position pages, a pool just large enough),
-  * an fp8 (e4m3) retrieval cache with unit tensor scales (DUO_KV_FP8).
+  * an fp8 (e4m3) retrieval cache with unit tensor scales, exact prefill
+    (the default) and prefill on the fp8 matrix cores,
+  * the dynamic decode split.
 
-Sampled prefill rows and decode steps of every query head are compared with
-the oracle of each format at the bar its own tests state; the cache is read
-back (bit for bit, or for rotated keys within the rotation tolerance)."""
+Sequences 0 and 7 are compared at sampled prefill rows and decode steps, in
+every query head, with the oracle of each format at the bar its own tests
+state; stored rows at sampled positions are read back (codes and scales bit
+for bit, bf16 rows bitwise)."""
 
 from __future__ import annotations
+
+import math
 
 import numpy as np
 import pytest
 import torch
 
 import kv_cache_duo_amd as duo
-from parity_util import assert_close, check_cache_bits, oracle_rows, require_gpu, run_sequence, to_np32
-from test_gpu_fp8 import assert_fp8_close, check_cache_fp8, oracle_fp8
-from test_gpu_int8 import check_cache_q8, oracle_q8
-from test_gpu_rope import check_cache_rope, oracle_rope
+from fp8_model import assert_fp8_mfma_close, mfma_sigma
+from oracle.fp8_cache import quantize_rows_fp8, seen_rows_fp8
+from oracle.quantized_cache import quantize_rows
+from parity_util import assert_close, oracle_rows, require_gpu, run_sequence, to_np32
+from test_gpu_fp8 import oracle_fp8
+from test_gpu_int8 import oracle_q8
+from test_gpu_rope import oracle_rope
 from workloads import WORKLOADS, qkv, workload_mask
 
 pytestmark = pytest.mark.gpu
 
-W = WORKLOADS["llama2_7b_mha_32k"]
-STEPS = [0, 1, 127, 255]
+W = WORKLOADS["llama3_8b_gqa_b8_128k"]
+SEQS = [0, 7]
+STEPS = [0, W.decode_steps - 1]
+LEGS = ["int8", "rope", "paged", "fp8", "fp8mfma", "dynamic"]
 
 
 def _say(msg):
@@ -36,10 +46,8 @@ def _say(msg):
 
 
 def _sampled_rows():
-    rng = np.random.default_rng(0)
     s, wd = W.sink, W.recent
-    return sorted(set([0, 1, s - 1, s, s + wd - 1, s + wd, 4095, 4096, W.prefill - 1] +
-                      rng.integers(0, W.prefill, 8).tolist()))
+    return [0, s - 1, s + wd, 4095, 65535, W.prefill - 1]
 
 
 def _cache(leg, mask, t):
@@ -49,58 +57,95 @@ def _cache(leg, mask, t):
     elif leg == "rope":
         kw = dict(rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF)
     elif leg == "paged":
-        kw = dict(page_tokens=1024, num_pages=(t + 1023) // 1024)
+        kw = dict(page_tokens=1024, num_pages=W.batch * ((t + 1023) // 1024))
     elif leg == "fp8":
         kw = dict(kv_format=duo.DUO_KV_FP8)
+    elif leg == "fp8mfma":
+        kw = dict(kv_format=duo.DUO_KV_FP8, fp8_prefill=duo.DUO_FP8_PREFILL_MFMA)
+    elif leg == "dynamic":
+        kw = dict(decode_split=duo.DUO_DECODE_DYNAMIC)
     cfg = duo.Config(W.batch, W.num_q_heads, W.num_kv_heads, W.head_dim, t, W.sink, W.recent,
                      [int(x) for x in mask], **kw)
     buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
     return duo.duo_cache_init(cfg, buf)
 
 
-@pytest.mark.parametrize("leg", ["int8", "rope", "paged", "fp8"])
-def test_bench_layer_leg(leg):
+def _readback(cache, leg, mask, kn, vn, k, v, positions):
+    """Stored retrieval rows of sequences SEQS at `positions`, against the
+    inputs (bf16 bitwise) or the oracle's encoding (codes and scales)."""
+    views = duo.cache_views(cache)
+    hidx = cache.head_index()
+    for i, b in enumerate(SEQS):
+        for kvh in range(W.num_kv_heads):
+            if not mask[kvh]:
+                continue
+            j = hidx[kvh]
+            if leg == "int8":
+                for name, x, sname in (("rk", kn, "rks"), ("rv", vn, "rvs")):
+                    codes, scales = quantize_rows(x[i, positions, kvh])
+                    assert np.array_equal(views[name][b, j, positions].cpu().numpy(), codes), f"{name} b{b} kv{kvh}"
+                    got_s = views[sname][b, j, positions].cpu().numpy()
+                    assert np.array_equal(got_s.view(np.uint32), scales.view(np.uint32)), f"{sname} b{b} kv{kvh}"
+            elif leg in ("fp8", "fp8mfma"):
+                for name, x in (("rk", kn), ("rv", vn)):
+                    got = views[name][b, j, positions].cpu().numpy()
+                    assert np.array_equal(got, quantize_rows_fp8(x[i, positions, kvh], 1.0)), f"{name} b{b} kv{kvh}"
+            elif leg != "rope":
+                for name, x in (("rk", k), ("rv", v)):
+                    got = views[name][b, j, positions].view(torch.int16).cpu()
+                    assert torch.equal(got, x[b, positions, kvh].view(torch.int16).cpu()), f"{name} b{b} kv{kvh}"
+
+
+@pytest.mark.parametrize("leg", LEGS)
+def test_bench_headline_leg(leg):
     require_gpu()
     _say(f"{W.name} {leg}")
     mask = workload_mask(W)
     t = W.prefill + W.decode_steps
-    q, k, v = qkv(1, t, W.num_q_heads, W.num_kv_heads, W.head_dim, W.seed, "cuda")
+    q, k, v = qkv(W.batch, t, W.num_q_heads, W.num_kv_heads, W.head_dim, W.seed * 100, "cuda")
     cache = _cache(leg, mask, t)
-    outp, outd, done = run_sequence(cache, q, k, v, [[W.prefill]], W.decode_steps)
+    outp, outd, done = run_sequence(cache, q, k, v, [[W.prefill] * W.batch], W.decode_steps)
+    assert cache.lengths() == [t] * W.batch
     rows = _sampled_rows()
     dec = [W.prefill + x for x in STEPS]
-    qn, kn, vn = to_np32(q), to_np32(k), to_np32(v)
-    got_p, got_d = to_np32(outp[0, rows]), to_np32(outd[STEPS, 0])
+    sub = lambda x: to_np32(x[SEQS])  # noqa: E731  (host copies of the checked sequences only)
+    qn, kn, vn = sub(q), sub(k), sub(v)
+    got_p = to_np32(outp[SEQS][:, rows])
+    got_d = to_np32(outd[STEPS][:, SEQS]).transpose(1, 0, 2, 3)
     s, wd = W.sink, W.recent
-    if leg == "int8":
-        ref_p = oracle_q8(qn, kn, vn, mask, s, wd, {0: rows}, [0])[0]
-        assert_close(got_p, ref_p, "int8 prefill")
-        for i, p in enumerate(dec):
-            ref = oracle_q8(qn, kn, vn, mask, s, wd, {0: [p]}, [p])[0]
-            assert_close(got_d[i:i + 1], ref, f"int8 decode step {STEPS[i]}")
-        check_cache_q8(cache, kn, vn, k, v, mask, done)
-    elif leg == "rope":
-        ref = oracle_rope(qn, kn, vn, mask, s, wd, {0: rows + dec}, 10000.0, duo.DUO_ROPE_HALF)[0]
-        assert_close(got_p, ref[:len(rows)], "rope prefill")
-        assert_close(got_d, ref[len(rows):], "rope decode")
-        check_cache_rope(cache, k, v, mask, done, 10000.0, duo.DUO_ROPE_HALF)
-    elif leg == "paged":
-        ref = oracle_rows(qn, kn, vn, mask, s, wd, {0: rows + dec})[0]
-        assert_close(got_p, ref[:len(rows)], "paged prefill")
-        assert_close(got_d, ref[len(rows):], "paged decode")
-        check_cache_bits(cache, k, v, mask, done)
-    else:
-        ref = oracle_fp8(qn, kn, vn, mask, s, wd, {0: rows + dec}, 1.0, 1.0)[0]
-        g = W.num_q_heads // W.num_kv_heads
-        retr = [h for h in range(W.num_q_heads) if mask[h // g]]
-        strm = [h for h in range(W.num_q_heads) if not mask[h // g]]
-        from oracle.fp8_cache import seen_rows_fp8
-        vmax = [np.abs(seen_rows_fp8(vn[0, :W.prefill, h // g], True, 1.0)).max() for h in retr]
-        worst = assert_fp8_close(got_p[:, retr], ref[:len(rows)][:, retr], vmax, "fp8 prefill")
-        _say(f"fp8 prefill worst max|d|/max|V| = {worst[0]:.3e}, relL2 = {worst[1]:.3e}")
-        assert_close(got_p[:, strm], ref[:len(rows)][:, strm], "fp8 prefill streaming")
-        assert_close(got_d, ref[len(rows):], "fp8 decode")
-        check_cache_fp8(cache, kn, vn, k, v, mask, done, 1.0, 1.0)
+    g = W.group
+    retr = [h for h in range(W.num_q_heads) if mask[h // g]]
+    strm = [h for h in range(W.num_q_heads) if not mask[h // g]]
+    for i, b in enumerate(SEQS):
+        if leg == "int8":  # one call: stored rows are the earlier ones, the call's own at input precision
+            ref_p = oracle_q8(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: rows}, [0])[0]
+            ref_d = np.concatenate([oracle_q8(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: [p]}, [p])[0]
+                                    for p in dec])
+        elif leg == "rope":
+            ref = oracle_rope(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: rows + dec}, 10000.0,
+                              duo.DUO_ROPE_HALF)[0]
+            ref_p, ref_d = ref[:len(rows)], ref[len(rows):]
+        elif leg in ("fp8", "fp8mfma"):
+            ref = oracle_fp8(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: rows + dec}, 1.0, 1.0)[0]
+            ref_p, ref_d = ref[:len(rows)], ref[len(rows):]
+        else:
+            ref = oracle_rows(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: rows + dec})[0]
+            ref_p, ref_d = ref[:len(rows)], ref[len(rows):]
+        if leg == "fp8mfma":
+            scale = 1.0 / math.sqrt(W.head_dim)
+            sig = np.empty((len(rows), len(retr), W.head_dim))
+            for j, h in enumerate(retr):
+                kvh = h // g
+                ks = seen_rows_fp8(kn[i, :, kvh], True, 1.0)
+                vs = seen_rows_fp8(vn[i, :, kvh], True, 1.0)
+                sig[:, j] = mfma_sigma(qn[i, rows, h], rows, ks, vs, True, s, wd, scale)
+            w = assert_fp8_mfma_close(got_p[i][:, retr], ref_p[:, retr], sig, f"{leg} prefill b{b}")
+            _say(f"fp8 mfma b{b}: |d|_2/predicted = {w[0]:.3f}, max |d|/sigma = {w[1]:.2f}")
+            assert_close(got_p[i][:, strm], ref_p[:, strm], f"{leg} prefill streaming b{b}")
+        else:
+            assert_close(got_p[i], ref_p, f"{leg} prefill b{b}")
+        assert_close(got_d[i], ref_d, f"{leg} decode b{b}")
+    _readback(cache, leg, mask, kn, vn, k, v, [0, 1, 4095, 65535, t - 1])
     del cache, q, k, v, outp, outd
     torch.cuda.synchronize()
     torch.cuda.empty_cache()

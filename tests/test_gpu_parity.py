@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import kv_cache_duo_amd as duo
-from parity_util import (assert_close, check_cache_bits, new_cache, oracle_rows, require_gpu,
+from parity_util import (assert_close, check_cache_bits, decode_steps_poisoned, new_cache, oracle_rows, require_gpu,
                          run_sequence, to_np32)
 from workloads import WORKLOADS, qkv, randn_bf16, workload_mask
 
@@ -129,28 +129,96 @@ def test_stress_inputs():
     _full_check(cache, q, k, v, mask, sink, recent, [[n - 8]], 8, "stress")
 
 
-def test_deterministic():
-    """Prefill outputs and the cache bytes are bitwise reproducible.  Decode
-    work-groups claim rows dynamically, so only the fp32 summation order of a
-    decode output may change between runs: equal up to a few bf16 ulps."""
+# (name, B, Hq, Hkv, D, mask, prefill lengths, decode steps, kv_format):
+# a few splits per head chunk (G = 4); one query head per work-group with
+# ~80 splits (direct arrivals, single-pass merge); ~200 splits (grouped
+# arrivals and the two-level merge); an int8 cache.
+DETERMINISM_CASES = [
+    ("gqa_700", 2, 16, 4, 128, [1, 0, 1, 0], [600, 650], 40, 0),
+    ("mha_20k", 1, 8, 8, 128, [1, 0, 0, 1, 0, 0, 0, 0], [20000], 4, 0),
+    ("single_100k", 1, 2, 2, 128, [1, 0], [100000], 3, 0),
+    ("int8_gqa_9k", 2, 16, 4, 128, [0, 1, 1, 0], [9000, 7000], 4, 1),
+]
+
+
+@pytest.mark.parametrize("case", DETERMINISM_CASES, ids=[c[0] for c in DETERMINISM_CASES])
+def test_deterministic(case):
+    """Two runs on the same inputs give bitwise equal prefill outputs, cache
+    bytes and decode outputs (the default static decode split: fixed rows
+    per work-group, records merged in work-group order).  The split records
+    are filled with NaN bytes before every decode call, so a record read
+    before its store in that call would show as a non-finite output."""
     require_gpu()
-    _say("determinism")
-    mask = [1, 0, 1, 0]
-    q, k, v = qkv(2, 700, 16, 4, 128, 21, "cuda")
+    name, b_n, hq, hkv, d, mask, lens, steps, fmt = case
+    _say(f"determinism {name}")
+    t = max(lens) + steps
+    q, k, v = qkv(b_n, t, hq, hkv, d, 21, "cuda")
     outs, caches = [], []
     for _ in range(2):
-        cache = new_cache(2, 16, 4, 128, 700, 16, 64, mask)
-        outs.append(run_sequence(cache, q, k, v, [[600, 650]], 40))
+        cfg = duo.Config(b_n, hq, hkv, d, t, 16, 64, mask, kv_format=fmt)
+        buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
+        cache = duo.duo_cache_init(cfg, buf)
+        if max(lens) > 20000:  # long context: fill by append, prefill only the last 64 tokens
+            pre = [n - 64 for n in lens]
+            duo.duo_cache_append(cache, k[:, :max(pre)].contiguous(), v[:, :max(pre)].contiguous(), pre)
+            c = 64
+            qc = torch.stack([q[i, pre[i]:pre[i] + c] for i in range(b_n)]).contiguous()
+            kc = torch.stack([k[i, pre[i]:pre[i] + c] for i in range(b_n)]).contiguous()
+            vc = torch.stack([v[i, pre[i]:pre[i] + c] for i in range(b_n)]).contiguous()
+            outp = torch.empty_like(qc)
+            duo.duo_prefill(cache, qc, kc, vc, [c] * b_n, outp)
+        else:
+            outp, _, _ = run_sequence(cache, q, k, v, [lens], 0)
+        outd = decode_steps_poisoned(cache, q, k, v, lens, steps)
+        outs.append((outp, outd))
         caches.append(cache)
-    assert torch.equal(outs[0][0], outs[1][0])
-    a, b = outs[0][1].float(), outs[1][1].float()
-    assert torch.allclose(a, b, rtol=2 ** -6, atol=2 ** -10), (a - b).abs().max().item()
+    assert torch.isfinite(outs[0][1].float()).all(), "decode read a record before writing it"
+    assert torch.equal(outs[0][0], outs[1][0]), "prefill outputs differ"
+    assert torch.equal(outs[0][1], outs[1][1]), "decode outputs differ"
     views = [duo.cache_views(c) for c in caches]
-    for name in views[0]:  # raw bits: unused rows hold the NaN poison
-        x, y = views[0][name], views[1][name]
+    for vname in views[0]:  # raw bits: unused rows hold the NaN poison
+        x, y = views[0][vname], views[1][vname]
         if x.dtype == torch.bfloat16:
             x, y = x.view(torch.int16), y.view(torch.int16)
-        assert torch.equal(x, y), name
+        elif x.dtype == torch.float32:
+            x, y = x.view(torch.int32), y.view(torch.int32)
+        assert torch.equal(x, y), vname
+
+
+def test_dynamic_split_within_summation_order_bound():
+    """DUO_DECODE_DYNAMIC: work-groups claim rows at run time, so the fp32
+    sums of a decode output may associate differently between runs.  Two
+    recursive fp32 sums of the same n terms in different orders differ by at
+    most about 2 (n - 1) u sum|terms| (u = 2^-24, the standard bound for
+    recursive summation).  The output is sum(p_j v_j) / sum(p_j) with
+    p_j >= 0, so the two fp32 results differ by at most
+    4 (n - 1) u max|v| + 2 (n - 1) u |o|, and their bf16 roundings by that
+    plus one bf16 ulp of the larger (<= 2^-7 |o|).  Both runs also meet the
+    oracle bar and stay finite with poisoned records."""
+    require_gpu()
+    _say("dynamic split")
+    mask = [1, 0]
+    n, steps = 9000, 3
+    q, k, v = qkv(2, n + steps, 8, 2, 128, 31, "cuda")
+    outs = []
+    for _ in range(2):
+        cfg = duo.Config(2, 8, 2, 128, n + steps, 64, 256, mask, decode_split=duo.DUO_DECODE_DYNAMIC)
+        buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
+        cache = duo.duo_cache_init(cfg, buf)
+        duo.duo_cache_append(cache, k[:, :n].contiguous(), v[:, :n].contiguous(), [n, n - 4000])
+        outs.append(decode_steps_poisoned(cache, q, k, v, [n, n - 4000], steps))
+    a, b = outs[0].double(), outs[1].double()
+    assert torch.isfinite(a).all() and torch.isfinite(b).all()
+    u = 2.0 ** -24
+    vmax = v.float().abs().max().item()
+    big = torch.maximum(a.abs(), b.abs())
+    bound = 4 * (n + steps) * u * vmax + (2 * (n + steps) * u + 2.0 ** -7) * big
+    assert ((a - b).abs() <= bound).all(), ((a - b).abs() - bound).max().item()
+    kn, vn, qn = to_np32(k), to_np32(v), to_np32(q)
+    pos = [n, n - 4000]
+    ref = oracle_rows(qn, kn, vn, mask, 64, 256, {i: [pos[i] + s for s in range(steps)] for i in range(2)})
+    for i in range(2):
+        assert_close(to_np32(outs[0][:, i]), ref[i], f"dynamic b{i}")
 
 
 def test_decode_many_splits():

@@ -15,9 +15,10 @@ then moves by at most one step (int8: one code, the row scale by at most
 one bf16 step of the row's largest magnitude; e4m3: one e4m3 step).  The
 cache check allows that for a small fraction of the K codes, holds V codes
 and scales bit for bit, and streaming K slots to the rope tests' bound.
-Outputs keep each format's bar: the usual one for int8 and for fp8 decode
-and streaming heads, the fp8 prefill bar (max |d| <= 2^-3 max |V|,
-relL2 <= 2^-4 per head) for fp8 retrieval heads' prefill.  Every cache
+Outputs keep each format's bar: the usual one for int8, for fp8 decode
+and streaming heads, and for the exact fp8 prefill (the default); the
+rounding model of tests/fp8_model.py for the fp8-matrix-core prefill of
+retrieval heads (DUO_FP8_PREFILL_MFMA).  Every cache
 buffer starts as 0xFF bytes (NaN scales and bf16 rows)."""
 
 from __future__ import annotations
@@ -33,7 +34,7 @@ from oracle import attend_rows, quantize_rows, seen_rows, streaming_slot_positio
 from oracle.fp8_cache import e4m3_decode, quantize_rows_fp8, seen_rows_fp8
 from oracle.rope import apply_rope
 from parity_util import assert_close, require_gpu, run_sequence, to_np32
-from test_gpu_fp8 import assert_fp8_close
+from fp8_model import assert_fp8_mfma_close, mfma_sigma
 from test_gpu_rope import assert_bf16_near, pair_magnitude, rotated_keys
 from workloads import qkv
 
@@ -178,6 +179,28 @@ def run_int8(cache, q, k, v, mask, chunks, steps, style, base=BASE):
     check_cache(cache, duo.DUO_KV_INT8, k, v, mask, done, base, style)
 
 
+def check_fp8_retrieval(cfg, got, ref, qn_b, kn_b, vn_b, rows, mask, base, style, what):
+    """Retrieval heads' prefill of one sequence (got / ref [len(rows), Hq, D]):
+    the usual bar for the exact mode; for the fp8-matrix-core mode the
+    rounding model, fed the turned q rows and the stored turned K rows."""
+    g = cfg.num_q_heads // cfg.num_kv_heads
+    retr = [h for h in range(cfg.num_q_heads) if mask[h // g]]
+    sk, sv = cfg.kv_scale_k or 1.0, cfg.kv_scale_v or 1.0
+    if cfg.fp8_prefill == duo.DUO_FP8_PREFILL_EXACT:
+        assert_close(got[:, retr] / sv, ref[:, retr] / sv, f"{what} (exact)")
+        return
+    sig = np.empty((len(rows), len(retr), cfg.head_dim))
+    scale = 1.0 / math.sqrt(cfg.head_dim)
+    for i, h in enumerate(retr):
+        kvh = h // g
+        ks = seen_rows_fp8(rotated_keys(kn_b[:, kvh], base, style), True, sk)
+        vs = seen_rows_fp8(vn_b[:, kvh], True, sv)
+        qr = apply_rope(qn_b[rows, h], rows, base, style)
+        sig[:, i] = mfma_sigma(qr, rows, ks, vs, True, cfg.sink, cfg.recent, scale)
+    w = assert_fp8_mfma_close(got[:, retr], ref[:, retr], sig, f"{what} (fp8 mfma)")
+    _say(f"{what}: |d|_2/predicted = {w[0]:.3f}, max |d|/sigma = {w[1]:.2f}")
+
+
 def run_fp8(cache, q, k, v, mask, chunks, steps, style, base=BASE, sk=1.0, sv=1.0):
     cfg = cache.cfg
     outp, outd, done = run_sequence(cache, q, k, v, chunks, steps)
@@ -194,9 +217,8 @@ def run_fp8(cache, q, k, v, mask, chunks, steps, style, base=BASE, sk=1.0, sv=1.
             got = to_np32(outp[b, :pre[b]])
             r = ref[b][:pre[b]]
             if retr:
-                vmax = [np.abs(seen_rows_fp8(vn[b, :pre[b], h // g], True, sv)).max() for h in retr]
-                w = assert_fp8_close(got[:, retr], r[:, retr], vmax, f"fp8 rope prefill b{b}")
-                _say(f"fp8 prefill b{b}: worst max|d|/max|V| = {w[0]:.3e}, relL2 = {w[1]:.3e}")
+                check_fp8_retrieval(cfg, got, r, qn[b], kn[b], vn[b], list(range(pre[b])), mask, base, style,
+                                    f"fp8 rope prefill b{b}")
             if strm:
                 assert_close(got[:, strm] / sv, r[:, strm] / sv, f"fp8 rope prefill streaming b{b}")
         if steps:
@@ -220,15 +242,18 @@ def test_int8_rope_chunked_prefill_and_decode(d, style):
     run_int8(cache, q, k, v, mask, CHUNKS, 12, style)
 
 
+@pytest.mark.parametrize("mode", [duo.DUO_FP8_PREFILL_EXACT, duo.DUO_FP8_PREFILL_MFMA], ids=["exact", "mfma"])
 @pytest.mark.parametrize("style", [INTERLEAVED, HALF])
 @pytest.mark.parametrize("d", [64, 128])
-def test_fp8_rope_chunked_prefill_and_decode(d, style):
-    """The same chunks on an fp8 cache: q turned before its e4m3 rounding."""
+def test_fp8_rope_chunked_prefill_and_decode(d, style, mode):
+    """The same chunks on an fp8 cache: every retrieval row attended through
+    its stored (turned) value; with the fp8 matrix cores q is turned before
+    its e4m3 rounding."""
     require_gpu()
-    _say(f"fp8 chunked d={d} style={style}")
+    _say(f"fp8 chunked d={d} style={style} mode={mode}")
     mask = [1, 0, 1, 0]
     q, k, v = qkv(2, 430, 8, 4, d, 62, "cuda")
-    cache = new_cache(duo.DUO_KV_FP8, 2, 8, 4, d, 430, 4, 16, mask, style)
+    cache = new_cache(duo.DUO_KV_FP8, 2, 8, 4, d, 430, 4, 16, mask, style, fp8_prefill=mode)
     run_fp8(cache, q, k, v, mask, CHUNKS, 12, style)
 
 
@@ -334,9 +359,8 @@ def test_rope_8bit_paged_varlen_equals_padded(fmt):
         if fmt == duo.DUO_KV_INT8:
             assert_close(got, ref[b], f"int8 varlen b{b}")
         else:
-            retr = [h for h in range(8) if mask[h // g]]
             strm = [h for h in range(8) if not mask[h // g]]
-            vmax = [np.abs(seen_rows_fp8(vn[b, :done[b], h // g], True, 1.0)).max() for h in retr]
-            assert_fp8_close(got[:, retr], ref[b][:, retr], vmax, f"fp8 varlen b{b}")
+            check_fp8_retrieval(packed.cfg, got, ref[b], qn[b], kn[b], vn[b], rows[b], mask, BASE, HALF,
+                                f"fp8 varlen b{b}")
             assert_close(got[:, strm], ref[b][:, strm], f"fp8 varlen streaming b{b}")
     check_cache(packed, fmt, k, v, mask, done, BASE, HALF)
