@@ -2,6 +2,9 @@
 // peaks when the kernels' roofline fractions are reported:
 //   ceiling stream_read <MiB>  -- 16-byte streaming reads of a buffer (HBM)
 //   ceiling stream_read_rotating <MiB> <n> -- the same over n buffers in turn
+//   ceiling copy <MiB>         -- a plain device copy of <MiB> (reads and writes
+//                                 <MiB> each, 16 bytes per lane): the known
+//                                 traffic that calibrates FETCH_SIZE / WRITE_SIZE
 //   ceiling mfma               -- back-to-back v_mfma_f32_32x32x16_bf16
 //   ceiling mfma_random        -- the same with changing pseudo-random operands
 //   ceiling mfma_fp8_random    -- v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit
@@ -37,6 +40,18 @@ __global__ __launch_bounds__(256) void stream_read(const u32x4* __restrict__ p, 
     for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
   if (acc == 0x9e3779b9u) out[blockIdx.x] = acc;  // keeps the loads; practically never true
+}
+
+// Each block copies one contiguous 64 KB slab, 4 loads in flight per thread.
+__global__ __launch_bounds__(256) void copy_slabs(const u32x4* __restrict__ src, u32x4* __restrict__ dst) {
+  const size_t base = (size_t)blockIdx.x * kSlab;
+  for (size_t i = threadIdx.x; i < kSlab; i += 256 * 4) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = src[base + i + (size_t)u * 256];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dst[base + i + (size_t)u * 256] = v[u];
+  }
 }
 
 // 4 independent accumulators per wave, `iters` rounds of 4 MFMAs each.
@@ -170,6 +185,28 @@ int run_stream_read(size_t mib) {
   return 0;
 }
 
+// A copy of `mib` MiB, launched 3 times (FETCH_SIZE / WRITE_SIZE calibration:
+// each launch reads and writes exactly mib MiB).
+int run_copy(size_t mib) {
+  const size_t bytes = mib << 20;
+  const unsigned blocks = (unsigned)(bytes / 16 / kSlab);
+  if (blocks == 0 || (size_t)blocks * kSlab * 16 != bytes) return 2;
+  u32x4 *src = nullptr, *dst = nullptr;
+  if (!ok(hipMalloc(&src, bytes), "hipMalloc") || !ok(hipMalloc(&dst, bytes), "hipMalloc")) return 1;
+  if (!ok(hipMemset(src, 1, bytes), "hipMemset")) return 1;
+  hipEvent_t a, b;
+  if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return 1;
+  (void)hipEventRecord(a, 0);
+  for (int r = 0; r < 3; ++r) hipLaunchKernelGGL(copy_slabs, dim3(blocks), dim3(256), 0, 0, src, dst);
+  (void)hipEventRecord(b, 0);
+  if (!ok(hipEventSynchronize(b), "sync")) return 1;
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, a, b);
+  printf("{\"ceiling\": \"copy\", \"mib\": %zu, \"launches\": 3, \"read_write_gbs\": %.1f}\n", mib,
+         3.0 * 2.0 * bytes / (ms * 1e-3) / 1e9);
+  return 0;
+}
+
 // One launch per buffer of `nbuf` separate buffers of `mib` MiB each, in
 // turn, so no launch finds its data in the 256 MB Infinity Cache: the rate
 // one launch of that size gets from HBM, launch ramp and drain included.
@@ -240,10 +277,12 @@ int main(int argc, char** argv) {
     return run_stream_read(argc >= 3 ? (size_t)std::atoll(argv[2]) : 4096);
   if (argc >= 2 && std::strcmp(argv[1], "stream_read_rotating") == 0)
     return run_stream_read_rotating(argc >= 3 ? (size_t)std::atoll(argv[2]) : 132, argc >= 4 ? std::atoi(argv[3]) : 8);
+  if (argc >= 2 && std::strcmp(argv[1], "copy") == 0) return run_copy(argc >= 3 ? (size_t)std::atoll(argv[2]) : 1024);
   if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma(0);
   if (argc >= 2 && std::strcmp(argv[1], "mfma_random") == 0) return run_mfma(1);
   if (argc >= 2 && std::strcmp(argv[1], "mfma_fp8_random") == 0) return run_mfma(2);
-  fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling stream_read_rotating <MiB> <buffers> | ceiling mfma"
+  fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling stream_read_rotating <MiB> <buffers> | ceiling copy <MiB>"
+                  " | ceiling mfma"
                   " | ceiling mfma_random | ceiling mfma_fp8_random\n");
   return 2;
 }
