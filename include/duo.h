@@ -284,6 +284,24 @@ duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v
 duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v,
                       void* out, void* stream);
 
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): decoding exactly as
+ * duo_decode -- same kernels, same results bit for bit -- but the split-K
+ * partial results and counters live in a static device array of the
+ * library instead of the cache buffer's work region.  The array is 64 MiB
+ * per GPU (4 MiB of counters, 60 MiB of partial results), held until the
+ * process ends; duo_cache_init looks it up and zeroes its counters once per
+ * device (on its stream), and every completed call leaves them at zero.
+ * The call allocates and frees nothing.  All calls on one GPU share the
+ * array: calls that overlap on one GPU (concurrent streams, or another
+ * thread) race and must not be issued.
+ * Errors: as duo_decode, plus UNSUPPORTED when the handle's decode needs
+ * more counters (units x counters per unit) or partial results (units x
+ * max splits x heads per work-group x (head_dim + 2) floats) than the
+ * array holds -- e.g. 256 KV heads x 128 sequences. */
+duo_status duo_decode_static_scratch(duo_cache* h, const void* q, const void* k, const void* v,
+                                     void* out, void* stream);
+
 /* Introspection (host only, no device work). */
 const char* duo_status_string(duo_status s);
 duo_status duo_cache_lengths(const duo_cache* h, int64_t* out /* [B] */);

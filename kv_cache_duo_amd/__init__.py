@@ -94,6 +94,7 @@ _SIGNATURES = {
     "duo_cache_append": (ctypes.c_int, [_P, _P, _P, _I32P, ctypes.c_int32, _P]),
     "duo_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I32P, ctypes.c_int32, _P, _P]),
     "duo_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
+    "duo_decode_static_scratch": (ctypes.c_int, [_P, _P, _P, _P, _P, _P]),
     "duo_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "duo_cache_lengths": (ctypes.c_int, [_P, _I64P]),
     "duo_cache_layout": (ctypes.c_int, [_P, ctypes.POINTER(Layout)]),
@@ -346,6 +347,18 @@ def duo_decode(cache: Cache, q, k, v, out, stream=None) -> None:
     kv_shape = (cfg.batch, cfg.num_kv_heads, cfg.head_dim)
     pk, pv = _dev(k, kv_shape, "k"), _dev(v, kv_shape, "v")
     _check(load_library().duo_decode(cache.handle, pq, pk, pv, po, _stream(stream)), "duo_decode")
+
+
+def duo_decode_static_scratch(cache: Cache, q, k, v, out, stream=None) -> None:
+    """duo_decode with the split-K scratch in the library's static device
+    array (for callers that cannot allocate; see include/duo.h)."""
+    cfg = cache.cfg
+    pq = _dev(q, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "q")
+    po = _dev(out, (cfg.batch, cfg.num_q_heads, cfg.head_dim), "out")
+    kv_shape = (cfg.batch, cfg.num_kv_heads, cfg.head_dim)
+    pk, pv = _dev(k, kv_shape, "k"), _dev(v, kv_shape, "v")
+    _check(load_library().duo_decode_static_scratch(cache.handle, pq, pk, pv, po, _stream(stream)),
+           "duo_decode_static_scratch")
 
 
 def cache_views(cache: Cache):

@@ -32,6 +32,7 @@
 // and the new K row are turned to position L once, in the prologue, and the
 // new token is scored outside the row loop (by work-group 0 of the unit).
 #include <cfloat>
+#include <mutex>
 #include <type_traits>
 
 #include "device_util.h"
@@ -891,6 +892,37 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 }
 
 }  // namespace
+
+// Scratch of duo_decode_static_scratch: counters first, partial results
+// after them.  In host code `scratch` names a host-side stand-in; its device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[kStaticTicketBytes + kStaticRecordBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_decode_scratch(void** base, hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // every call that completes leaves the counters it used at zero; they
+    // start at zero here, on the caller's stream, before its first decode
+    e = launch_zero_words(static_cast<uint32_t*>(p), kStaticTicketBytes / 4, s);
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = p;
+  }
+  *base = g_scratch[dev];
+  return hipSuccess;
+}
 
 int32_t max_splits_for(int64_t max_len, int32_t slots, int head_chunk) {
   const int64_t rows = max_len > slots ? max_len : slots;

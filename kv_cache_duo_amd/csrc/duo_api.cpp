@@ -238,6 +238,10 @@ duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int6
     const int64_t words = (reinterpret_cast<char*>(h->geom.partials) - reinterpret_cast<char*>(h->geom.lengths)) / 4;
     hipError_t e = duo::launch_zero_words(reinterpret_cast<uint32_t*>(h->geom.lengths), words,
                                           static_cast<hipStream_t>(stream));
+    // set up this device's static decode scratch now (look-up and zeroing,
+    // once per device), so that duo_decode_static_scratch itself only uses it
+    void* scratch = nullptr;
+    if (e == hipSuccess) e = duo::static_decode_scratch(&scratch, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) {
       delete h;
       return DUO_ERR_HIP;
@@ -407,6 +411,57 @@ duo_status prefill_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const 
   return DUO_OK;
 }
 
+// One decode call.  static_scratch: the split counters and records live in
+// the library's static device array (duo_decode_static_scratch) instead of
+// the cache buffer's work region.
+duo_status decode_call(duo_cache* h, const void* q, const void* k, const void* v, void* out, void* stream,
+                       bool static_scratch) {
+  if (h == nullptr || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return DUO_ERR_INVALID_ARG;
+  for (int b = 0; b < h->cfg.batch; ++b)
+    if (h->len[b] + 1 > h->cfg.max_len) return DUO_ERR_CAPACITY;
+  duo::Seqs sq;
+  std::memset(&sq, 0, sizeof(sq));
+  for (int b = 0; b < h->cfg.batch; ++b) {
+    sq.len[b] = (int32_t)h->len[b];
+    sq.n[b] = 1;
+    sq.off[b] = b;
+  }
+  duo_status st = check_pages(h, sq);
+  if (st != DUO_OK) return st;
+  duo::Geom g = h->geom;
+  if (static_scratch) {
+    const int64_t units = (int64_t)g.B * g.Hkv * (g.G / duo::decode_head_chunk(g.G, g.kv_int8 || g.kv_fp8));
+    const int64_t gc = duo::decode_head_chunk(g.G, g.kv_int8 || g.kv_fp8);
+    if (4 * units * g.tickets_per_unit > duo::kStaticTicketBytes ||
+        4 * units * g.max_splits * gc * (g.D + 2) > duo::kStaticRecordBytes)
+      return DUO_ERR_UNSUPPORTED;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const PageMark mark = mark_pages(h);
+  hipError_t e = hipSuccess;
+  if (static_scratch) {
+    void* base = nullptr;
+    e = duo::static_decode_scratch(&base, s);
+    if (e == hipSuccess) {
+      g.tickets = static_cast<uint32_t*>(base);
+      g.partials = reinterpret_cast<float*>(static_cast<char*>(base) + duo::kStaticTicketBytes);
+    }
+  }
+  if (e == hipSuccess) e = take_pages(h, sq, s);
+  if (e == hipSuccess) {
+    const duo::DecodePlan p = duo::plan_decode(g, sq, h->num_cus);
+    e = duo::launch_decode(g, sq, p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), s);
+  }
+  if (e != hipSuccess) {
+    rollback_pages(h, mark);
+    return DUO_ERR_HIP;
+  }
+  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += 1;
+  return DUO_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -502,33 +557,12 @@ duo_status duo_prefill_varlen(duo_cache* h, const void* q, const void* k, const 
 }
 
 duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v, void* out, void* stream) {
-  if (h == nullptr || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return DUO_ERR_INVALID_ARG;
-  for (int b = 0; b < h->cfg.batch; ++b)
-    if (h->len[b] + 1 > h->cfg.max_len) return DUO_ERR_CAPACITY;
-  duo::Seqs sq;
-  std::memset(&sq, 0, sizeof(sq));
-  for (int b = 0; b < h->cfg.batch; ++b) {
-    sq.len[b] = (int32_t)h->len[b];
-    sq.n[b] = 1;
-    sq.off[b] = b;
-  }
-  duo_status st = check_pages(h, sq);
-  if (st != DUO_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  const PageMark mark = mark_pages(h);
-  hipError_t e = take_pages(h, sq, s);
-  if (e == hipSuccess) {
-    const duo::DecodePlan p = duo::plan_decode(h->geom, sq, h->num_cus);
-    e = duo::launch_decode(h->geom, sq, p, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                           static_cast<const uint16_t*>(v), static_cast<uint16_t*>(out), s);
-  }
-  if (e != hipSuccess) {
-    rollback_pages(h, mark);
-    return DUO_ERR_HIP;
-  }
-  for (int b = 0; b < h->cfg.batch; ++b) h->len[b] += 1;
-  return DUO_OK;
+  return decode_call(h, q, k, v, out, stream, false);
+}
+
+duo_status duo_decode_static_scratch(duo_cache* h, const void* q, const void* k, const void* v, void* out,
+                                     void* stream) {
+  return decode_call(h, q, k, v, out, stream, true);
 }
 
 duo_status duo_cache_lengths(const duo_cache* h, int64_t* out) {

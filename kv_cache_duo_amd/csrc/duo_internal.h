@@ -151,6 +151,16 @@ hipError_t launch_prefill_fp8(const Geom& g, const Seqs& q, const uint16_t* qin,
 hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, const uint16_t* kin,
                           const uint16_t* vin, int32_t max_n, uint16_t* out, hipStream_t s);
 
+// The library's own decode scratch for callers that cannot allocate
+// (duo_decode_static_scratch): one static device array per GPU, split into
+// a counter region (zero between calls) and a partial-result region.
+constexpr int64_t kStaticTicketBytes = int64_t(4) << 20;
+constexpr int64_t kStaticRecordBytes = int64_t(60) << 20;
+// Device address of this GPU's array (the current device's), looked up once
+// per device; the first call on a device also enqueues the zeroing of its
+// counter region on `s`.  Returns the HIP error of the look-up or launch.
+hipError_t static_decode_scratch(void** base, hipStream_t s);
+
 // Query heads of one KV group handled together by a decode work-group (at
 // most 4 with an int8 retrieval cache, whose lanes hold 16 dims each).
 inline int decode_head_chunk(int G, bool kv_int8) {

@@ -390,3 +390,17 @@ def test_stale_library_is_refused(tmp_path, monkeypatch):
     (tmp_path / "libduo.build.json").write_text(json.dumps({"sources_sha256": "0" * 64, "arch": "gfx950"}))
     with pytest.raises(RuntimeError, match="other sources"):
         duo.load_library()
+
+
+def test_static_scratch_decode_checks_its_size_first():
+    """duo_decode_static_scratch refuses a handle whose decode needs more
+    counters or partial results than the library's static array holds
+    (UNSUPPORTED), before any device work."""
+    lib = duo.load_library()
+    big = _cfg(batch=128, num_q_heads=256, num_kv_heads=256, head_dim=128, max_len=1000,
+               kv_head_is_retrieval=[1] * 256)
+    c = _attach(big, [0] * 128)
+    fake = ctypes.c_void_p(FAKE)
+    assert lib.duo_decode_static_scratch(c.handle, fake, fake, fake, fake, None) == duo.DUO_ERR_UNSUPPORTED
+    assert c.lengths() == [0] * 128
+    assert lib.duo_decode_static_scratch(None, fake, fake, fake, fake, None) == duo.DUO_ERR_INVALID_ARG
