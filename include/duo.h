@@ -203,7 +203,10 @@ typedef struct duo_layout {
                                        between calls are unspecified) */
 } duo_layout;
 
-/* Lay out a new, empty cache in `dev_buf`.
+/* Lay out a new, empty cache in `dev_buf`.  The head-split layout is the
+ * method's memory saving: a full cache only for retrieval heads and a
+ * constant-length sink + recent cache for streaming heads (sourcepulse.org
+ * project card, "How It Works"; abstract on the pith.science review page).
  * dev_buf == NULL: only writes *required_bytes (no device work); *out untouched.
  * Otherwise dev_buf (256-byte aligned, buf_bytes long, caller-owned, must
  * outlive the handle) receives the layout above; the lengths and the split
@@ -238,7 +241,10 @@ void duo_cache_destroy(duo_cache* h);
  * Errors: INVALID_ARG (null handle, b out of range), HIP. */
 duo_status duo_cache_release(duo_cache* h, int32_t b, void* stream);
 
-/* Append n_new[b] tokens to every sequence without attending.
+/* Append n_new[b] tokens to every sequence without attending.  Retrieval
+ * heads keep every token and streaming heads only the sinks and the most
+ * recent ones, evicting the oldest (sourcepulse.org project card, "How It
+ * Works"; the ajithp.com blog, "How DuoAttention Works").
  * k, v: bf16 [B][chunk][Hkv][D]; rows i >= n_new[b] of sequence b are
  * ignored.  Token i of sequence b gets position len_b + i (with rotary
  * embedding, k is stored rotated at that position).  Retrieval heads
@@ -264,7 +270,10 @@ duo_status duo_cache_append_varlen(duo_cache* h, const void* k, const void* v,
 duo_status duo_prefill_varlen(duo_cache* h, const void* q, const void* k, const void* v,
                               const int32_t* cu_seqlens, void* out, void* stream);
 
-/* Pre-filling: for every new token i < n_new[b] of sequence b at position
+/* Pre-filling (the abstract on the pith.science review page: the head split
+ * speeds up pre-filling as well as decoding; retrieval heads attend to every
+ * token, streaming heads to the attention sinks and recent tokens).
+ * For every new token i < n_new[b] of sequence b at position
  * p = len_b + i and every query head, out = softmax(scale * q k^T) v over
  * the positions that head may see (retrieval: 0..p; streaming: sinks and
  * p-recent+1..p), where earlier positions come from the cache and the rest
@@ -277,8 +286,12 @@ duo_status duo_prefill_varlen(duo_cache* h, const void* q, const void* k, const 
 duo_status duo_prefill(duo_cache* h, const void* q, const void* k, const void* v,
                        const int32_t* n_new, int32_t chunk, void* out, void* stream);
 
-/* Decoding: append one token per sequence at p = len_b and attend from it
+/* Decoding (the abstract on the pith.science review page: full attention
+ * over the full cache for retrieval heads, the constant-length cache for
+ * streaming heads).  Append one token per sequence at p = len_b and attend from it
  * (itself included), exactly as duo_prefill with n_new[b] = 1 for all b.
+ * With decode_split = DUO_DECODE_STATIC (the default) two calls on equal
+ * caches and inputs give bitwise equal outputs (duo_decode_split).
  * q, out: bf16 [B][Hq][D]; k, v: bf16 [B][Hkv][D].
  * Errors: INVALID_ARG (null/misaligned pointers), CAPACITY, HIP. */
 duo_status duo_decode(duo_cache* h, const void* q, const void* k, const void* v,
