@@ -931,6 +931,45 @@ int32_t max_splits_for(int64_t max_len, int32_t slots, int head_chunk) {
   return (int32_t)(s < cap ? s : cap);
 }
 
+namespace {
+template <int DD, int GG>
+const void* decode_fn(const Geom& g) {
+  if constexpr (GG <= 4) {
+    if (g.kv_int8) return reinterpret_cast<const void*>(&decode_kernel<DD, GG, 1>);
+    if (g.kv_fp8) return reinterpret_cast<const void*>(&decode_kernel<DD, GG, 2>);
+  }
+  return reinterpret_cast<const void*>(&decode_kernel<DD, GG, 0>);
+}
+std::mutex g_occ_mu;
+int32_t g_occ[2][4][3] = {};  // [D 64/128][head chunk 1/2/4/8][format]: 0 = not yet queried
+}  // namespace
+
+// Decode work-groups of the instance that `g` launches with `head_chunk`
+// that one CU holds at once (its occupancy), queried once per instance;
+// 4 when no device answers.
+int32_t decode_wgs_per_cu(const Geom& g, int head_chunk) {
+  const int di = g.D == 128 ? 1 : 0;
+  const int ci = head_chunk == 8 ? 3 : head_chunk == 4 ? 2 : head_chunk == 2 ? 1 : 0;
+  const int fi = g.kv_int8 ? 1 : g.kv_fp8 ? 2 : 0;
+  std::lock_guard<std::mutex> lock(g_occ_mu);
+  int32_t& slot = g_occ[di][ci][fi];
+  if (slot == 0) {
+    const void* fn = nullptr;
+#define DUO_OCC_CASE(DD, GG) \
+    if (g.D == DD && head_chunk == GG) fn = decode_fn<DD, GG>(g);
+    DUO_OCC_CASE(128, 1) DUO_OCC_CASE(128, 2) DUO_OCC_CASE(128, 4) DUO_OCC_CASE(128, 8)
+    DUO_OCC_CASE(64, 1) DUO_OCC_CASE(64, 2) DUO_OCC_CASE(64, 4) DUO_OCC_CASE(64, 8)
+#undef DUO_OCC_CASE
+    int n = 0;
+    if (fn == nullptr || hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0) != hipSuccess || n < 1) {
+      (void)hipGetLastError();
+      return 4;
+    }
+    slot = n;
+  }
+  return slot;
+}
+
 DecodePlan plan_decode(const Geom& g, const Seqs& q, int32_t num_cus) {
   DecodePlan p;
   const bool byte_rows = g.kv_int8 || g.kv_fp8;
@@ -968,6 +1007,46 @@ DecodePlan plan_decode(const Geom& g, const Seqs& q, int32_t num_cus) {
   if (ts < min_pairs * pair) ts = min_pairs * pair;
   const int64_t ts_cap = round_pair(((int64_t)tmax + g.max_splits - 1) / g.max_splits);
   if (ts < ts_cap) ts = ts_cap;
+  // Several query heads per work-group: size the split so that the call's
+  // work-groups fill a whole number of rounds of the resident work-groups
+  // (CUs x the instance's occupancy), the streaming units' short work-groups
+  // counted in: the smallest split whose work-groups fit.
+  if (p.head_chunk > 1 && g.nR > 0) {
+    const int64_t slots = (int64_t)num_cus * decode_wgs_per_cu(g, p.head_chunk);
+    int64_t wg_s = 0;
+    for (int b = 0; b < g.B; ++b) wg_s += (int64_t)g.nS * n_hc * (q.len[b] + 1 > 0 ? 1 : 0);
+    // Measured (sweep of 1-3 rounds): for sequences of equal length two
+    // rounds, which is what the ~2048 rule gave already (the 8 x 128K GQA
+    // batch: 354 us at one, two or that rule, 369 at three); three when
+    // lengths differ (the mixed batch of 32, U[4096, 65536]: 0.70-0.75 of
+    // HBM peak at three against 0.56-0.74 by that rule and 0.54-0.73 at two),
+    // where every unit ends in a partial work-group and finer splits balance
+    // them better.
+    bool same_len = true;
+    for (int b = 1; b < g.B; ++b) same_len = same_len && q.len[b] == q.len[0];
+    const int rounds = same_len ? 2 : 3;
+    const int64_t target = rounds * slots - wg_s;
+    if (target >= (int64_t)g.B * g.nR * n_hc) {
+      auto wgs = [&](int64_t t) {
+        int64_t n = 0;
+        for (int b = 0; b < g.B; ++b) n += (int64_t)g.nR * n_hc * (((int64_t)q.len[b] + 1 + t - 1) / t);
+        return n;
+      };
+      // smallest multiple of the pair size, at least the minimum split and
+      // the record cap's split, whose work-groups fit the target
+      // (wgs() does not grow with the split: a binary search over pairs)
+      int64_t lo = round_pair((total + target - 1) / target);
+      if (lo < min_pairs * pair) lo = min_pairs * pair;
+      if (lo < ts_cap) lo = ts_cap;
+      int64_t hi = round_pair(tmax) > lo ? round_pair(tmax) : lo;  // one work-group per unit fits
+      while (lo < hi) {
+        const int64_t mid = lo + ((hi - lo) / pair / 2) * pair;
+        if (wgs(mid) <= target) hi = mid;
+        else lo = mid + pair;
+      }
+      ts = lo;
+    }
+  }
   p.split_tokens = (int32_t)ts;
   p.splits_r = (int32_t)((tmax + ts - 1) / ts);
   const int32_t smax = tmax < g.slots ? tmax : g.slots;

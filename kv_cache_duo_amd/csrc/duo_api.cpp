@@ -251,6 +251,35 @@ duo_status new_handle(const duo_config* cfg, void* buf, size_t bytes, const int6
   return DUO_OK;
 }
 
+}  // namespace
+
+namespace duo {
+void finish_seqs(Seqs& q, int32_t batch) {
+  int32_t idx[DUO_MAX_BATCH];
+  int32_t n = 0;
+  for (int b = 0; b < batch; ++b)
+    if (q.n[b] > 0) idx[n++] = b;
+  // longest stored prefix first (then the most new tokens); stable
+  for (int i = 1; i < n; ++i) {
+    const int32_t x = idx[i];
+    int j = i;
+    while (j > 0 && (q.len[idx[j - 1]] < q.len[x] || (q.len[idx[j - 1]] == q.len[x] && q.n[idx[j - 1]] < q.n[x]))) {
+      idx[j] = idx[j - 1];
+      --j;
+    }
+    idx[j] = x;
+  }
+  q.nact = n;
+  q.uniform = 1;
+  for (int i = 0; i < n; ++i) {
+    q.act[i] = idx[i];
+    if (q.len[idx[i]] != q.len[idx[0]] || q.n[idx[i]] != q.n[idx[0]]) q.uniform = 0;
+  }
+}
+}  // namespace duo
+
+namespace {
+
 // Shared validation of a chunk call; fills the sequence table.
 duo_status check_chunk(const duo_cache* h, const int32_t* n_new, int32_t chunk, duo::Seqs* sq, int32_t* max_n) {
   if (chunk < 1) return DUO_ERR_INVALID_ARG;
@@ -267,6 +296,7 @@ duo_status check_chunk(const duo_cache* h, const int32_t* n_new, int32_t chunk, 
     sq->n[b] = n_new[b];
     sq->off[b] = b * chunk;
   }
+  duo::finish_seqs(*sq, h->cfg.batch);
   *max_n = mx;
   return DUO_OK;
 }
@@ -287,6 +317,7 @@ duo_status check_varlen(const duo_cache* h, const int32_t* cu, duo::Seqs* sq, in
     sq->n[b] = cu[b + 1] - cu[b];
     sq->off[b] = cu[b];
   }
+  duo::finish_seqs(*sq, h->cfg.batch);
   *max_n = mx;
   return DUO_OK;
 }
@@ -427,6 +458,7 @@ duo_status decode_call(duo_cache* h, const void* q, const void* k, const void* v
     sq.n[b] = 1;
     sq.off[b] = b;
   }
+  duo::finish_seqs(sq, h->cfg.batch);
   duo_status st = check_pages(h, sq);
   if (st != DUO_OK) return st;
   duo::Geom g = h->geom;

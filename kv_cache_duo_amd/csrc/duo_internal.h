@@ -110,7 +110,18 @@ struct Seqs {
   int32_t len[DUO_MAX_BATCH];
   int32_t n[DUO_MAX_BATCH];
   int32_t off[DUO_MAX_BATCH];
+  // Sequences with new tokens, the longest stored prefix first (prefill
+  // work-groups index them), and whether every one of them has the same
+  // stored and new lengths (equal work per unit).
+  int32_t nact;
+  int32_t uniform;
+  int32_t act[DUO_MAX_BATCH];
 };
+// Fill nact / uniform / act from len and n.
+void finish_seqs(Seqs& q, int32_t batch);
+
+// Sequence of active slot i (i work-group uniform).
+__device__ __forceinline__ int active_seq(const Seqs& q, int i) { return q.act[i]; }
 
 // Writes of int32 words of the cache buffer (page-table entries, device
 // lengths), carried in the kernel arguments.

@@ -157,19 +157,22 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int col = lane & 31;   // query row of the 32-row block held by this lane
   const int half = lane >> 5;  // which 8-wide k slice / 4-row group
 
-  // ---- work item: longest query tiles first.  Work-groups go to the 8 XCDs
-  // round-robin (blockIdx mod 8); when the units (sequence, KV head, head
-  // chunk) of a kind split evenly over the XCDs, every unit stays on one XCD
-  // and that XCD runs its query tiles in order, so the resident work-groups
-  // of a unit stream the same K/V tiles nearly together and share them in
-  // the XCD's L2.  Otherwise: t-major, unit-minor.
+  // ---- work item: longest query tiles first, over the sequences that have
+  // new tokens (longest stored prefix first).  Work-groups go to the 8 XCDs
+  // round-robin (blockIdx mod 8).  When every unit (sequence, KV head, head
+  // chunk) does the same work and the units of a kind split evenly over the
+  // XCDs, every unit stays on one XCD and that XCD runs its query tiles in
+  // order, so the resident work-groups of a unit stream the same K/V tiles
+  // nearly together and share them in the XCD's L2.  Otherwise (sequences of
+  // different lengths: pinned units would load some XCDs far more than
+  // others) t-major, unit-minor, which spreads every unit over all XCDs.
   int id = blockIdx.x;
   const bool retrieval = id < a.items_r;
   if (!retrieval) id -= a.items_r;
   const int nkind = retrieval ? g.nR : g.nS;
-  const int per_t = g.B * nkind * a.n_hc;
+  const int per_t = sq.nact * nkind * a.n_hc;
   int t, rest;
-  if (per_t % kXcds == 0 && (retrieval || a.items_r % kXcds == 0)) {
+  if (sq.uniform && per_t % kXcds == 0 && (retrieval || a.items_r % kXcds == 0)) {
     const int x = id % kXcds, k = id / kXcds, per_x = per_t / kXcds;
     t = a.tiles_max - 1 - k / per_x;
     rest = x + kXcds * (k % per_x);
@@ -180,7 +183,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int hc = rest % a.n_hc;
   rest /= a.n_hc;
   const int idx = rest % nkind;
-  const int b = rest / nkind;
+  const int b = active_seq(sq, rest / nkind);
   const int n = sq.n[b];
   if (t * a.tq >= n) return;
   const int L = sq.len[b];
@@ -618,7 +621,10 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sacc[kb2][r]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32));  // tile max relative to mu
+      {  // max with lane ^ 32 (a VALU swap of the wave's halves, not an LDS round trip)
+        const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));  // tile max relative to mu
+      }
       if (__any(mt > thr)) {
         const float m_new = fmaxf(m_run, mu + mt);
         const float mu_new = m_new == -INFINITY ? 0.f : m_new;
@@ -715,8 +721,8 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
                     bool streaming_only = false) {
   a.tq = kWaves * 32 / a.gh;
   a.tiles_max = (max_n + a.tq - 1) / a.tq;
-  a.items_r = streaming_only ? 0 : a.tiles_max * g.B * g.nR * a.n_hc;
-  const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * g.B * g.nS * a.n_hc;
+  a.items_r = streaming_only ? 0 : a.tiles_max * q.nact * g.nR * a.n_hc;
+  const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * q.nact * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE, F8>), dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
   return hipGetLastError();

@@ -111,12 +111,14 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs s
   const int col = lane & 31;
   const int half = lane >> 5;
 
-  // ---- work item: retrieval units, longest query tiles first; a unit stays
-  // on one XCD when the units split evenly over the XCDs (blockIdx mod 8)
+  // ---- work item: retrieval units of the sequences with new tokens
+  // (longest stored prefix first), longest query tiles first; a unit stays on
+  // one XCD (blockIdx mod 8) when every unit does the same work and the units
+  // split evenly over the XCDs, else t-major, unit-minor over all XCDs
   const int id = blockIdx.x;
-  const int per_t = g.B * g.nR * a.n_hc;
+  const int per_t = sq.nact * g.nR * a.n_hc;
   int t, rest;
-  if (per_t % kXcds == 0) {
+  if (sq.uniform && per_t % kXcds == 0) {
     const int x = id % kXcds, k = id / kXcds, per_x = per_t / kXcds;
     t = a.tiles_max - 1 - k / per_x;
     rest = x + kXcds * (k % per_x);
@@ -127,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs s
   const int hc = rest % a.n_hc;
   rest /= a.n_hc;
   const int idx = rest % g.nR;
-  const int b = rest / g.nR;
+  const int b = active_seq(sq, rest / g.nR);
   const int n = sq.n[b];
   if (t * a.tq >= n) return;
   const int L = sq.len[b];
@@ -423,7 +425,7 @@ hipError_t launch_prefill_fp8(const Geom& g, const Seqs& q, const uint16_t* qin,
   a.n_hc = g.G / a.gh;
   a.tq = kWaves * 32 / a.gh;
   a.tiles_max = (max_n + a.tq - 1) / a.tq;
-  const int64_t blocks = (int64_t)a.tiles_max * g.B * g.nR * a.n_hc;
+  const int64_t blocks = (int64_t)a.tiles_max * q.nact * g.nR * a.n_hc;
   if (blocks <= 0) return hipSuccess;
   if (g.D == 128)
     hipLaunchKernelGGL(prefill_fp8_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
