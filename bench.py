@@ -25,10 +25,13 @@ Legs (--legs, each with its own fixed repetitions):
   mixed      32 sequences of lengths U[4096, 65536], chunked prefill in
              4096-token calls then 64 decode steps, 2/4/6 of 8 KV heads
              retrieval and the full-attention reference (8 of 8)
-  int8, fp8, fp8mfma, rope, paged, dynamic
-             the headline step over an int8 / fp8 retrieval cache (fp8mfma:
-             retrieval prefill on fp8 matrix cores), with rotary embedding,
-             over a paged cache, and with the dynamic decode split
+             (and, at 4 of 8, over an int8 retrieval cache: prefill over the
+             stored int8 prefix decoded per tile or staged once per call)
+  int8, int8rope, fp8, fp8mfma, rope, paged, dynamic
+             the headline step over an int8 / fp8 retrieval cache (int8rope:
+             int8 with rotary embedding, rows staged per call and per tile;
+             fp8mfma: retrieval prefill on fp8 matrix cores), with rotary
+             embedding, over a paged cache, and with the dynamic decode split
   cpu_baseline  the fp64 oracle on a bounded sample of the headline
              workload (decode and prefill rows), with all host cores and
              with one, and the full workload's oracle time extrapolated
@@ -53,7 +56,7 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "decode_traffic.json")
-ALL_LEGS = "mha32k,stack1m,mixed,int8,fp8,fp8mfma,rope,paged,dynamic"
+ALL_LEGS = "mha32k,stack1m,mixed,int8,int8rope,fp8,fp8mfma,rope,paged,dynamic"
 
 
 def say(msg):
@@ -410,9 +413,10 @@ def leg_mixed(R, reps, warmup):
     res = {"workload": w.name, "batch": w.batch, "mean_length": round(sum(lens) / len(lens), 1),
            "prefill_calls": ncalls, "reps": reps, "ratios": {}}
     buf = None
-    for nr in list(w.extra["ratio_sweep"]) + [hkv]:
-        mask = retrieval_mask(hkv, nr, w.seed + nr) if nr < hkv else full_mask(w)  # the parity test's masks
-        cfg = duo.Config(w.batch, hq, hkv, d, t_all, w.sink, w.recent, [int(x) for x in mask])
+
+    def run(cfg):
+        """(prefill ms, decode ms) summed over the timed repetitions."""
+        nonlocal buf
         need = duo.required_bytes(cfg)
         if buf is None or buf.numel() < need:
             buf = None
@@ -437,6 +441,12 @@ def leg_mixed(R, reps, warmup):
                 pre_ms += ev[0].elapsed_time(ev[1])
                 dec_ms += ev[1].elapsed_time(ev[2])
             del cache
+        return pre_ms, dec_ms, need
+
+    for nr in list(w.extra["ratio_sweep"]) + [hkv]:
+        mask = retrieval_mask(hkv, nr, w.seed + nr) if nr < hkv else full_mask(w)  # the parity test's masks
+        cfg = duo.Config(w.batch, hq, hkv, d, t_all, w.sink, w.recent, [int(x) for x in mask])
+        pre_ms, dec_ms, need = run(cfg)
         flops = prefill_flops(w, mask, [(0, L) for L in lens])
         byts = sum(decode_bytes(w, mask, [L + s for L in lens]) for s in range(w.decode_steps))
         gbs = byts * reps / (dec_ms * 1e-3) / 1e9
@@ -454,6 +464,24 @@ def leg_mixed(R, reps, warmup):
             r["decode_speedup_vs_full"] = ratio(full["decode_us_per_call"], r["decode_us_per_call"])
             r["prefill_speedup_vs_full"] = ratio(full["prefill_ms"], r["prefill_ms"])
             r["memory_reduction_vs_full"] = ratio(full["cache_bytes"], r["cache_bytes"])
+    # an int8 retrieval cache at 4 of 8 retrieval KV heads: every chunk after
+    # the first attends a stored int8 prefix, decoded in every tile (tiled)
+    # or once per call into the staging workspace (staged)
+    nr = hkv // 2
+    mask = retrieval_mask(hkv, nr, w.seed + nr)
+    base = res["ratios"][f"{100 * nr // hkv}%"]
+    res["int8_prefix"] = {"retrieval_kv_heads": nr}
+    for mode in ("tiled", "staged"):
+        cfg = duo.Config(w.batch, hq, hkv, d, t_all, w.sink, w.recent, [int(x) for x in mask],
+                         kv_format=duo.DUO_KV_INT8)
+        if mode == "staged":
+            cfg.int8_staging = torch.empty(duo.int8_staging_bytes(cfg), dtype=torch.uint8, device=R.dev)
+        pre_ms, dec_ms, need = run(cfg)
+        res["int8_prefix"][mode] = {
+            "prefill_ms": round(pre_ms / reps, 3), "prefill_time_vs_bf16": ratio(pre_ms / reps, base["prefill_ms"]),
+            "decode_us_per_call": round(dec_ms / reps / w.decode_steps * 1e3, 2),
+            "cache_bytes": need, "staging_bytes": duo.int8_staging_bytes(cfg) if mode == "staged" else 0}
+        del cfg
     del pool, buf
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -658,6 +686,21 @@ def main():
     if "int8" in legs:
         result["int8"] = {**variant("int8", int8_row(w), kv_format=duo.DUO_KV_INT8),
                           "cache": "retrieval K/V as int8 codes + fp32 row scales (DUO_KV_INT8)"}
+    if "int8rope" in legs:
+        # int8 cache with rotary embedding: the one-shot prefill attends the
+        # chunk's own rows turned; staged once per call into the workspace
+        # (the default here) or in every tile (tiled_prefill_ms)
+        stg = torch.empty(duo.int8_staging_bytes(dataclasses.replace(cfgs[0], kv_format=duo.DUO_KV_INT8)),
+                          dtype=torch.uint8, device=R.dev)
+        result["int8rope"] = {**variant("int8rope", int8_row(w), kv_format=duo.DUO_KV_INT8, rope_base=10000.0,
+                                        rope_style=duo.DUO_ROPE_HALF, int8_staging=stg),
+                              "staging_bytes": stg.numel()}
+        del stg
+        tiled = variant("int8rope_tiled", int8_row(w), kv_format=duo.DUO_KV_INT8, rope_base=10000.0,
+                        rope_style=duo.DUO_ROPE_HALF)
+        result["int8rope"]["tiled_prefill_ms"] = tiled["prefill_ms_per_call"]
+        result["int8rope"]["tiled_prefill_time_vs_bf16"] = tiled["prefill_time_vs_bf16"]
+        torch.cuda.empty_cache()
     if "fp8" in legs:
         result["fp8"] = {**variant("fp8", fp8_row(w), kv_format=duo.DUO_KV_FP8),
                          "cache": "retrieval K/V as e4m3 codes, one power-of-two scale per tensor (DUO_KV_FP8)"}

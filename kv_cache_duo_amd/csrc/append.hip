@@ -89,7 +89,7 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
     const uint4 vx = reinterpret_cast<const uint4*>(v + src)[c];
     if (g.rope) {
       float cs[8], sn[8];
-      rope_angles8<D>((int)p, c, g.rope_half, g.rope_rho, cs, sn);
+      rope_angles8_key<D>((int)p, c, g.rope_half, g.rope_rho, cs, sn);
       kx = rope_apply8<CH>(kx, cs, sn, g.rope_half, c);
     }
     if (retrieval && g.kv_fp8) {
@@ -103,6 +103,57 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
       reinterpret_cast<uint4*>(dk)[c] = kx;
       reinterpret_cast<uint4*>(dv)[c] = vx;
     }
+  }
+}
+
+// The retrieval rows that a prefill over an int8 cache reads, written once
+// per call as bf16 into a staging area [B][nR][rows][D] (K and V apart): the
+// stored prefix [0, len) decoded (code * scale rounded to bf16, the value a
+// tile decoded in the attention kernel would hold), and with rotary
+// embedding the chunk's own rows too, K turned to its position, V as given.
+// One block per (sequence, retrieval head, 64 rows); sequences without new
+// rows in the call are skipped.
+template <int D>
+__global__ __launch_bounds__(kAppendThreads) void stage_kernel(Geom g, Seqs q, const uint16_t* __restrict__ k,
+                                                               const uint16_t* __restrict__ v,
+                                                               uint16_t* __restrict__ st_k,
+                                                               uint16_t* __restrict__ st_v, int64_t rows,
+                                                               int32_t xr, int32_t with_chunk) {
+  constexpr int CH = D / 8;
+  constexpr int ROWS_PER_PASS = kAppendThreads / CH;
+  const int id = blockIdx.x;
+  const int x = id % xr;
+  const int idx = (id / xr) % g.nR;
+  const int b = id / (xr * g.nR);
+  const int len = q.len[b];
+  const int n = q.n[b];
+  if (n <= 0) return;
+  const int count = len + (with_chunk ? n : 0);
+  const int kvh = kv_head_of_unit(g, idx);
+  const int c = threadIdx.x % CH;
+  const int64_t base = ((int64_t)b * g.nR + idx) * rows;
+  const uint8_t* rk8 = reinterpret_cast<const uint8_t*>(g.rk);
+  const uint8_t* rv8 = reinterpret_cast<const uint8_t*>(g.rv);
+  for (int p = x * kRowsPerBlock + threadIdx.x / CH; p < min(count, (x + 1) * kRowsPerBlock); p += ROWS_PER_PASS) {
+    uint4 kx, vx;
+    if (p < len) {
+      const int64_t rrow = retrieval_row0(g, b, idx, p) + p;
+      const uint2 kc = reinterpret_cast<const uint2*>(rk8 + rrow * D)[c];
+      const uint2 vc = reinterpret_cast<const uint2*>(rv8 + rrow * D)[c];
+      kx = int8_dequant8(kc.x, kc.y, g.rks[rrow]);
+      vx = int8_dequant8(vc.x, vc.y, g.rvs[rrow]);
+    } else {
+      const int64_t src = (((int64_t)q.off[b] + (p - len)) * g.Hkv + kvh) * D;
+      kx = reinterpret_cast<const uint4*>(k + src)[c];
+      vx = reinterpret_cast<const uint4*>(v + src)[c];
+      if (g.rope) {
+        float cs[8], sn[8];
+        rope_angles8_key<D>(p, c, g.rope_half, g.rope_rho, cs, sn);
+        kx = rope_apply8<CH>(kx, cs, sn, g.rope_half, c);
+      }
+    }
+    reinterpret_cast<uint4*>(st_k + (base + p) * D)[c] = kx;
+    reinterpret_cast<uint4*>(st_v + (base + p) * D)[c] = vx;
   }
 }
 
@@ -143,6 +194,20 @@ hipError_t launch_append(const Geom& g, const Seqs& q, const uint16_t* k, const 
   else
     hipLaunchKernelGGL(append_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, xr, xs,
                        (int32_t)nr_blocks);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v, uint16_t* st_k,
+                        uint16_t* st_v, int64_t rows, bool with_chunk, hipStream_t s) {
+  if (rows <= 0 || g.nR <= 0) return hipSuccess;
+  const int32_t xr = (int32_t)((rows + kRowsPerBlock - 1) / kRowsPerBlock);
+  const int64_t blocks = (int64_t)g.B * g.nR * xr;
+  if (g.D == 128)
+    hipLaunchKernelGGL(stage_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, st_k, st_v,
+                       rows, xr, (int32_t)with_chunk);
+  else
+    hipLaunchKernelGGL(stage_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, st_k, st_v,
+                       rows, xr, (int32_t)with_chunk);
   return hipGetLastError();
 }
 

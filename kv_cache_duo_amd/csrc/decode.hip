@@ -362,11 +362,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   }
 
   // The new token's K chunk c, turned to position L with rotary embedding
-  // (rows are stored rotated: the cached rows already are).
+  // (rows are stored rotated: the cached rows already are); q turned by the
+  // same angles.
   uint4 knew = reinterpret_cast<const uint4*>(nk)[c];
   if (g.rope) {
     float cs[8], sn[8];
-    rope_angles8<D>(L, c, g.rope_half, g.rope_rho, cs, sn);
+    rope_angles8_key<D>(L, c, g.rope_half, g.rope_rho, cs, sn);
 #pragma unroll
     for (int gg = 0; gg < GC; ++gg) {
       const uint4 t = rope_apply8<LPR>(make_uint4(qw[gg][0], qw[gg][1], qw[gg][2], qw[gg][3]), cs, sn, g.rope_half, c);

@@ -89,6 +89,22 @@ __device__ __forceinline__ void store_int8_row(uint8_t* codes, float* scale_out,
   if (c == 0) *scale_out = scale;
 }
 
+// The eight values of codes w0, w1 (byte code + 128, as stored) of a row
+// with scale sc, as bf16 pairs: (b - 128) sc rounded once to bf16, computed
+// as one fma of b, sc and -128 sc (exact), so the same single rounding as
+// the product.
+__device__ __forceinline__ uint4 int8_dequant8(uint32_t w0, uint32_t w1, float sc) {
+  const float off = -128.0f * sc;
+  const uint32_t cw[2] = {w0, w1};
+  uint32_t w[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t h = cw[e >> 1] >> (16 * (e & 1));
+    w[e] = pack_bf16x2(fmaf((float)(h & 0xffu), sc, off), fmaf((float)((h >> 8) & 0xffu), sc, off));
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
 // fp8 retrieval cache (duo_kv_format DUO_KV_FP8): OCP E4M3 codes of
 // x / scale, the scale a power of two (so x * (1/scale) is exact).  The
 // conversion instruction rounds to nearest even but turns magnitudes from
@@ -189,6 +205,45 @@ __device__ __forceinline__ void rope_angles8(int p, int c, bool half, double rho
       cs[e] = cs[e - 1];
       sn[e] = sn[e - 1];
     }
+  }
+}
+
+// One step of a row group's angles: (cs, sn) turned by (cd, sd), the angles
+// of the positions between two rows of the group (complex multiplication in
+// fp32).
+__device__ __forceinline__ void rope_step8(float (&cs)[8], float (&sn)[8], const float (&cd)[8], const float (&sd)[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float c2 = fmaf(cs[e], cd[e], -sn[e] * sd[e]);
+    sn[e] = fmaf(sn[e], cd[e], cs[e] * sd[e]);
+    cs[e] = c2;
+  }
+}
+
+// Positions between the rows that one lane loads in the prefill kernel's
+// 64-row tiles (4 waves of 64 lanes, 16 bytes each: 512 / D rows per wave).
+template <int D>
+constexpr int rope_key_step() {
+  return (512 / D) * 4;
+}
+
+// The angles of a K row at position p, formed the one way every K rotation
+// forms them (the prefill's tile loads; the stores of append, decode and the
+// int8 staging): the angles of the row group's base p - j R (R =
+// rope_key_step, j = (p mod 64) / R) from fp64 turns, then j steps by the
+// angles of R positions.  The tile loads turn R-spaced rows this way with
+// one set of fp64 angles per lane; every other site reproduces it, so a key
+// turns to the same bf16 value wherever it is turned.
+template <int D>
+__device__ __forceinline__ void rope_angles8_key(int p, int c, bool half, double rho, float (&cs)[8],
+                                                 float (&sn)[8]) {
+  constexpr int R = rope_key_step<D>();
+  const int j = (p & 63) / R;
+  rope_angles8<D>(p - j * R, c, half, rho, cs, sn);
+  if (j > 0) {
+    float cd[8], sd[8];
+    rope_angles8<D>(R, c, half, rho, cd, sd);
+    for (int t = 0; t < j; ++t) rope_step8(cs, sn, cd, sd);
   }
 }
 

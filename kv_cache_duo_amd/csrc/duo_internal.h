@@ -32,6 +32,8 @@ struct Geom {
   float fp8_scale_k, fp8_scale_v, fp8_inv_k, fp8_inv_v;
   int64_t max_len;
   float scale_log2;           // softmax scale * log2(e): scores in base-2 units
+  uint16_t* int8_staging;     // kv_int8: caller's workspace for bf16 rows staged by a prefill (or null)
+  int64_t int8_staging_bytes;
   int32_t rope;               // rotary position embedding applied to q and k
   int32_t rope_half;          // pairs (i, i + D/2) instead of (2i, 2i + 1)
   double rope_rho;            // rotary base^(-2/D): pair i turns by rho^i per position
@@ -156,6 +158,11 @@ hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p,
 
 // Retrieval heads of an fp8 cache (DUO_KV_FP8), on fp8 matrix cores; the
 // chunk's retrieval rows must be stored first.
+// Stage the retrieval rows [0, len_b) of an int8 cache (with_chunk: also
+// the chunk's rows, K turned when g.rope) as bf16 rows
+// [B][nR][rows][D] at st_k / st_v.
+hipError_t launch_stage(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v, uint16_t* st_k,
+                        uint16_t* st_v, int64_t rows, bool with_chunk, hipStream_t s);
 hipError_t launch_prefill_fp8(const Geom& g, const Seqs& q, const uint16_t* qin, int32_t max_n, uint16_t* out,
                               hipStream_t s);
 

@@ -481,17 +481,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   auto store_tile = [&](char* kbuf, char* vbuf) __attribute__((always_inline)) {
     auto granule = [&](const u32x4_t& x, bool q8) __attribute__((always_inline)) -> u32x4_t {
       if (!q8) return x;
-      // (b - 128) sc as one fma of b, sc and -128 sc (exact): the same
-      // single rounding as the product
-      const float sc = __uint_as_float(x.z);
-      const float off = -128.0f * sc;
-      uint32_t w[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t cw = x[e >> 1] >> (16 * (e & 1));
-        w[e] = pack_bf16x2(fmaf((float)(cw & 0xffu), sc, off), fmaf((float)((cw >> 8) & 0xffu), sc, off));
-      }
-      return u32x4_t{w[0], w[1], w[2], w[3]};
+      const uint4 r = int8_dequant8(x.x, x.y, __uint_as_float(x.z));
+      return u32x4_t{r.x, r.y, r.z, r.w};
     };
     char* dst = kbuf + wave * 1024 + lane * 16;
     char* vdst = vbuf + wave * 1024 + lane * 16;
@@ -516,7 +507,9 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       // half-split pairs exchange values across lanes)
       // the angles of row r0 from fp64 turns; rows r0 + j ROWS_J by complex
       // multiplication with the angles of ROWS_J positions (NJ - 1 fp32
-      // steps, a few 1e-7 on cos and sin, far below the bf16 rounding of K)
+      // steps, a few 1e-7 on cos and sin, far below the bf16 rounding of K):
+      // rope_angles8_key, which every other K rotation uses
+      static_assert(ROWS_J == rope_key_step<D>(), "tile row groups and the key angles' steps");
       float cs[8], sn[8], cd[8], sd[8];
       rope_angles8<D>(st_k0 + r0, gK, g.rope_half, g.rope_rho, cs, sn);
       if constexpr (NJ > 1) {
@@ -528,14 +521,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        if (j > 0) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float c2 = fmaf(cs[e], cd[e], -sn[e] * sd[e]);
-            sn[e] = fmaf(sn[e], cd[e], cs[e] * sd[e]);
-            cs[e] = c2;
-          }
-        }
+        if (j > 0) rope_step8(cs, sn, cd, sd);
         const uint4 x = make_uint4(kst[j].x, kst[j].y, kst[j].z, kst[j].w);
         const uint4 r = rope_apply8<CH>(x, cs, sn, g.rope_half, gK);
         const u32x4_t kr = ((rotrows >> j) & 1u) ? u32x4_t{r.x, r.y, r.z, r.w} : kst[j];
@@ -758,6 +744,34 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
                         : launch_t<64, false, true>(g, q, a, max_n, s, true);
     return g.D == 128 ? launch_t<128, false, false>(g, q, a, max_n, s, true)
                       : launch_t<64, false, false>(g, q, a, max_n, s, true);
+  }
+  if (g.kv_int8 && g.nR > 0 && (prefix || g.rope) && g.int8_staging != nullptr) {
+    // Stage the rows the call reads as bf16 in the caller's workspace (once
+    // per call, instead of once per work-group and tile), then attend as
+    // over a bf16 cache laid out [B][nR][rows][D]; with rotary embedding the
+    // chunk's rows are staged turned, as a bf16 cache would hold them.
+    int64_t rows = 0;
+    for (int i = 0; i < q.nact; ++i) {
+      const int b = q.act[i];
+      const int64_t r = (int64_t)q.len[b] + (g.rope ? q.n[b] : 0);
+      rows = r > rows ? r : rows;
+    }
+    const int64_t elems = (int64_t)g.B * g.nR * rows * g.D;  // per tensor
+    if (rows > 0 && 4 * elems <= g.int8_staging_bytes) {
+      Geom gs = g;
+      gs.kv_int8 = 0;
+      gs.rk = g.int8_staging;
+      gs.rv = g.int8_staging + elems;
+      gs.rks = gs.rvs = nullptr;
+      gs.paged = 0;
+      gs.nblk = 1;
+      gs.max_len = rows;
+      hipError_t e = launch_stage(g, q, kin, vin, gs.rk, gs.rv, rows, g.rope != 0, s);
+      if (e != hipSuccess) return e;
+      if (g.rope)
+        return g.D == 128 ? launch_t<128, false, true>(gs, q, a, max_n, s) : launch_t<64, false, true>(gs, q, a, max_n, s);
+      return g.D == 128 ? launch_t<128, false, false>(gs, q, a, max_n, s) : launch_t<64, false, false>(gs, q, a, max_n, s);
+    }
   }
   if (g.rope && g.kv_int8 && g.nR > 0)  // stored rows as int8, the chunk's rows turned from the input
     return g.D == 128 ? launch_t<128, true, true>(g, q, a, max_n, s) : launch_t<64, true, true>(g, q, a, max_n, s);

@@ -18,7 +18,7 @@ import torch
 
 import kv_cache_duo_amd as duo
 from oracle import attend_rows, quantize_rows, seen_rows, streaming_slot_positions
-from parity_util import assert_close, require_gpu, to_np32
+from parity_util import assert_close, require_gpu, staging_workspace, to_np32
 from workloads import qkv
 
 pytestmark = pytest.mark.gpu
@@ -28,8 +28,13 @@ def _say(msg):
     print(f"[gpu-int8] {msg}", flush=True)
 
 
-def new_cache_q8(batch, hq, hkv, d, max_len, sink, recent, mask):
-    cfg = duo.Config(batch, hq, hkv, d, max_len, sink, recent, [int(x) for x in mask], kv_format=duo.DUO_KV_INT8)
+def new_cache_q8(batch, hq, hkv, d, max_len, sink, recent, mask, staged=False, **kw):
+    """staged: with a full prefill staging workspace (int8_staging), else none
+    (every tile decodes its stored rows)."""
+    cfg = duo.Config(batch, hq, hkv, d, max_len, sink, recent, [int(x) for x in mask], kv_format=duo.DUO_KV_INT8,
+                     **kw)
+    if staged:
+        staging_workspace(cfg)
     buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
     return duo.duo_cache_init(cfg, buf)
 
@@ -125,25 +130,30 @@ def run_q8(cache, q, k, v, chunks, decode_steps, mask):
     return done
 
 
+STAGED = pytest.mark.parametrize("staged", [False, True], ids=["tiled", "staged"])
+
+
+@STAGED
 @pytest.mark.parametrize("d", [64, 128])
-def test_q8_chunked_prefill_and_decode(d):
+def test_q8_chunked_prefill_and_decode(d, staged):
     require_gpu()
-    _say(f"chunked prefill + decode D={d}")
+    _say(f"chunked prefill + decode D={d} staged={staged}")
     mask = [1, 0, 1, 0]
     q, k, v = qkv(2, 420, 8, 4, d, 41, "cuda")
-    cache = new_cache_q8(2, 8, 4, d, 420, 4, 16, mask)
+    cache = new_cache_q8(2, 8, 4, d, 420, 4, 16, mask, staged)
     run_q8(cache, q, k, v, [[100, 50], [64, 1], [1, 63], [65, 0], [0, 130], [130, 100]], 12, mask)
 
 
 @pytest.mark.parametrize("hq,hkv,mask", [(32, 8, [1, 0, 0, 1, 1, 0, 1, 0]), (16, 2, [1, 0]), (4, 4, [1, 1, 0, 1]),
                                           (24, 3, [0, 1, 1])])
-def test_q8_group_sizes(hq, hkv, mask):
+@STAGED
+def test_q8_group_sizes(hq, hkv, mask, staged):
     """G = 4, 8, 1, 8: with an int8 cache a decode work-group serves at most
     4 query heads, so G = 8 runs two head chunks per KV head."""
     require_gpu()
-    _say(f"groups Hq={hq} Hkv={hkv}")
+    _say(f"groups Hq={hq} Hkv={hkv} staged={staged}")
     q, k, v = qkv(3, 300, hq, hkv, 128, 42, "cuda")
-    cache = new_cache_q8(3, hq, hkv, 128, 300, 8, 32, mask)
+    cache = new_cache_q8(3, hq, hkv, 128, 300, 8, 32, mask, staged)
     run_q8(cache, q, k, v, [[200, 3, 77], [50, 140, 0]], 6, mask)
 
 
@@ -184,3 +194,62 @@ def test_q8_first_token_decode():
     q, k, v = qkv(1, 5, 4, 2, 64, 44, "cuda")
     cache = new_cache_q8(1, 4, 2, 64, 8, 2, 4, mask)
     run_q8(cache, q, k, v, [], 5, mask)
+
+
+@pytest.mark.parametrize("variant", ["contiguous", "paged", "rope", "rope_paged"])
+def test_q8_staged_prefill_equals_tiled(variant):
+    """The staged prefill (stored rows decoded once per call into the
+    workspace) and the tiled one (decoded in every tile) attend the same
+    values: outputs and caches equal bit for bit, also when a workspace too
+    small for the later calls makes them fall back to the tiled path.  The
+    chunk plan mixes sequences with and without new rows, prefixes that end
+    inside a tile, and chunks of one row."""
+    require_gpu()
+    _say(f"staged == tiled, {variant}")
+    mask = [1, 0, 1, 1]
+    b_n, hq, hkv, d, t = 3, 8, 4, 128, 1500
+    kw = {}
+    if "paged" in variant:
+        kw.update(page_tokens=512, num_pages=b_n * 3)
+    if "rope" in variant:
+        kw.update(rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF)
+    q, k, v = qkv(b_n, t, hq, hkv, d, 45, "cuda")
+    plan = [[300, 0, 130], [1, 700, 64], [500, 1, 0], [0, 300, 900], [699, 499, 1]]
+    cfg0 = duo.Config(b_n, hq, hkv, d, t, 8, 64, mask, kv_format=duo.DUO_KV_INT8, **kw)
+    n_r = sum(mask)
+    # enough for rows up to 820 (the first three calls), not for the last two
+    small = 4 * b_n * n_r * d * 820
+    outs = {}
+    caches = {}
+    for mode, nbytes in (("tiled", None), ("staged", duo.int8_staging_bytes(cfg0)), ("small", small)):
+        cfg = duo.Config(**{**cfg0.__dict__})
+        if nbytes is not None:
+            staging_workspace(cfg, nbytes)
+        buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
+        cache = duo.duo_cache_init(cfg, buf)
+        done = [0] * b_n
+        res = []
+        for n_new in plan:
+            c = max(n_new)
+            qc = torch.zeros(b_n, c, hq, d, dtype=torch.bfloat16, device="cuda")
+            kc = torch.zeros(b_n, c, hkv, d, dtype=torch.bfloat16, device="cuda")
+            vc = torch.zeros_like(kc)
+            for b in range(b_n):
+                qc[b, :n_new[b]] = q[b, done[b]:done[b] + n_new[b]]
+                kc[b, :n_new[b]] = k[b, done[b]:done[b] + n_new[b]]
+                vc[b, :n_new[b]] = v[b, done[b]:done[b] + n_new[b]]
+            oc = torch.zeros_like(qc)
+            duo.duo_prefill(cache, qc, kc, vc, n_new, oc)
+            res.append(oc)
+            done = [done[b] + n_new[b] for b in range(b_n)]
+        torch.cuda.synchronize()
+        assert all(torch.isfinite(o.float()).all() for o in res), mode
+        outs[mode] = res
+        caches[mode] = cache
+    for mode in ("staged", "small"):
+        for i, (a, b) in enumerate(zip(outs["tiled"], outs[mode])):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{mode} call {i}"
+        for name in ("rk", "rv", "rks", "rvs", "sk", "sv"):
+            va = duo.cache_views(caches["tiled"])[name]
+            vb = duo.cache_views(caches[mode])[name]
+            assert torch.equal(va.view(torch.uint8), vb.view(torch.uint8)), f"{mode} {name}"

@@ -239,3 +239,50 @@ def run_sequence_from(cache, q, k, v, start, chunks, steps):
     sequence (q/k/v index positions from 0)."""
     sl = slice(start, None)
     return run_sequence(cache, q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), chunks, steps)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("style", [INTERLEAVED, HALF])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_chunked_equals_one_shot_bitwise(d, style, fmt):
+    """Chunk boundaries on multiples of 64 positions, so every query row meets
+    the same keys in the same tiles and waves as in one call over the whole
+    sequence.  Outputs and caches then equal bit for bit -- which holds only
+    if a key gets the same turned value where a tile load turns it (the
+    call's own rows of streaming heads) and where it is stored and read back
+    (rows of earlier chunks: the streaming ring, every retrieval row)."""
+    require_gpu()
+    _say(f"chunked == one-shot, d={d} style={style} {fmt}")
+    mask = [1, 0, 1, 0]
+    b_n, hq, hkv, t = 2, 8, 4, 1024
+    q, k, v = qkv(b_n, t, hq, hkv, d, 71, "cuda")
+    kw = dict(kv_format=duo.DUO_KV_FP8) if fmt == "fp8" else {}
+    plans = {"one": [[t, t]], "chunked": [[256, 128], [128, 448], [640, 448]]}
+    outs, views = {}, {}
+    for name, plan in plans.items():
+        cfg = duo.Config(b_n, hq, hkv, d, t, 8, 64, mask, rope_base=10000.0, rope_style=style, **kw)
+        buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
+        cache = duo.duo_cache_init(cfg, buf)
+        out = torch.zeros(b_n, t, hq, d, dtype=torch.bfloat16, device="cuda")
+        done = [0] * b_n
+        for n_new in plan:
+            c = max(n_new)
+            qc = torch.zeros(b_n, c, hq, d, dtype=torch.bfloat16, device="cuda")
+            kc = torch.zeros(b_n, c, hkv, d, dtype=torch.bfloat16, device="cuda")
+            vc = torch.zeros_like(kc)
+            for b in range(b_n):
+                qc[b, :n_new[b]] = q[b, done[b]:done[b] + n_new[b]]
+                kc[b, :n_new[b]] = k[b, done[b]:done[b] + n_new[b]]
+                vc[b, :n_new[b]] = v[b, done[b]:done[b] + n_new[b]]
+            oc = torch.zeros_like(qc)
+            duo.duo_prefill(cache, qc, kc, vc, n_new, oc)
+            for b in range(b_n):
+                out[b, done[b]:done[b] + n_new[b]] = oc[b, :n_new[b]]
+            done = [done[b] + n_new[b] for b in range(b_n)]
+        torch.cuda.synchronize()
+        outs[name] = out
+        views[name] = {n: x.clone() for n, x in duo.cache_views(cache).items()}
+    assert torch.equal(outs["one"].view(torch.int16), outs["chunked"].view(torch.int16))
+    for n in ("rk", "rv", "sk", "sv"):
+        a, b = views["one"][n], views["chunked"][n]
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), n

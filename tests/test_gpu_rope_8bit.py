@@ -33,7 +33,7 @@ import kv_cache_duo_amd as duo
 from oracle import attend_rows, quantize_rows, seen_rows, streaming_slot_positions
 from oracle.fp8_cache import e4m3_decode, quantize_rows_fp8, seen_rows_fp8
 from oracle.rope import apply_rope
-from parity_util import assert_close, require_gpu, run_sequence, to_np32
+from parity_util import assert_close, require_gpu, run_sequence, staging_workspace, to_np32
 from fp8_model import assert_fp8_mfma_close, mfma_sigma
 from test_gpu_rope import assert_bf16_near, pair_magnitude, rotated_keys
 from workloads import qkv
@@ -48,9 +48,12 @@ def _say(msg):
     print(f"[gpu-rope-8bit] {msg}", flush=True)
 
 
-def new_cache(fmt, batch, hq, hkv, d, max_len, sink, recent, mask, style, base=BASE, **kw):
+def new_cache(fmt, batch, hq, hkv, d, max_len, sink, recent, mask, style, base=BASE, staged=False, **kw):
+    """staged (DUO_KV_INT8): with a full prefill staging workspace."""
     cfg = duo.Config(batch, hq, hkv, d, max_len, sink, recent, [int(x) for x in mask], kv_format=fmt,
                      rope_base=base, rope_style=style, **kw)
+    if staged:
+        staging_workspace(cfg)
     buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
     return duo.duo_cache_init(cfg, buf)
 
@@ -229,16 +232,18 @@ def run_fp8(cache, q, k, v, mask, chunks, steps, style, base=BASE, sk=1.0, sv=1.
 CHUNKS = [[100, 50], [64, 1], [1, 63], [65, 0], [0, 130], [130, 100]]
 
 
+@pytest.mark.parametrize("staged", [False, True], ids=["tiled", "staged"])
 @pytest.mark.parametrize("style", [INTERLEAVED, HALF])
 @pytest.mark.parametrize("d", [64, 128])
-def test_int8_rope_chunked_prefill_and_decode(d, style):
+def test_int8_rope_chunked_prefill_and_decode(d, style, staged):
     """Chunks around the window (W=16, S=4): retrieval tiles mix stored int8
-    rows with the call's own rows, turned as they are staged."""
+    rows with the call's own rows, turned as they are loaded (tiled) or once
+    per call into the staging workspace (staged)."""
     require_gpu()
-    _say(f"int8 chunked d={d} style={style}")
+    _say(f"int8 chunked d={d} style={style} staged={staged}")
     mask = [1, 0, 1, 0]
     q, k, v = qkv(2, 430, 8, 4, d, 61, "cuda")
-    cache = new_cache(duo.DUO_KV_INT8, 2, 8, 4, d, 430, 4, 16, mask, style)
+    cache = new_cache(duo.DUO_KV_INT8, 2, 8, 4, d, 430, 4, 16, mask, style, staged=staged)
     run_int8(cache, q, k, v, mask, CHUNKS, 12, style)
 
 
@@ -270,28 +275,30 @@ def test_rope_8bit_group_sizes(fmt):
         run(cache, q, k, v, mask, [[200, 3, 77], [50, 140, 0]], 6, HALF, base=500000.0)
 
 
-@pytest.mark.parametrize("fmt", [duo.DUO_KV_INT8, duo.DUO_KV_FP8])
-def test_rope_8bit_long_one_shot_then_decode(fmt):
+@pytest.mark.parametrize("fmt,staged", [(duo.DUO_KV_INT8, False), (duo.DUO_KV_INT8, True), (duo.DUO_KV_FP8, False)],
+                         ids=["int8", "int8_staged", "fp8"])
+def test_rope_8bit_long_one_shot_then_decode(fmt, staged):
     """A 2100-token one-shot prefill (many tiles, a ragged last one), then
     decode over the stored prefix with several split-K work-groups."""
     require_gpu()
     _say(f"one-shot 2100 fmt={fmt}")
     mask = [1, 0]
     q, k, v = qkv(1, 2104, 4, 2, 128, 64, "cuda")
-    cache = new_cache(fmt, 1, 4, 2, 128, 2104, 64, 256, mask, INTERLEAVED)
+    cache = new_cache(fmt, 1, 4, 2, 128, 2104, 64, 256, mask, INTERLEAVED, staged=staged)
     run = run_int8 if fmt == duo.DUO_KV_INT8 else run_fp8
     run(cache, q, k, v, mask, [[2100]], 4, INTERLEAVED)
 
 
-@pytest.mark.parametrize("fmt", [duo.DUO_KV_INT8, duo.DUO_KV_FP8])
-def test_rope_8bit_paged(fmt):
+@pytest.mark.parametrize("fmt,staged", [(duo.DUO_KV_INT8, False), (duo.DUO_KV_INT8, True), (duo.DUO_KV_FP8, False)],
+                         ids=["int8", "int8_staged", "fp8"])
+def test_rope_8bit_paged(fmt, staged):
     """A paged cache (512-position pages): chunked prefill across page
     boundaries, then decode."""
     require_gpu()
     _say(f"paged fmt={fmt}")
     mask = [1, 1, 0, 1]
     q, k, v = qkv(2, 1300, 8, 4, 64, 65, "cuda")
-    cache = new_cache(fmt, 2, 8, 4, 64, 1300, 8, 64, mask, HALF, page_tokens=512, num_pages=6)
+    cache = new_cache(fmt, 2, 8, 4, 64, 1300, 8, 64, mask, HALF, page_tokens=512, num_pages=6, staged=staged)
     run = run_int8 if fmt == duo.DUO_KV_INT8 else run_fp8
     run(cache, q, k, v, mask, [[600, 100], [500, 700], [190, 490]], 5, HALF)
 
