@@ -273,6 +273,10 @@ __device__ void merge_records(const Geom& g, const DecodeArgs& a, char* lds, flo
   }
 }
 
+// 8-bit decode rows: the softmax reference moves only when a score passes
+// it by more than this (log2 units), so the weights stay below 2^8.
+constexpr float kDecodeSlack = 8.f;
+
 typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -328,7 +332,6 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
   const int new_row = retrieval ? L : (L < g.S ? L : g.S + (L - g.S) % g.W);
   const int ns = (T + a.split_tokens - 1) / a.split_tokens;  // work-groups of this unit
   if (split >= ns) return;
-  const int npairs = (T + PAIR - 1) / PAIR;
   const int kvh = kv_head_of_unit(g, retrieval ? idx : g.nR + idx);
   const int64_t unit_rows = retrieval ? g.max_len : (int64_t)g.slots;
   const int64_t unit_row0 = ((int64_t)b * nkind + idx) * unit_rows;  // contiguous rows of the unit
@@ -528,6 +531,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       const int grp8 = lane / LPR8, c8 = lane % LPR8;
       const int Tc = L;
       typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+      const f16x2_t ones16 = {(_Float16)1.0f, (_Float16)1.0f};
       uint32_t q16[GC][8];  // f16 pairs of dims 16 c8 .. 16 c8 + 15
       float qoff[GC], qsc[GC], cacc[GC], o8[GC][16];
 #pragma unroll
@@ -622,18 +626,57 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
             s[j][gg] = valid ? acc * (FMT == 1 ? r[j].ks * qsc[gg] : qsc[gg]) : -INFINITY;
           }
         }
+        // fp8: the codes of rows 2t and 2t + 1 for dim 4e + k as one exact
+        // f16 pair (bytes interleaved by v_perm, then converted two at a time)
+        f16x2_t vh[FMT == 2 ? kInFlight / 2 : 1][16];
+        if constexpr (FMT == 2) {
+#pragma unroll
+          for (int t = 0; t < kInFlight / 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t a0 = r[2 * t].v[e], a1 = r[2 * t + 1].v[e];
+              const uint32_t lo = __builtin_amdgcn_perm(a1, a0, 0x05010400u);  // bytes a0.0 a1.0 a0.1 a1.1
+              const uint32_t hi = __builtin_amdgcn_perm(a1, a0, 0x07030602u);  // bytes a0.2 a1.2 a0.3 a1.3
+              vh[t][4 * e] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+              vh[t][4 * e + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+              vh[t][4 * e + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+              vh[t][4 * e + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+            }
+        }
 #pragma unroll
         for (int gg = 0; gg < GC; ++gg) {
           float mx = s[0][gg];
 #pragma unroll
           for (int j = 1; j < kInFlight; ++j) mx = fmaxf(mx, s[j][gg]);
-          const float mn = fmaxf(m[gg], mx);
-          const float mu = max_or_zero(mn);
-          const float alpha = exp2_fast(m[gg] - mu);
-          l[gg] *= alpha;
-          cacc[gg] *= alpha;
+          // m is the reference the weights are taken against; it moves (and
+          // l, cacc, o8 with it) only when a score passes it by more than the
+          // slack (wave vote): exact, since they always share it, and it
+          // saves the 8-bit rows' VALU-bound loop most of its rescales
+          if (__any(mx > m[gg] + kDecodeSlack)) {
+            const float mn = fmaxf(m[gg], mx);
+            const float alpha = exp2_fast(m[gg] - max_or_zero(mn));
+            l[gg] *= alpha;
+            cacc[gg] *= alpha;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o8[gg][e] *= alpha;
+            for (int e = 0; e < 16; ++e) o8[gg][e] *= alpha;
+            m[gg] = mn;
+          }
+          const float mu = max_or_zero(m[gg]);
+          if constexpr (FMT == 2) {
+            // rows in pairs: the two weights (at most 2^8) as one f16 pair,
+            // l summed from those same values, and one v_dot2 per dim with
+            // the pair's two codes of that dim (the exact f16 values of
+            // vh); the V scale, one per tensor, comes in at the end
+#pragma unroll
+            for (int t = 0; t < kInFlight / 2; ++t) {
+              const f16x2_t ph = {(_Float16)exp2_fast(s[2 * t][gg] - mu), (_Float16)exp2_fast(s[2 * t + 1][gg] - mu)};
+              l[gg] = __builtin_amdgcn_fdot2(ph, ones16, l[gg], false);
+#pragma unroll
+              for (int e = 0; e < 16; ++e)
+                o8[gg][e] = __builtin_amdgcn_fdot2(vh[t][e], ph, o8[gg][e], false);
+            }
+            continue;
+          }
 #pragma unroll
           for (int j = 0; j < kInFlight; ++j) {
             const float p = exp2_fast(s[j][gg] - mu);
@@ -653,19 +696,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
                 o8[gg][4 * e + 2] = fmaf(pv, (float)hi.x, o8[gg][4 * e + 2]);
                 o8[gg][4 * e + 3] = fmaf(pv, (float)hi.y, o8[gg][4 * e + 3]);
               }
-            } else {
-              const float pv = p * g.fp8_scale_v;
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float2 f0 = fp8_unpack2<false>(r[j].v[e]), f1 = fp8_unpack2<true>(r[j].v[e]);
-                o8[gg][4 * e] = fmaf(pv, f0.x, o8[gg][4 * e]);
-                o8[gg][4 * e + 1] = fmaf(pv, f0.y, o8[gg][4 * e + 1]);
-                o8[gg][4 * e + 2] = fmaf(pv, f1.x, o8[gg][4 * e + 2]);
-                o8[gg][4 * e + 3] = fmaf(pv, f1.y, o8[gg][4 * e + 3]);
-              }
             }
           }
-          m[gg] = mn;
         }
       };
       if (Tc > 0) {
@@ -682,6 +714,11 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
         for (int gg = 0; gg < GC; ++gg)
 #pragma unroll
           for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-1152.0f, cacc[gg], o8[gg][e]);
+      } else {
+#pragma unroll
+        for (int gg = 0; gg < GC; ++gg)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) o8[gg][e] *= g.fp8_scale_v;  // a power of two: exact
       }
 #pragma unroll
       for (int off = LPR8; off < 64; off <<= 1) {
