@@ -517,12 +517,14 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
       // two codes) and meet q in v_dot2_f32_f16; q is held in f16 scaled by a
       // power of two (2^(15 - e), amax = m 2^e over the head: no overflow,
       // bf16 values stay exact), and the 1024 + 128 offset comes back as one
-      // per-lane constant -1152 * sum(q).  V: the same f16 values 1024 + b
-      // meet p * scale_v (fp32) in mixed-precision FMAs (fp32 accumulate),
-      // with 1152 * sum(p * scale_v) taken off once at the end.
+      // per-lane constant -1152 * sum(q).  V: a lane's rows are taken in
+      // pairs, and one v_dot2 per dim adds both rows' products: the bytes b
+      // as exact bf16 values against p * scale_v rounded to bf16, with
+      // 128 * sum(p * scale_v) taken off once at the end.
       // fp8 (FMT 2): K codes become exact f16 pairs (v_cvt_scalef32_pk_f16_fp8)
-      // for the same dot2 with no offset, V codes fp32 values; the two
-      // per-tensor scales fold into the score constant and into p.
+      // for the same dot2 with no offset; V codes exact f16 pairs of a row
+      // pair against the two weights in f16; the K tensor scale folds into
+      // the score constant, the V scale multiplies the sums at the end.
       constexpr int LPR8 = D / 16;
       constexpr int RPW8 = 64 / LPR8;
       constexpr int ITER8 = kWaves * RPW8 * kInFlight;
@@ -627,8 +629,20 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
           }
         }
         // fp8: the codes of rows 2t and 2t + 1 for dim 4e + k as one exact
-        // f16 pair (bytes interleaved by v_perm, then converted two at a time)
+        // f16 pair (bytes interleaved by v_perm, then converted two at a time);
+        // int8: their stored bytes b (0..255, exact in bf16) as one bf16 pair
         f16x2_t vh[FMT == 2 ? kInFlight / 2 : 1][16];
+        uint32_t vb[FMT == 1 ? kInFlight / 2 : 1][16];
+        if constexpr (FMT == 1) {
+#pragma unroll
+          for (int t = 0; t < kInFlight / 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int k = 0; k < 4; ++k)
+                vb[t][4 * e + k] = pack_bf16x2((float)((r[2 * t].v[e] >> (8 * k)) & 0xffu),
+                                               (float)((r[2 * t + 1].v[e] >> (8 * k)) & 0xffu));
+        }
         if constexpr (FMT == 2) {
 #pragma unroll
           for (int t = 0; t < kInFlight / 2; ++t)
@@ -675,27 +689,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
               for (int e = 0; e < 16; ++e)
                 o8[gg][e] = __builtin_amdgcn_fdot2(vh[t][e], ph, o8[gg][e], false);
             }
-            continue;
-          }
+          } else {
+            // int8, rows in pairs: the weights times the rows' V scales as
+            // one bf16 pair (range of any scale), one v_dot2 per dim with the
+            // pair's two bytes of that dim (vb); 128 * sum of those same
+            // rounded products comes off once at the end
 #pragma unroll
-          for (int j = 0; j < kInFlight; ++j) {
-            const float p = exp2_fast(s[j][gg] - mu);
-            l[gg] += p;
-            if constexpr (FMT == 1) {
-              // the codes as the exact f16 values 1024 + b, two per v_perm
-              // (as on the K side), into mixed-precision FMAs with p in
-              // fp32; 1152 * sum(p * scale_v) comes off once at the end
-              const float pv = p * r[j].vs;
-              cacc[gg] += pv;
+            for (int t = 0; t < kInFlight / 2; ++t) {
+              const float p0 = exp2_fast(s[2 * t][gg] - mu), p1 = exp2_fast(s[2 * t + 1][gg] - mu);
+              l[gg] += p0 + p1;
+              const uint32_t pw = pack_bf16x2(p0 * r[2 * t].vs, p1 * r[2 * t + 1].vs);
+              cacc[gg] = dot2_bf16(pw, 0x3f803f80u, cacc[gg]);  // (1, 1)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const f16x2_t lo = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, r[j].v[e], 0x04010400u));
-                const f16x2_t hi = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_perm(0x64646464u, r[j].v[e], 0x04030402u));
-                o8[gg][4 * e] = fmaf(pv, (float)lo.x, o8[gg][4 * e]);
-                o8[gg][4 * e + 1] = fmaf(pv, (float)lo.y, o8[gg][4 * e + 1]);
-                o8[gg][4 * e + 2] = fmaf(pv, (float)hi.x, o8[gg][4 * e + 2]);
-                o8[gg][4 * e + 3] = fmaf(pv, (float)hi.y, o8[gg][4 * e + 3]);
-              }
+              for (int e = 0; e < 16; ++e) o8[gg][e] = dot2_bf16(vb[t][e], pw, o8[gg][e]);
             }
           }
         }
@@ -713,7 +719,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
 #pragma unroll
         for (int gg = 0; gg < GC; ++gg)
 #pragma unroll
-          for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-1152.0f, cacc[gg], o8[gg][e]);
+          for (int e = 0; e < 16; ++e) o8[gg][e] = fmaf(-128.0f, cacc[gg], o8[gg][e]);
       } else {
 #pragma unroll
         for (int gg = 0; gg < GC; ++gg)
