@@ -84,15 +84,16 @@ def measured_traffic(workload: str):
     return ent.get("bytes_per_launch")
 
 
-def measured_ceilings(decode_mib: int):
-    """Streaming-read (launches of the decode call's size over 8 buffers in
-    turn, and 4 GiB) and MFMA-loop ceilings from kv_cache_duo_amd/ceiling,
-    run as a child process."""
+def measured_ceilings(decode_mib: int, extra_mib=()):
+    """Streaming-read (launches of the decode call's size -- and of each
+    size in extra_mib -- over 8 buffers in turn, and 4 GiB) and MFMA-loop
+    ceilings from kv_cache_duo_amd/ceiling, run as a child process."""
     import subprocess
     exe = os.path.join(ROOT, "kv_cache_duo_amd", "ceiling")
     out = {}
-    for args in (["stream_read_rotating", str(decode_mib), "8"], ["stream_read", "4096"], ["mfma"], ["mfma_random"],
-                 ["mfma_fp8_random"]):
+    sizes = [decode_mib] + [m for m in extra_mib if m != decode_mib]
+    for args in ([["stream_read_rotating", str(m), "8"] for m in sizes] +
+                 [["stream_read", "4096"], ["mfma"], ["mfma_random"], ["mfma_fp8_random"]]):
         r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=120)
         if r.returncode != 0:
             raise RuntimeError(f"{exe} {' '.join(args)} failed: {r.stderr}")
@@ -737,7 +738,18 @@ def main():
         result["stack1m"] = leg_stack(R)
     if not args.no_ceilings:
         say("ceilings")
-        result["measured_ceilings"] = measured_ceilings(max(1, int(round(bytes_launch / 2**20))))
+        mib = lambda b: max(1, int(round(b / 2**20)))  # noqa: E731
+        legs8 = [k for k in ("int8", "fp8") if k in result]
+        result["measured_ceilings"] = measured_ceilings(mib(bytes_launch),
+                                                        [mib(result[k]["decode_bytes_per_call"]) for k in legs8])
+        # the decode calls against a measured single-launch read of their own size
+        rec = result["measured_ceilings"].get(f"stream_read_rotating_{mib(bytes_launch)}MiB")
+        if rec:
+            result["decode"]["frac_of_measured_read"] = round(result["decode"]["gbs"] / rec["nontemporal_gbs"], 4)
+        for k in legs8:
+            rec = result["measured_ceilings"].get(f"stream_read_rotating_{mib(result[k]['decode_bytes_per_call'])}MiB")
+            if rec:
+                result[k]["decode_frac_of_measured_read"] = round(result[k]["decode_gbs"] / rec["nontemporal_gbs"], 4)
     print(json.dumps(result), flush=True)
 
 
