@@ -14,8 +14,8 @@ import pytest
 import torch
 
 import kv_cache_duo_amd as duo
-from oracle import attend_rows, streaming_slot_positions
-from parity_util import assert_close, new_cache, require_gpu
+from oracle import attend_rows, seen_rows, streaming_slot_positions
+from parity_util import assert_close, new_cache, require_gpu, staging_workspace
 from workloads import WORKLOADS, randn_bf16, sequence_lengths, workload_mask
 
 pytestmark = pytest.mark.gpu
@@ -86,14 +86,19 @@ def test_llama3_gqa_batch8_128k():
     _free()
 
 
-@pytest.mark.parametrize("n_retrieval", [2, 4, 6])
-def test_mixed_gqa_batch32_chunked(n_retrieval):
+@pytest.mark.parametrize("n_retrieval,fmt", [(2, "bf16"), (4, "bf16"), (6, "bf16"), (4, "int8_staged")])
+def test_mixed_gqa_batch32_chunked(n_retrieval, fmt):
     """32 sequences of lengths U[4096, 65536], chunked prefill in 4096-token
     calls (finished sequences pass 0), then 64 decode steps; retrieval ratio
-    25/50/75%.  Four sequences (shortest, longest, two others) are checked."""
+    25/50/75%, and at 50% over an int8 retrieval cache with the prefill
+    staging workspace (as the benchmark's int8 leg of this workload runs it:
+    every call after the first attends a stored int8 prefix, decoded once per
+    call).  Four sequences (shortest, longest, two others) are checked; for
+    int8 against the oracle's view of each call (rows stored by earlier
+    calls through their codes, the call's own rows as given)."""
     require_gpu()
     w = WORKLOADS["mixed_gqa_b32"]
-    _say(f"{w.name} nR={n_retrieval}")
+    _say(f"{w.name} nR={n_retrieval} {fmt}")
     from workloads import retrieval_mask
     mask = retrieval_mask(w.num_kv_heads, n_retrieval, w.seed + n_retrieval)
     dev = torch.device("cuda", 0)
@@ -101,8 +106,15 @@ def test_mixed_gqa_batch32_chunked(n_retrieval):
     order = np.argsort(lens)
     check = sorted({int(order[0]), int(order[-1]), int(order[5]), int(order[20])})
     max_len = int(lens.max()) + w.decode_steps
-    cache = new_cache(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, w.sink, w.recent, mask,
-                      poison=False)
+    int8 = fmt == "int8_staged"
+    if int8:
+        cfg = duo.Config(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, w.sink, w.recent,
+                         [int(x) for x in mask], kv_format=duo.DUO_KV_INT8)
+        staging_workspace(cfg)
+        cache = duo.duo_cache_init(cfg, torch.empty(duo.required_bytes(cfg), dtype=torch.uint8, device=dev))
+    else:
+        cache = new_cache(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, max_len, w.sink, w.recent, mask,
+                          poison=False)
     hq, hkv, d, c = w.num_q_heads, w.num_kv_heads, w.head_dim, w.chunk
     # host copies (bf16) of the checked sequences' tokens, and of outputs at sampled rows
     seq_q = {b: [] for b in check}
@@ -152,9 +164,18 @@ def test_mixed_gqa_batch32_chunked(n_retrieval):
         for kvh in range(hkv):
             kv = _kv64(ks[:, kvh], vs[:, kvh])
             for h in range(kvh * g, (kvh + 1) * g):
-                ref = _oracle(qs[pos, h], kv, pos, bool(mask[kvh]), w)
+                if not int8:
+                    ref = _oracle(qs[pos, h], kv, pos, bool(mask[kvh]), w)
+                else:  # rows grouped by the call that computed them: stored rows before it
+                    ref = np.empty((len(pos), w.head_dim))
+                    before = [(p // c) * c if p < n else p for p in pos]
+                    for sb in sorted(set(before)):
+                        idx = [i for i, x in enumerate(before) if x == sb]
+                        seen = (seen_rows(kv[0], bool(mask[kvh]), sb), seen_rows(kv[1], bool(mask[kvh]), sb))
+                        ref[idx] = _oracle(qs[[pos[i] for i in idx], h], seen, [pos[i] for i in idx],
+                                           bool(mask[kvh]), w)
                 assert_close(os_[pos, h].float().numpy()[:, None, :], ref[:, None, :],
-                             f"mixed nR={n_retrieval} b{b} h{h}")
+                             f"mixed nR={n_retrieval} {fmt} b{b} h{h}")
     del cache
     _free()
 

@@ -8,7 +8,9 @@ as the benchmark launches it, with
   * a paged retrieval cache (1024-position pages, a pool just large enough),
   * an fp8 (e4m3) retrieval cache with unit tensor scales, exact prefill
     (the default) and prefill on the fp8 matrix cores,
-  * the dynamic decode split.
+  * the dynamic decode split,
+  * an int8 retrieval cache with rotary embedding and the prefill staging
+    workspace (the chunk's K rows turned once per call).
 
 Sequences 0 and 7 are compared at sampled prefill rows and decode steps, in
 every query head, with the oracle of each format at the bar its own tests
@@ -27,10 +29,11 @@ import kv_cache_duo_amd as duo
 from fp8_model import assert_fp8_mfma_close, mfma_sigma
 from oracle.fp8_cache import quantize_rows_fp8, seen_rows_fp8
 from oracle.quantized_cache import quantize_rows
-from parity_util import assert_close, oracle_rows, require_gpu, run_sequence, to_np32
+from parity_util import assert_close, oracle_rows, require_gpu, run_sequence, staging_workspace, to_np32
 from test_gpu_fp8 import oracle_fp8
 from test_gpu_int8 import oracle_q8
 from test_gpu_rope import oracle_rope
+from test_gpu_rope_8bit import oracle as oracle_8bit
 from workloads import WORKLOADS, qkv, workload_mask
 
 pytestmark = pytest.mark.gpu
@@ -38,7 +41,7 @@ pytestmark = pytest.mark.gpu
 W = WORKLOADS["llama3_8b_gqa_b8_128k"]
 SEQS = [0, 7]
 STEPS = [0, W.decode_steps - 1]
-LEGS = ["int8", "rope", "paged", "fp8", "fp8mfma", "dynamic"]
+LEGS = ["int8", "rope", "paged", "fp8", "fp8mfma", "dynamic", "int8rope"]
 
 
 def _say(msg):
@@ -64,8 +67,12 @@ def _cache(leg, mask, t):
         kw = dict(kv_format=duo.DUO_KV_FP8, fp8_prefill=duo.DUO_FP8_PREFILL_MFMA)
     elif leg == "dynamic":
         kw = dict(decode_split=duo.DUO_DECODE_DYNAMIC)
+    elif leg == "int8rope":
+        kw = dict(kv_format=duo.DUO_KV_INT8, rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF)
     cfg = duo.Config(W.batch, W.num_q_heads, W.num_kv_heads, W.head_dim, t, W.sink, W.recent,
                      [int(x) for x in mask], **kw)
+    if leg == "int8rope":
+        staging_workspace(cfg)
     buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
     return duo.duo_cache_init(cfg, buf)
 
@@ -80,8 +87,10 @@ def _readback(cache, leg, mask, kn, vn, k, v, positions):
             if not mask[kvh]:
                 continue
             j = hidx[kvh]
-            if leg == "int8":
-                for name, x, sname in (("rk", kn, "rks"), ("rv", vn, "rvs")):
+            if leg in ("int8", "int8rope"):
+                # (int8rope: V only -- a turned K may sit one code from the
+                # oracle's at a rounding tie, which the rotary tests bound)
+                for name, x, sname in ((("rk", kn, "rks"),) if leg == "int8" else ()) + (("rv", vn, "rvs"),):
                     codes, scales = quantize_rows(x[i, positions, kvh])
                     assert np.array_equal(views[name][b, j, positions].cpu().numpy(), codes), f"{name} b{b} kv{kvh}"
                     got_s = views[sname][b, j, positions].cpu().numpy()
@@ -121,6 +130,11 @@ def test_bench_headline_leg(leg):
             ref_p = oracle_q8(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: rows}, [0])[0]
             ref_d = np.concatenate([oracle_q8(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: [p]}, [p])[0]
                                     for p in dec])
+        elif leg == "int8rope":  # one call: the chunk's own rows at input precision (turned)
+            ref_p = oracle_8bit(duo.DUO_KV_INT8, qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: rows}, [0],
+                                10000.0, duo.DUO_ROPE_HALF)[0]
+            ref_d = np.concatenate([oracle_8bit(duo.DUO_KV_INT8, qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd,
+                                                {0: [p]}, [p], 10000.0, duo.DUO_ROPE_HALF)[0] for p in dec])
         elif leg == "rope":
             ref = oracle_rope(qn[i:i + 1], kn[i:i + 1], vn[i:i + 1], mask, s, wd, {0: rows + dec}, 10000.0,
                               duo.DUO_ROPE_HALF)[0]
