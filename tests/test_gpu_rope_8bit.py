@@ -315,13 +315,16 @@ def test_rope_8bit_first_token_decode(fmt):
     run(cache, q, k, v, mask, [], 6, INTERLEAVED)
 
 
-@pytest.mark.parametrize("fmt", [duo.DUO_KV_INT8, duo.DUO_KV_FP8])
-def test_rope_8bit_paged_varlen_equals_padded(fmt):
+@pytest.mark.parametrize("fmt,staged", [(duo.DUO_KV_INT8, False), (duo.DUO_KV_INT8, True), (duo.DUO_KV_FP8, False)],
+                         ids=["int8", "int8_staged", "fp8"])
+def test_rope_8bit_paged_varlen_equals_padded(fmt, staged):
     """Rotary embedding, an 8-bit paged cache and a stored prefix together:
     a packed (cu_seqlens) prefill gives the padded call's outputs and cache
-    bytes bit for bit, and both match the oracle."""
+    bytes bit for bit, and both match the oracle (int8 also through the
+    staging workspace, where the packed rows are staged from their packed
+    offsets)."""
     require_gpu()
-    _say(f"paged varlen == padded fmt={fmt}")
+    _say(f"paged varlen == padded fmt={fmt} staged={staged}")
     mask = [1, 0, 1, 1]
     b_n = 3
     pre, lens = [700, 0, 90], [300, 520, 0]
@@ -329,7 +332,8 @@ def test_rope_8bit_paged_varlen_equals_padded(fmt):
     q, k, v = qkv(b_n, t, 8, 4, 64, 67, "cuda")
 
     def fresh():
-        return new_cache(fmt, b_n, 8, 4, 64, t, 8, 32, mask, HALF, page_tokens=512, num_pages=b_n * 2)
+        return new_cache(fmt, b_n, 8, 4, 64, t, 8, 32, mask, HALF, page_tokens=512, num_pages=b_n * 2,
+                         staged=staged)
 
     pad, packed = fresh(), fresh()
     for cache in (pad, packed):
