@@ -29,9 +29,10 @@ Legs (--legs, each with its own fixed repetitions):
              stored int8 prefix decoded per tile or staged once per call)
   int8, int8rope, fp8, fp8mfma, rope, paged, dynamic
              the headline step over an int8 / fp8 retrieval cache (int8rope:
-             int8 with rotary embedding, rows staged per call and per tile;
-             fp8mfma: retrieval prefill on fp8 matrix cores), with rotary
-             embedding, over a paged cache, and with the dynamic decode split
+             int8 with rotary embedding; fp8mfma: retrieval prefill on fp8
+             matrix cores), with rotary embedding, over a paged cache, and
+             with the dynamic decode split; the rotary legs run with the
+             prefill staging workspace and once without it (tiled)
   cpu_baseline  the fp64 oracle on a bounded sample of the headline
              workload (decode and prefill rows), with all host cores and
              with one, and the full workload's oracle time extrapolated
@@ -476,12 +477,12 @@ def leg_mixed(R, reps, warmup):
         cfg = duo.Config(w.batch, hq, hkv, d, t_all, w.sink, w.recent, [int(x) for x in mask],
                          kv_format=duo.DUO_KV_INT8)
         if mode == "staged":
-            cfg.int8_staging = torch.empty(duo.int8_staging_bytes(cfg), dtype=torch.uint8, device=R.dev)
+            cfg.prefill_staging = torch.empty(duo.prefill_staging_bytes(cfg), dtype=torch.uint8, device=R.dev)
         pre_ms, dec_ms, need = run(cfg)
         res["int8_prefix"][mode] = {
             "prefill_ms": round(pre_ms / reps, 3), "prefill_time_vs_bf16": ratio(pre_ms / reps, base["prefill_ms"]),
             "decode_us_per_call": round(dec_ms / reps / w.decode_steps * 1e3, 2),
-            "cache_bytes": need, "staging_bytes": duo.int8_staging_bytes(cfg) if mode == "staged" else 0}
+            "cache_bytes": need, "staging_bytes": duo.prefill_staging_bytes(cfg) if mode == "staged" else 0}
         del cfg
     del pool, buf
     torch.cuda.synchronize()
@@ -691,10 +692,11 @@ def main():
         # int8 cache with rotary embedding: the one-shot prefill attends the
         # chunk's own rows turned; staged once per call into the workspace
         # (the default here) or in every tile (tiled_prefill_ms)
-        stg = torch.empty(duo.int8_staging_bytes(dataclasses.replace(cfgs[0], kv_format=duo.DUO_KV_INT8)),
+        stg = torch.empty(duo.prefill_staging_bytes(dataclasses.replace(cfgs[0], kv_format=duo.DUO_KV_INT8,
+                                                                        rope_base=10000.0)),
                           dtype=torch.uint8, device=R.dev)
         result["int8rope"] = {**variant("int8rope", int8_row(w), kv_format=duo.DUO_KV_INT8, rope_base=10000.0,
-                                        rope_style=duo.DUO_ROPE_HALF, int8_staging=stg),
+                                        rope_style=duo.DUO_ROPE_HALF, prefill_staging=stg),
                               "staging_bytes": stg.numel()}
         del stg
         tiled = variant("int8rope_tiled", int8_row(w), kv_format=duo.DUO_KV_INT8, rope_base=10000.0,
@@ -710,8 +712,19 @@ def main():
                                        fp8_prefill=duo.DUO_FP8_PREFILL_MFMA),
                              "cache": "DUO_KV_FP8, retrieval prefill on fp8 matrix cores (priced at 5 PFLOP/s)"}
     if "rope" in legs:
-        result["rope"] = {**variant("rope", rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF),
-                          "embedding": "rotary, base 10000, pairs (i, i + D/2), applied inside the library"}
+        # the streaming heads' chunk K rows turned once per call into the
+        # staging workspace (the default here), or in every tile that holds
+        # them (tiled_prefill_ms)
+        stg = torch.empty(duo.prefill_staging_bytes(dataclasses.replace(cfgs[0], rope_base=10000.0)),
+                          dtype=torch.uint8, device=R.dev)
+        result["rope"] = {**variant("rope", rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF, prefill_staging=stg),
+                          "embedding": "rotary, base 10000, pairs (i, i + D/2), applied inside the library",
+                          "staging_bytes": stg.numel()}
+        del stg
+        tiled = variant("rope_tiled", rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF)
+        result["rope"]["tiled_prefill_ms"] = tiled["prefill_ms_per_call"]
+        result["rope"]["tiled_prefill_time_vs_bf16"] = tiled["prefill_time_vs_bf16"]
+        torch.cuda.empty_cache()
     if "paged" in legs:
         result["paged"] = {**variant("paged", page_tokens=1024, num_pages=w.batch * (-(-t_all // 1024))),
                            "page_tokens": 1024}

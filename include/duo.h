@@ -157,21 +157,28 @@ typedef struct duo_config {
   float kv_scale_v;
   int32_t fp8_prefill;  /* duo_fp8_prefill (read with DUO_KV_FP8) */
   int32_t decode_split; /* duo_decode_split */
-  /* DUO_KV_INT8: an optional caller-owned DEVICE workspace (16-byte aligned,
-   * int8_staging_bytes long, must outlive the handle) in which a prefill
-   * call first decodes the stored retrieval rows it reads to bf16 -- and,
-   * with rotary embedding, turns its own chunk's K rows -- once per call;
-   * its attention then runs as over a bf16 cache.  A call needs
-   * 4 * batch * retrieval KV heads * head_dim * rows bytes, rows = the
-   * largest len_b (len_b + n_new[b] with rotary embedding) among the
-   * sequences it extends; duo_layout.int8_staging_bytes is the most any
-   * call needs.  A call that needs more than int8_staging_bytes (or finds
-   * none) decodes the stored rows in every tile it loads instead.  Both
-   * ways attend the same values (code * scale rounded once to bf16) and
-   * give bitwise equal outputs.  Caches whose calls run in order on one
-   * stream may share one workspace.  NULL / 0: no workspace. */
-  void* int8_staging;
-  int64_t int8_staging_bytes;
+  /* An optional caller-owned DEVICE workspace (16-byte aligned,
+   * prefill_staging_bytes long, must outlive the handle) where a prefill
+   * call first writes, once per call, rows its attention would otherwise
+   * prepare in every tile that reads them:
+   *   - DUO_KV_INT8: the stored retrieval rows it reads, decoded to bf16 K
+   *     and V (with rotary embedding also its own chunk's rows, K turned):
+   *     4 * batch * retrieval KV heads * head_dim * rows bytes, rows = the
+   *     largest len_b (len_b + n_new[b] with rotary embedding) among the
+   *     sequences it extends;
+   *   - rotary embedding (any format): the chunk's K rows of every streaming
+   *     head, turned: 2 * batch * streaming KV heads * head_dim * chunk
+   *     bytes, after the int8 rows.
+   * Each part is used when the workspace has room for it (and, for the
+   * turned rows, when the int8 rows are staged or the cache is not int8);
+   * otherwise the tiles prepare those rows themselves.  duo_layout.
+   * prefill_staging_bytes is the most any call needs.  Both ways attend the
+   * same values (a stored int8 row as code * scale rounded once to bf16, a
+   * key turned as every K rotation turns it) and give bitwise equal outputs.
+   * Caches whose calls run in order on one stream may share one workspace.
+   * NULL / 0: no workspace. */
+  void* prefill_staging;
+  int64_t prefill_staging_bytes;
 } duo_config;
 
 /* Opaque host-side handle: configuration, head maps, region offsets and the
@@ -216,8 +223,9 @@ typedef struct duo_layout {
   int64_t work_records_offset;      /* decoding's split-K partial results, up to work_offset + work_bytes
                                        (written by a decode call before it reads them; their contents
                                        between calls are unspecified) */
-  int64_t int8_staging_bytes;       /* DUO_KV_INT8: the duo_config.int8_staging size that serves every
-                                       prefill call (4 * B * nR * D * max_len); 0 otherwise */
+  int64_t prefill_staging_bytes;    /* the duo_config.prefill_staging size that serves every prefill call:
+                                       4 * B * nR * D * max_len for DUO_KV_INT8, plus 2 * B * nS * D * max_len
+                                       with rotary embedding; 0 when neither applies */
 } duo_layout;
 
 /* Lay out a new, empty cache in `dev_buf`.  The head-split layout is the
@@ -234,8 +242,8 @@ typedef struct duo_layout {
  * rope_style not a duo_rope_style, page_tokens not 0 or a power of two in
  * 512..65536, page_tokens > 0 with num_pages < 1, kv_scale_k / kv_scale_v
  * not 0 or a power of two in [2^-32, 2^32], fp8_prefill not a
- * duo_fp8_prefill, decode_split not a duo_decode_split, int8_staging
- * misaligned or int8_staging_bytes < 0), UNSUPPORTED (head_dim, batch,
+ * duo_fp8_prefill, decode_split not a duo_decode_split, prefill_staging
+ * misaligned or prefill_staging_bytes < 0), UNSUPPORTED (head_dim, batch,
  * num_kv_heads, max_len or sink + recent beyond the library's limits),
  * BUFFER_TOO_SMALL, HIP. */
 duo_status duo_cache_init(const duo_config* cfg, void* dev_buf, size_t buf_bytes,

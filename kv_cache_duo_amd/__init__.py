@@ -63,7 +63,7 @@ class _Config(ctypes.Structure):
         ("page_tokens", ctypes.c_int32), ("num_pages", ctypes.c_int64),
         ("kv_scale_k", ctypes.c_float), ("kv_scale_v", ctypes.c_float),
         ("fp8_prefill", ctypes.c_int32), ("decode_split", ctypes.c_int32),
-        ("int8_staging", ctypes.c_void_p), ("int8_staging_bytes", ctypes.c_int64),
+        ("prefill_staging", ctypes.c_void_p), ("prefill_staging_bytes", ctypes.c_int64),
     ]
 
 
@@ -79,7 +79,7 @@ class Layout(ctypes.Structure):
         ("page_table_offset", ctypes.c_int64), ("page_tokens", ctypes.c_int32),
         ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int64),
         ("block_tokens", ctypes.c_int32), ("work_records_offset", ctypes.c_int64),
-        ("int8_staging_bytes", ctypes.c_int64),
+        ("prefill_staging_bytes", ctypes.c_int64),
     ]
 
 
@@ -182,9 +182,11 @@ class Config:
     kv_scale_v: float = 0.0  # DUO_KV_FP8: power-of-two V scale (0 = 1)
     fp8_prefill: int = 0     # DUO_FP8_PREFILL_EXACT (bf16 matrix cores) or DUO_FP8_PREFILL_MFMA (fp8 ones)
     decode_split: int = 0    # DUO_DECODE_STATIC (bitwise reproducible) or DUO_DECODE_DYNAMIC
-    # DUO_KV_INT8: device workspace (a CUDA tensor, kept alive with the config)
-    # where a prefill stages the stored rows it reads as bf16; see int8_staging_bytes()
-    int8_staging: object = None
+    # DUO_KV_INT8 or rotary embedding: device workspace (a CUDA tensor, kept
+    # alive with the config) where a prefill stages, once per call, the int8
+    # rows it reads as bf16 and the streaming heads' turned chunk K rows; see
+    # prefill_staging_bytes()
+    prefill_staging: object = None
 
     def _c(self):
         mask = (ctypes.c_uint8 * max(len(self.kv_head_is_retrieval), 1))(
@@ -194,12 +196,12 @@ class Config:
                     ctypes.cast(mask, ctypes.POINTER(ctypes.c_uint8)), self.kv_format, self.rope_base,
                     self.rope_style, self.page_tokens, self.num_pages, self.kv_scale_k, self.kv_scale_v,
                     self.fp8_prefill, self.decode_split, None, 0)
-        if self.int8_staging is not None:
-            t = self.int8_staging
+        if self.prefill_staging is not None:
+            t = self.prefill_staging
             if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or not t.is_contiguous():
-                raise ValueError("int8_staging must be a contiguous CUDA tensor")
-            c.int8_staging = t.data_ptr()
-            c.int8_staging_bytes = t.numel() * t.element_size()
+                raise ValueError("prefill_staging must be a contiguous CUDA tensor")
+            c.prefill_staging = t.data_ptr()
+            c.prefill_staging_bytes = t.numel() * t.element_size()
         return c, mask  # keep the mask alive for the call
 
 
@@ -219,13 +221,19 @@ def _dev(t: torch.Tensor, shape, name: str) -> int:
     return t.data_ptr()
 
 
-def int8_staging_bytes(cfg: Config) -> int:
-    """Workspace bytes that let every prefill of an int8 cache stage its rows
-    (4 * batch * retrieval KV heads * head_dim * max_len; 0 for other formats)."""
-    if cfg.kv_format != DUO_KV_INT8:
-        return 0
+def prefill_staging_bytes(cfg: Config) -> int:
+    """Workspace bytes that let every prefill stage what it can: for an int8
+    cache the stored rows as bf16 K and V (4 * batch * retrieval KV heads *
+    head_dim * max_len), with rotary embedding the streaming heads' turned
+    chunk K rows (2 * batch * streaming KV heads * head_dim * max_len)."""
     n_r = sum(1 for x in cfg.kv_head_is_retrieval if x)
-    return 4 * cfg.batch * n_r * cfg.head_dim * cfg.max_len
+    n_s = cfg.num_kv_heads - n_r
+    out = 0
+    if cfg.kv_format == DUO_KV_INT8:
+        out += 4 * cfg.batch * n_r * cfg.head_dim * cfg.max_len
+    if cfg.rope_base > 0:
+        out += 2 * cfg.batch * n_s * cfg.head_dim * cfg.max_len
+    return out
 
 
 def required_bytes(cfg: Config) -> int:

@@ -157,6 +157,35 @@ __global__ __launch_bounds__(kAppendThreads) void stage_kernel(Geom g, Seqs q, c
   }
 }
 
+// With rotary embedding: the chunk's K rows of every streaming head turned
+// to their positions once per call, into [B][nS][rows][D] (the prefill's
+// tiles then load them as they are, instead of turning them in every
+// work-group that reads them).  One block per (sequence, streaming head,
+// 64 rows); sequences without new rows are skipped.
+template <int D>
+__global__ __launch_bounds__(kAppendThreads) void turn_kernel(Geom g, Seqs q, const uint16_t* __restrict__ k,
+                                                              uint16_t* __restrict__ rot, int32_t rows, int32_t xr) {
+  constexpr int CH = D / 8;
+  constexpr int ROWS_PER_PASS = kAppendThreads / CH;
+  const int id = blockIdx.x;
+  const int x = id % xr;
+  const int idx = (id / xr) % g.nS;
+  const int b = id / (xr * g.nS);
+  const int len = q.len[b];
+  const int n = q.n[b];
+  if (n <= 0) return;
+  const int kvh = kv_head_of_unit(g, g.nR + idx);
+  const int c = threadIdx.x % CH;
+  const int64_t base = ((int64_t)b * g.nS + idx) * rows;
+  for (int i = x * kRowsPerBlock + threadIdx.x / CH; i < min(n, (x + 1) * kRowsPerBlock); i += ROWS_PER_PASS) {
+    const int64_t src = (((int64_t)q.off[b] + i) * g.Hkv + kvh) * D;
+    float cs[8], sn[8];
+    rope_angles8_key<D>(len + i, c, g.rope_half, g.rope_rho, cs, sn);
+    reinterpret_cast<uint4*>(rot + (base + i) * D)[c] =
+        rope_apply8<CH>(reinterpret_cast<const uint4*>(k + src)[c], cs, sn, g.rope_half, c);
+  }
+}
+
 // Page-table entries and device lengths written by the host's calls.
 __global__ __launch_bounds__(kAppendThreads) void word_writes_kernel(int32_t* base, WordWrites w) {
   for (int i = threadIdx.x; i < w.n; i += blockDim.x) base[w.index[i]] = w.value[i];
@@ -208,6 +237,17 @@ hipError_t launch_stage(const Geom& g, const Seqs& q, const uint16_t* k, const u
   else
     hipLaunchKernelGGL(stage_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, v, st_k, st_v,
                        rows, xr, (int32_t)with_chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_turn(const Geom& g, const Seqs& q, const uint16_t* k, uint16_t* rot, int32_t rows, hipStream_t s) {
+  if (rows <= 0 || g.nS <= 0) return hipSuccess;
+  const int32_t xr = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const int64_t blocks = (int64_t)g.B * g.nS * xr;
+  if (g.D == 128)
+    hipLaunchKernelGGL(turn_kernel<128>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, rot, rows, xr);
+  else
+    hipLaunchKernelGGL(turn_kernel<64>, dim3((unsigned)blocks), dim3(kAppendThreads), 0, s, g, q, k, rot, rows, xr);
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ duo_status check_config(const duo_config* c) {
   }
   if (c->fp8_prefill != DUO_FP8_PREFILL_EXACT && c->fp8_prefill != DUO_FP8_PREFILL_MFMA) return DUO_ERR_INVALID_ARG;
   if (c->decode_split != DUO_DECODE_STATIC && c->decode_split != DUO_DECODE_DYNAMIC) return DUO_ERR_INVALID_ARG;
-  if (c->int8_staging_bytes < 0 || (c->int8_staging != nullptr && !aligned16(c->int8_staging)))
+  if (c->prefill_staging_bytes < 0 || (c->prefill_staging != nullptr && !aligned16(c->prefill_staging)))
     return DUO_ERR_INVALID_ARG;
   if (!(c->rope_base >= 0.f) || !std::isfinite(c->rope_base)) return DUO_ERR_INVALID_ARG;
   if (c->rope_base > 0.f && c->rope_style != DUO_ROPE_INTERLEAVED && c->rope_style != DUO_ROPE_HALF)
@@ -114,9 +114,9 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   g->kv_fp8 = c->kv_format == DUO_KV_FP8;
   g->fp8_mfma = g->kv_fp8 && c->fp8_prefill == DUO_FP8_PREFILL_MFMA;
   g->decode_dynamic = c->decode_split == DUO_DECODE_DYNAMIC;
-  if (g->kv_int8 && c->int8_staging != nullptr) {
-    g->int8_staging = static_cast<uint16_t*>(c->int8_staging);
-    g->int8_staging_bytes = c->int8_staging_bytes;
+  if ((g->kv_int8 || c->rope_base > 0.f) && c->prefill_staging != nullptr) {
+    g->prefill_staging = static_cast<uint16_t*>(c->prefill_staging);
+    g->prefill_staging_bytes = c->prefill_staging_bytes;
   }
   {
     const float sk = c->kv_scale_k > 0.f ? c->kv_scale_k : 1.f, sv = c->kv_scale_v > 0.f ? c->kv_scale_v : 1.f;
@@ -188,8 +188,11 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   L->sv_offset = off;
   off = align_up(off + (int64_t)g->B * ns * g->slots * row);
   L->total_bytes = off;
-  // the staging workspace of a prefill that reads rows up to max_len
-  L->int8_staging_bytes = g->kv_int8 ? 4 * (int64_t)g->B * nr * g->D * g->max_len : 0;
+  // the staging workspace of a prefill that reads rows up to max_len: int8
+  // rows as bf16 K and V, and with rotary embedding the streaming heads'
+  // turned chunk K rows
+  L->prefill_staging_bytes = (g->kv_int8 ? 4 * (int64_t)g->B * nr * g->D * g->max_len : 0) +
+                             (c->rope_base > 0.f ? 2 * (int64_t)g->B * ns * g->D * g->max_len : 0);
   L->n_retrieval = nr;
   L->n_streaming = ns;
   L->slots_per_streaming_head = g->slots;

@@ -32,8 +32,8 @@ struct Geom {
   float fp8_scale_k, fp8_scale_v, fp8_inv_k, fp8_inv_v;
   int64_t max_len;
   float scale_log2;           // softmax scale * log2(e): scores in base-2 units
-  uint16_t* int8_staging;     // kv_int8: caller's workspace for bf16 rows staged by a prefill (or null)
-  int64_t int8_staging_bytes;
+  uint16_t* prefill_staging;     // kv_int8 or rope: caller's workspace for bf16 rows a prefill stages (or null)
+  int64_t prefill_staging_bytes;
   int32_t rope;               // rotary position embedding applied to q and k
   int32_t rope_half;          // pairs (i, i + D/2) instead of (2i, 2i + 1)
   double rope_rho;            // rotary base^(-2/D): pair i turns by rho^i per position
@@ -163,6 +163,9 @@ hipError_t launch_decode(const Geom& g, const Seqs& q, const DecodePlan& p,
 // [B][nR][rows][D] at st_k / st_v.
 hipError_t launch_stage(const Geom& g, const Seqs& q, const uint16_t* k, const uint16_t* v, uint16_t* st_k,
                         uint16_t* st_v, int64_t rows, bool with_chunk, hipStream_t s);
+// With rotary embedding: the chunk's K rows of every streaming head turned
+// (as every K rotation turns them) into rot [B][nS][rows][D].
+hipError_t launch_turn(const Geom& g, const Seqs& q, const uint16_t* k, uint16_t* rot, int32_t rows, hipStream_t s);
 hipError_t launch_prefill_fp8(const Geom& g, const Seqs& q, const uint16_t* qin, int32_t max_n, uint16_t* out,
                               hipStream_t s);
 

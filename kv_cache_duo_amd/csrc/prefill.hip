@@ -74,6 +74,11 @@ struct PrefillArgs {
   int32_t tq;         // tokens per query tile
   int32_t n_hc;       // G / gh
   int32_t items_r;    // work-groups of retrieval heads
+  // rotary embedding with the staging workspace: the chunk's K rows of every
+  // streaming head, turned once per call, [B][nS][rot_n][D] (null: turned
+  // in every tile that holds them)
+  const uint16_t* rot_k;
+  int32_t rot_n;
 };
 
 // LDS has 64 banks of 4 bytes; a wave's 16-byte reads are served 16 lanes
@@ -120,9 +125,15 @@ __device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
 // Q8: the retrieval cache holds int8 rows (DUO_KV_INT8) and some sequence
 // has a stored prefix; tiles with stored retrieval rows are then staged
 // through registers and dequantized into the bf16 LDS layout.
-// ROPE: rotary position embedding.  With Q8 as well (an int8 cache with
-// rotary embedding, prefix or not) every retrieval tile is staged: stored
-// rows dequantized, the chunk's rows turned to their positions.
+// ROPE: rotary position embedding; q is turned in the prologue.  ROPE 1:
+// every turned key comes from memory (retrieval rows from the cache, which
+// holds them turned; the streaming heads' chunk rows from the call's turned
+// copy, PrefillArgs::rot_k), so tiles load straight into LDS as without
+// rotation.  ROPE 2: the streaming heads' chunk rows are turned in each tile
+// that holds them (staged through registers), and with Q8 as well (an int8
+// cache with rotary embedding, prefix or not) every retrieval tile is
+// staged: stored rows dequantized, the chunk's rows turned to their
+// positions.
 // F8: the retrieval cache holds e4m3 rows (DUO_KV_FP8, exact prefill); the
 // call's own rows are stored first, so every retrieval tile is staged from
 // the cache: codes through registers, decoded at unit scale -- exactly, an
@@ -130,7 +141,7 @@ __device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
 // scale joins q's pre-multiplication and the V scale the final
 // normalisation; both are powers of two, so the result is the bf16 tile
 // engine's over the stored values, bit for bit.
-template <int D, bool Q8, bool ROPE, bool F8 = false>
+template <int D, bool Q8, int ROPE, bool F8 = false>
 __global__ __launch_bounds__(kThreads, 2)
 void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // The K and V tiles of the two pipeline stages are four distinct LDS
@@ -143,7 +154,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char lds_v1[Lds<D>::TILE];
   // ROPE: cos (first D) and sin (next D) of the turn of the ROWS_J positions
   // between the rows a lane stages, per dim
-  __shared__ __attribute__((aligned(16))) float lds_step[ROPE ? 2 * D : 4];
+  __shared__ __attribute__((aligned(16))) float lds_step[ROPE == 2 ? 2 * D : 4];
   using LD = Lds<D>;
   constexpr int CH = D / 8;                 // 16-byte granules per row
   constexpr int RPC = 64 / CH;              // rows per 1 KB wave load (4 or 8)
@@ -319,7 +330,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // (bit j of rotrows: row j is a chunk row whose K is turned in store_tile).
   // Both: retrieval tiles mix stored int8 rows and chunk rows to be turned.
   // F8: a staged retrieval tile's e4m3 granules wait in kst / vst (.x .y).
-  u32x4_t kst[(Q8 || ROPE || F8) ? NJ : 1], vst[(Q8 || ROPE || F8) ? NJ : 1];
+  u32x4_t kst[(Q8 || ROPE == 2 || F8) ? NJ : 1], vst[(Q8 || ROPE == 2 || F8) ? NJ : 1];
   uint32_t q8rows = 0, rotrows = 0;
   int st_k0 = 0;  // first key of the staged tile
   auto load_tile = [&](int tile, char* kbuf, char* vbuf) __attribute__((always_inline)) -> bool {  // true: staged, store_tile to follow
@@ -353,7 +364,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
         return true;
       }
     }
-    if constexpr (Q8 && ROPE) {
+    if constexpr (Q8 && ROPE == 2) {
       if (retrieval) {
         // stored rows (kp < L) as int8 codes + scale, the chunk's rows from
         // the input (turned in store_tile), rows past qmax chunk row 0
@@ -382,7 +393,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
         return true;
       }
     }
-    if constexpr (ROPE && !Q8) {
+    if constexpr (ROPE != 0 && !Q8) {
       if (retrieval) {
         // every key row is in the cache (this chunk's rows were stored,
         // rotated, before the kernel); rows past qmax read row 0 instead
@@ -405,7 +416,29 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
         return false;
       }
     }
-    if constexpr (ROPE) {
+    if constexpr (ROPE == 1) {
+      if (k0 + kBN - 1 >= L) {
+        // a streaming tile with chunk rows whose K rows were turned once for
+        // the call: straight into LDS, K of chunk rows from the turned copy
+        // (rows no query may use read the copy's row 0: masked, finite)
+        const uint16_t* rot = a.rot_k + ((int64_t)b * g.nS + idx) * a.rot_n * D;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int kp = k0 + r0 + j * ROWS_J;
+          const bool in_chunk = kp >= L;
+          const bool ok = kp <= qmax && (in_chunk || kp < g.S || kp >= L - g.W);
+          const bool from_cache = !in_chunk && ok;
+          const int64_t cache_row = kp < g.S ? (int64_t)kp : (int64_t)(g.S + (kp - g.S) % g.W);
+          const int64_t ci = (ok && in_chunk) ? (int64_t)(kp - L) : 0;
+          const uint16_t* ksrc = from_cache ? ck + cache_row * D : rot + ci * D;
+          const uint16_t* vsrc = from_cache ? cv + cache_row * D : a.v + in_base + ci * in_stride;
+          global_to_lds16(ksrc + gK * 8, dst + j * kWaves * 1024);
+          global_to_lds16(vsrc + gV * 8, vdst + j * kWaves * 1024);
+        }
+        return false;
+      }
+    }
+    if constexpr (ROPE == 2) {
       if (k0 + kBN - 1 >= L) {  // a streaming tile with chunk rows: stage it
         st_k0 = k0;
         rotrows = 0;
@@ -502,7 +535,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
         return;
       }
     }
-    if constexpr (ROPE) {
+    if constexpr (ROPE == 2) {
       // chunk K rows turned to their positions (every lane takes part: the
       // half-split pairs exchange values across lanes)
       // the angles of row r0 from fp64 turns; rows r0 + j ROWS_J by complex
@@ -651,14 +684,14 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           }
         }
     }
-    if constexpr (Q8 || ROPE || F8) {
+    if constexpr (Q8 || ROPE == 2 || F8) {
       if (staged) store_tile(knext, vnext);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the direct-to-LDS loads of the next tile
     __syncthreads();
   };
 
-  if constexpr (ROPE && NJ > 1) {  // the turn of ROWS_J positions, per dim: the same for every staged tile
+  if constexpr (ROPE == 2 && NJ > 1) {  // the turn of ROWS_J positions, per dim: the same for every staged tile
     if (threadIdx.x < D / 8) {
       float cs[8], sn[8];
       rope_angles8<D>(ROWS_J, threadIdx.x, g.rope_half, g.rope_rho, cs, sn);
@@ -702,7 +735,7 @@ int heads_per_group(int G) {
   return 1;
 }
 
-template <int D, bool Q8, bool ROPE, bool F8 = false>
+template <int D, bool Q8, int ROPE, bool F8 = false>
 hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, hipStream_t s,
                     bool streaming_only = false) {
   a.tq = kWaves * 32 / a.gh;
@@ -726,60 +759,85 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   a.out = out;
   a.gh = heads_per_group(g.G);
   a.n_hc = g.G / a.gh;
+  a.rot_k = nullptr;
+  a.rot_n = 0;
   // int8 retrieval rows are only read from a stored prefix
   bool prefix = false;
   for (int b = 0; b < g.B; ++b) prefix = prefix || (q.n[b] > 0 && q.len[b] > 0);
-  if (g.kv_fp8 && !g.fp8_mfma) {  // stored e4m3 rows decoded exactly, bf16 matrix cores, one launch
-    if (g.rope)
-      return g.D == 128 ? launch_t<128, false, true, true>(g, q, a, max_n, s)
-                        : launch_t<64, false, true, true>(g, q, a, max_n, s);
-    return g.D == 128 ? launch_t<128, false, false, true>(g, q, a, max_n, s)
-                      : launch_t<64, false, false, true>(g, q, a, max_n, s);
+  // The staging workspace, per call: first the int8 rows (below), then the
+  // streaming heads' turned chunk K rows, each only if the rest has room.
+  uint16_t* ws = g.prefill_staging;
+  const int64_t ws_bytes = ws != nullptr ? g.prefill_staging_bytes : 0;
+  int64_t int8_elems = 0;  // per tensor, when the int8 rows are staged
+  int64_t int8_rows = 0;
+  if (g.kv_int8 && g.nR > 0 && (prefix || g.rope) && ws != nullptr) {
+    for (int i = 0; i < q.nact; ++i) {
+      const int b = q.act[i];
+      const int64_t r = (int64_t)q.len[b] + (g.rope ? q.n[b] : 0);
+      int8_rows = r > int8_rows ? r : int8_rows;
+    }
+    const int64_t elems = (int64_t)g.B * g.nR * int8_rows * g.D;
+    if (int8_rows > 0 && 4 * elems <= ws_bytes) int8_elems = elems;
   }
+  // the int8 kernel that stages its own tiles turns the chunk's rows itself
+  const bool q8_tiles = g.kv_int8 && g.nR > 0 && (prefix || g.rope) && int8_elems == 0;
+  if (g.rope && g.nS > 0 && ws != nullptr && !q8_tiles) {
+    const int64_t rot_elems = (int64_t)g.B * g.nS * max_n * g.D;
+    if (2 * (2 * int8_elems + rot_elems) <= ws_bytes) {
+      uint16_t* rot = ws + 2 * int8_elems;
+      const hipError_t e = launch_turn(g, q, kin, rot, max_n, s);
+      if (e != hipSuccess) return e;
+      a.rot_k = rot;
+      a.rot_n = max_n;
+    }
+  }
+  // rotary mode of the kernels: 1 when every turned key comes from memory
+  // (no streaming heads, or their turned copy), 2 when tiles turn them
+  const int rope = !g.rope ? 0 : (g.nS == 0 || a.rot_k != nullptr) ? 1 : 2;
+  // launch_t for the cache format's flags and the rotary mode
+  auto run = [&](const Geom& gg, auto q8_c, auto f8_c, bool streaming_only = false) -> hipError_t {
+    constexpr bool Q8 = decltype(q8_c)::value, F8 = decltype(f8_c)::value;
+    if (gg.D == 128) {
+      if (rope == 0) return launch_t<128, Q8, 0, F8>(gg, q, a, max_n, s, streaming_only);
+      if constexpr (!Q8) {
+        if (rope == 1) return launch_t<128, Q8, 1, F8>(gg, q, a, max_n, s, streaming_only);
+      }
+      return launch_t<128, Q8, 2, F8>(gg, q, a, max_n, s, streaming_only);
+    }
+    if (rope == 0) return launch_t<64, Q8, 0, F8>(gg, q, a, max_n, s, streaming_only);
+    if constexpr (!Q8) {
+      if (rope == 1) return launch_t<64, Q8, 1, F8>(gg, q, a, max_n, s, streaming_only);
+    }
+    return launch_t<64, Q8, 2, F8>(gg, q, a, max_n, s, streaming_only);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (g.kv_fp8 && !g.fp8_mfma)  // stored e4m3 rows decoded exactly, bf16 matrix cores, one launch
+    return run(g, F(), T());
   if (g.kv_fp8) {  // retrieval heads on fp8 matrix cores, streaming heads here
-    hipError_t e = launch_prefill_fp8(g, q, qin, max_n, out, s);
+    const hipError_t e = launch_prefill_fp8(g, q, qin, max_n, out, s);
     if (e != hipSuccess) return e;
-    if (g.rope)
-      return g.D == 128 ? launch_t<128, false, true>(g, q, a, max_n, s, true)
-                        : launch_t<64, false, true>(g, q, a, max_n, s, true);
-    return g.D == 128 ? launch_t<128, false, false>(g, q, a, max_n, s, true)
-                      : launch_t<64, false, false>(g, q, a, max_n, s, true);
+    return run(g, F(), F(), true);
   }
-  if (g.kv_int8 && g.nR > 0 && (prefix || g.rope) && g.int8_staging != nullptr) {
+  if (int8_elems > 0) {
     // Stage the rows the call reads as bf16 in the caller's workspace (once
     // per call, instead of once per work-group and tile), then attend as
     // over a bf16 cache laid out [B][nR][rows][D]; with rotary embedding the
     // chunk's rows are staged turned, as a bf16 cache would hold them.
-    int64_t rows = 0;
-    for (int i = 0; i < q.nact; ++i) {
-      const int b = q.act[i];
-      const int64_t r = (int64_t)q.len[b] + (g.rope ? q.n[b] : 0);
-      rows = r > rows ? r : rows;
-    }
-    const int64_t elems = (int64_t)g.B * g.nR * rows * g.D;  // per tensor
-    if (rows > 0 && 4 * elems <= g.int8_staging_bytes) {
-      Geom gs = g;
-      gs.kv_int8 = 0;
-      gs.rk = g.int8_staging;
-      gs.rv = g.int8_staging + elems;
-      gs.rks = gs.rvs = nullptr;
-      gs.paged = 0;
-      gs.nblk = 1;
-      gs.max_len = rows;
-      hipError_t e = launch_stage(g, q, kin, vin, gs.rk, gs.rv, rows, g.rope != 0, s);
-      if (e != hipSuccess) return e;
-      if (g.rope)
-        return g.D == 128 ? launch_t<128, false, true>(gs, q, a, max_n, s) : launch_t<64, false, true>(gs, q, a, max_n, s);
-      return g.D == 128 ? launch_t<128, false, false>(gs, q, a, max_n, s) : launch_t<64, false, false>(gs, q, a, max_n, s);
-    }
+    Geom gs = g;
+    gs.kv_int8 = 0;
+    gs.rk = ws;
+    gs.rv = ws + int8_elems;
+    gs.rks = gs.rvs = nullptr;
+    gs.paged = 0;
+    gs.nblk = 1;
+    gs.max_len = int8_rows;
+    const hipError_t e = launch_stage(g, q, kin, vin, gs.rk, gs.rv, int8_rows, g.rope != 0, s);
+    if (e != hipSuccess) return e;
+    return run(gs, F(), F());
   }
-  if (g.rope && g.kv_int8 && g.nR > 0)  // stored rows as int8, the chunk's rows turned from the input
-    return g.D == 128 ? launch_t<128, true, true>(g, q, a, max_n, s) : launch_t<64, true, true>(g, q, a, max_n, s);
-  if (g.rope)
-    return g.D == 128 ? launch_t<128, false, true>(g, q, a, max_n, s) : launch_t<64, false, true>(g, q, a, max_n, s);
-  if (g.kv_int8 && g.nR > 0 && prefix)
-    return g.D == 128 ? launch_t<128, true, false>(g, q, a, max_n, s) : launch_t<64, true, false>(g, q, a, max_n, s);
-  return g.D == 128 ? launch_t<128, false, false>(g, q, a, max_n, s) : launch_t<64, false, false>(g, q, a, max_n, s);
+  if (q8_tiles) return run(g, T(), F());  // stored rows as int8 (with rotary embedding: chunk rows turned per tile)
+  return run(g, F(), F());
 }
 
 }  // namespace duo

@@ -35,10 +35,10 @@ def new_cache(batch, hq, hkv, d, max_len, sink, recent, mask, poison=True):
 
 def staging_workspace(cfg, nbytes=None):
     """Attach an int8 prefill staging workspace to cfg (all of
-    int8_staging_bytes(cfg) by default), filled with 0xFF bytes: a staged row
+    prefill_staging_bytes(cfg) by default), filled with 0xFF bytes: a staged row
     read before it is written would be a bf16 NaN and poison the output."""
-    n = duo.int8_staging_bytes(cfg) if nbytes is None else nbytes
-    cfg.int8_staging = torch.full((max(n, 16),), 0xFF, dtype=torch.uint8, device="cuda")[:n] if n else None
+    n = duo.prefill_staging_bytes(cfg) if nbytes is None else nbytes
+    cfg.prefill_staging = torch.full((max(n, 16),), 0xFF, dtype=torch.uint8, device="cuda")[:n] if n else None
     return cfg
 
 

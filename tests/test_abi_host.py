@@ -174,21 +174,27 @@ def test_int8_layout():
     assert e.value.status == duo.DUO_ERR_INVALID_ARG
 
 
-def test_int8_staging_workspace_size_and_checks():
-    """The layout reports the staging workspace that serves every prefill of
-    an int8 cache (4 B nR D max_len bytes; 0 for the other formats), and the
-    configuration's workspace must be 16-byte aligned with a size >= 0."""
+def test_prefill_staging_workspace_size_and_checks():
+    """The layout reports the staging workspace that serves every prefill:
+    4 B nR D max_len bytes for an int8 cache, plus 2 B nS D max_len with
+    rotary embedding (0 otherwise); the configuration's workspace must be
+    16-byte aligned with a size >= 0."""
     cfg = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], kv_format=duo.DUO_KV_INT8)
     lay = _attach(cfg, [5, 7]).layout()
-    assert lay.int8_staging_bytes == duo.int8_staging_bytes(cfg) == 4 * 2 * 2 * 128 * 1000
+    assert lay.prefill_staging_bytes == duo.prefill_staging_bytes(cfg) == 4 * 2 * 2 * 128 * 1000
     for fmt in (duo.DUO_KV_BF16, duo.DUO_KV_FP8):
         other = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], kv_format=fmt)
-        assert _attach(other, [5, 7]).layout().int8_staging_bytes == 0 == duo.int8_staging_bytes(other)
+        assert _attach(other, [5, 7]).layout().prefill_staging_bytes == 0 == duo.prefill_staging_bytes(other)
+    # rotary embedding adds the streaming heads' turned chunk K rows (any format)
+    for fmt, extra in ((duo.DUO_KV_BF16, 0), (duo.DUO_KV_INT8, 4 * 2 * 2 * 128 * 1000)):
+        rope = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], kv_format=fmt, rope_base=10000.0)
+        want = extra + 2 * 2 * 2 * 128 * 1000
+        assert _attach(rope, [5, 7]).layout().prefill_staging_bytes == want == duo.prefill_staging_bytes(rope)
     lib = duo.load_library()
     for ptr, nbytes, ok in ((FAKE, 1 << 20, True), (None, 0, True), (FAKE + 8, 1 << 20, False), (FAKE, -1, False)):
         c, _mask = cfg._c()
-        c.int8_staging = ptr
-        c.int8_staging_bytes = nbytes
+        c.prefill_staging = ptr
+        c.prefill_staging_bytes = nbytes
         req = ctypes.c_size_t(0)
         st = lib.duo_cache_init(ctypes.byref(c), None, 0, ctypes.byref(req), None, None)
         assert (st == duo.DUO_OK) == ok, (ptr, nbytes, st)

@@ -29,7 +29,7 @@ def _say(msg):
 
 
 def new_cache_q8(batch, hq, hkv, d, max_len, sink, recent, mask, staged=False, **kw):
-    """staged: with a full prefill staging workspace (int8_staging), else none
+    """staged: with a full prefill staging workspace (prefill_staging), else none
     (every tile decodes its stored rows)."""
     cfg = duo.Config(batch, hq, hkv, d, max_len, sink, recent, [int(x) for x in mask], kv_format=duo.DUO_KV_INT8,
                      **kw)
@@ -221,7 +221,7 @@ def test_q8_staged_prefill_equals_tiled(variant):
     small = 4 * b_n * n_r * d * 820
     outs = {}
     caches = {}
-    for mode, nbytes in (("tiled", None), ("staged", duo.int8_staging_bytes(cfg0)), ("small", small)):
+    for mode, nbytes in (("tiled", None), ("staged", duo.prefill_staging_bytes(cfg0)), ("small", small)):
         cfg = duo.Config(**{**cfg0.__dict__})
         if nbytes is not None:
             staging_workspace(cfg, nbytes)

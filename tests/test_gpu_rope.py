@@ -23,7 +23,7 @@ import torch
 import kv_cache_duo_amd as duo
 from oracle import attend_rows, streaming_slot_positions
 from oracle.rope import apply_rope, pair_dims, round_bf16
-from parity_util import assert_close, require_gpu, run_sequence, to_np32
+from parity_util import assert_close, require_gpu, run_sequence, staging_workspace, to_np32
 from workloads import qkv
 
 pytestmark = pytest.mark.gpu
@@ -241,7 +241,7 @@ def run_sequence_from(cache, q, k, v, start, chunks, steps):
     return run_sequence(cache, q[:, sl].contiguous(), k[:, sl].contiguous(), v[:, sl].contiguous(), chunks, steps)
 
 
-@pytest.mark.parametrize("fmt", ["bf16", "fp8"])
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "bf16_staged"])
 @pytest.mark.parametrize("style", [INTERLEAVED, HALF])
 @pytest.mark.parametrize("d", [64, 128])
 def test_rope_chunked_equals_one_shot_bitwise(d, style, fmt):
@@ -261,6 +261,8 @@ def test_rope_chunked_equals_one_shot_bitwise(d, style, fmt):
     outs, views = {}, {}
     for name, plan in plans.items():
         cfg = duo.Config(b_n, hq, hkv, d, t, 8, 64, mask, rope_base=10000.0, rope_style=style, **kw)
+        if fmt == "bf16_staged":
+            staging_workspace(cfg)
         buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
         cache = duo.duo_cache_init(cfg, buf)
         out = torch.zeros(b_n, t, hq, d, dtype=torch.bfloat16, device="cuda")
@@ -286,3 +288,82 @@ def test_rope_chunked_equals_one_shot_bitwise(d, style, fmt):
     for n in ("rk", "rv", "sk", "sv"):
         a, b = views["one"][n], views["chunked"][n]
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), n
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "int8"])
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
+def test_rope_staged_prefill_equals_tiled(paged, fmt):
+    """With the prefill staging workspace a call turns its streaming heads'
+    chunk K rows once (and an int8 cache's rows are staged); without it every
+    tile turns them.  Both turn a key the one way, so outputs and caches are
+    equal bit for bit -- also when the workspace is too small for the later
+    calls (which then fall back).  Chunks mix sequences with and without new
+    rows and windows that straddle the chunk boundary."""
+    require_gpu()
+    _say(f"rope staged == tiled, {fmt} paged={paged}")
+    mask = [1, 0, 0, 1]
+    b_n, hq, hkv, d, t = 3, 8, 4, 128, 1500
+    kw = dict(rope_base=10000.0, rope_style=HALF)
+    if paged:
+        kw.update(page_tokens=512, num_pages=b_n * 3)
+    if fmt == "fp8":
+        kw.update(kv_format=duo.DUO_KV_FP8)
+    elif fmt == "int8":
+        kw.update(kv_format=duo.DUO_KV_INT8)
+    q, k, v = qkv(b_n, t, hq, hkv, d, 72, "cuda")
+    plan = [[300, 0, 130], [1, 700, 64], [500, 1, 0], [0, 300, 900], [699, 499, 1]]
+    cfg0 = duo.Config(b_n, hq, hkv, d, t, 8, 64, mask, **kw)
+    outs, views = {}, {}
+    # "small": room for the turned rows of the first three calls' chunks only
+    small = 2 * b_n * (hkv - sum(mask)) * d * 700 + (4 * b_n * sum(mask) * d * 820 if fmt == "int8" else 0)
+    for mode, nbytes in (("tiled", None), ("staged", duo.prefill_staging_bytes(cfg0)), ("small", small)):
+        cfg = duo.Config(**{**cfg0.__dict__})
+        if nbytes is not None:
+            staging_workspace(cfg, nbytes)
+        buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
+        cache = duo.duo_cache_init(cfg, buf)
+        done = [0] * b_n
+        res = []
+        for n_new in plan:
+            c = max(n_new)
+            qc = torch.zeros(b_n, c, hq, d, dtype=torch.bfloat16, device="cuda")
+            kc = torch.zeros(b_n, c, hkv, d, dtype=torch.bfloat16, device="cuda")
+            vc = torch.zeros_like(kc)
+            for b in range(b_n):
+                qc[b, :n_new[b]] = q[b, done[b]:done[b] + n_new[b]]
+                kc[b, :n_new[b]] = k[b, done[b]:done[b] + n_new[b]]
+                vc[b, :n_new[b]] = v[b, done[b]:done[b] + n_new[b]]
+            oc = torch.zeros_like(qc)
+            duo.duo_prefill(cache, qc, kc, vc, n_new, oc)
+            res.append(oc)
+            done = [done[b] + n_new[b] for b in range(b_n)]
+        torch.cuda.synchronize()
+        assert all(torch.isfinite(o.float()).all() for o in res), mode
+        outs[mode] = res
+        views[mode] = {n: x.clone() for n, x in duo.cache_views(cache).items()}
+    for mode in ("staged", "small"):
+        for i, (a, b) in enumerate(zip(outs["tiled"], outs[mode])):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), f"{mode} call {i}"
+        for name in views["tiled"]:
+            assert torch.equal(views["tiled"][name].view(torch.uint8), views[mode][name].view(torch.uint8)), \
+                f"{mode} {name}"
+
+
+@pytest.mark.parametrize("staged", [False, True], ids=["tiled", "staged"])
+@pytest.mark.parametrize("d", [64, 128])
+def test_rope_all_retrieval_and_staged_chunks(d, staged):
+    """Every KV head a retrieval head (the kernels then read every turned key
+    from the cache, with or without a workspace), and with streaming heads
+    the staged path (the chunk's turned K rows read from the call's copy)
+    checked against the oracle on chunked prefill and decode."""
+    require_gpu()
+    _say(f"all retrieval + staged d={d} staged={staged}")
+    for mask in ([1, 1, 1, 1], [1, 0, 0, 1]):
+        q, k, v = qkv(2, 420, 8, 4, d, 73, "cuda")
+        cfg = duo.Config(2, 8, 4, d, 420, 4, 16, mask, rope_base=10000.0, rope_style=INTERLEAVED)
+        if staged:
+            staging_workspace(cfg)
+        buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
+        cache = duo.duo_cache_init(cfg, buf)
+        run_and_check(cache, q, k, v, mask, [[100, 50], [64, 1], [1, 63], [0, 130], [130, 100]], 6, 10000.0,
+                      INTERLEAVED, f"mask {mask} staged={staged}")
