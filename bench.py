@@ -31,8 +31,8 @@ Legs (--legs, each with its own fixed repetitions):
              the headline step over an int8 / fp8 retrieval cache (int8rope:
              int8 with rotary embedding; fp8mfma: retrieval prefill on fp8
              matrix cores), with rotary embedding, over a paged cache, and
-             with the dynamic decode split; the rotary legs run with the
-             prefill staging workspace and once without it (tiled)
+             with the dynamic decode split; the rotary and fp8 legs run
+             with the prefill staging workspace and once without it (tiled)
   cpu_baseline  the fp64 oracle on a bounded sample of the headline
              workload (decode and prefill rows), with all host cores and
              with one, and the full workload's oracle time extrapolated
@@ -705,8 +705,19 @@ def main():
         result["int8rope"]["tiled_prefill_time_vs_bf16"] = tiled["prefill_time_vs_bf16"]
         torch.cuda.empty_cache()
     if "fp8" in legs:
-        result["fp8"] = {**variant("fp8", fp8_row(w), kv_format=duo.DUO_KV_FP8),
-                         "cache": "retrieval K/V as e4m3 codes, one power-of-two scale per tensor (DUO_KV_FP8)"}
+        # exact prefill: the stored rows decoded once per call into the
+        # staging workspace (the default here), or in every tile
+        # (tiled_prefill_ms)
+        stg = torch.empty(duo.prefill_staging_bytes(dataclasses.replace(cfgs[0], kv_format=duo.DUO_KV_FP8)),
+                          dtype=torch.uint8, device=R.dev)
+        result["fp8"] = {**variant("fp8", fp8_row(w), kv_format=duo.DUO_KV_FP8, prefill_staging=stg),
+                         "cache": "retrieval K/V as e4m3 codes, one power-of-two scale per tensor (DUO_KV_FP8)",
+                         "staging_bytes": stg.numel()}
+        del stg
+        tiled = variant("fp8_tiled", fp8_row(w), kv_format=duo.DUO_KV_FP8)
+        result["fp8"]["tiled_prefill_ms"] = tiled["prefill_ms_per_call"]
+        result["fp8"]["tiled_prefill_time_vs_bf16"] = tiled["prefill_time_vs_bf16"]
+        torch.cuda.empty_cache()
     if "fp8mfma" in legs and hasattr(duo, "DUO_FP8_PREFILL_MFMA"):
         result["fp8mfma"] = {**variant("fp8mfma", fp8_row(w), FP8_MFMA_PEAK_TFLOPS, kv_format=duo.DUO_KV_FP8,
                                        fp8_prefill=duo.DUO_FP8_PREFILL_MFMA),

@@ -166,15 +166,20 @@ typedef struct duo_config {
    *     4 * batch * retrieval KV heads * head_dim * rows bytes, rows = the
    *     largest len_b (len_b + n_new[b] with rotary embedding) among the
    *     sequences it extends;
+   *   - DUO_KV_FP8 with DUO_FP8_PREFILL_EXACT: every retrieval row it reads,
+   *     its own chunk's among them (stored first), as code * scale in bf16
+   *     (exact): 4 * batch * retrieval KV heads * head_dim * rows bytes, rows
+   *     = the largest len_b + n_new[b];
    *   - rotary embedding (any format): the chunk's K rows of every streaming
    *     head, turned: 2 * batch * streaming KV heads * head_dim * chunk
-   *     bytes, after the int8 rows.
+   *     bytes, after the 8-bit rows.
    * Each part is used when the workspace has room for it (and, for the
    * turned rows, when the int8 rows are staged or the cache is not int8);
    * otherwise the tiles prepare those rows themselves.  duo_layout.
    * prefill_staging_bytes is the most any call needs.  Both ways attend the
-   * same values (a stored int8 row as code * scale rounded once to bf16, a
-   * key turned as every K rotation turns it) and give bitwise equal outputs.
+   * same values (a stored int8 row as code * scale rounded once to bf16, an
+   * fp8 row as code * scale, a key turned as every K rotation turns it) and
+   * give bitwise equal outputs.
    * Caches whose calls run in order on one stream may share one workspace.
    * NULL / 0: no workspace. */
   void* prefill_staging;
@@ -224,8 +229,9 @@ typedef struct duo_layout {
                                        (written by a decode call before it reads them; their contents
                                        between calls are unspecified) */
   int64_t prefill_staging_bytes;    /* the duo_config.prefill_staging size that serves every prefill call:
-                                       4 * B * nR * D * max_len for DUO_KV_INT8, plus 2 * B * nS * D * max_len
-                                       with rotary embedding; 0 when neither applies */
+                                       4 * B * nR * D * max_len for DUO_KV_INT8 and for DUO_KV_FP8 with exact
+                                       prefill, plus 2 * B * nS * D * max_len with rotary embedding; 0 when
+                                       none applies */
 } duo_layout;
 
 /* Lay out a new, empty cache in `dev_buf`.  The head-split layout is the

@@ -223,13 +223,14 @@ def _dev(t: torch.Tensor, shape, name: str) -> int:
 
 def prefill_staging_bytes(cfg: Config) -> int:
     """Workspace bytes that let every prefill stage what it can: for an int8
-    cache the stored rows as bf16 K and V (4 * batch * retrieval KV heads *
-    head_dim * max_len), with rotary embedding the streaming heads' turned
-    chunk K rows (2 * batch * streaming KV heads * head_dim * max_len)."""
+    cache, and an fp8 cache with exact prefill, the retrieval rows as bf16 K
+    and V (4 * batch * retrieval KV heads * head_dim * max_len), with rotary
+    embedding the streaming heads' turned chunk K rows (2 * batch *
+    streaming KV heads * head_dim * max_len)."""
     n_r = sum(1 for x in cfg.kv_head_is_retrieval if x)
     n_s = cfg.num_kv_heads - n_r
     out = 0
-    if cfg.kv_format == DUO_KV_INT8:
+    if cfg.kv_format == DUO_KV_INT8 or (cfg.kv_format == DUO_KV_FP8 and cfg.fp8_prefill == DUO_FP8_PREFILL_EXACT):
         out += 4 * cfg.batch * n_r * cfg.head_dim * cfg.max_len
     if cfg.rope_base > 0:
         out += 2 * cfg.batch * n_s * cfg.head_dim * cfg.max_len

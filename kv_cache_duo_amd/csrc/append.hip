@@ -106,11 +106,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(Geom g, Seqs q, 
   }
 }
 
-// The retrieval rows that a prefill over an int8 cache reads, written once
-// per call as bf16 into a staging area [B][nR][rows][D] (K and V apart): the
-// stored prefix [0, len) decoded (code * scale rounded to bf16, the value a
-// tile decoded in the attention kernel would hold), and with rotary
-// embedding the chunk's own rows too, K turned to its position, V as given.
+// The retrieval rows that a prefill over an 8-bit cache reads, written once
+// per call as bf16 into a staging area [B][nR][rows][D] (K and V apart).
+// int8: the stored prefix [0, len) decoded (code * scale rounded to bf16,
+// the value a tile decoded in the attention kernel would hold), and with
+// rotary embedding the chunk's own rows too, K turned to its position, V as
+// given.  fp8 (exact prefill): every row [0, len + n), the call's own rows
+// stored before the attention, as code * scale (exact in bf16).
 // One block per (sequence, retrieval head, 64 rows); sequences without new
 // rows in the call are skipped.
 template <int D>
@@ -128,7 +130,10 @@ __global__ __launch_bounds__(kAppendThreads) void stage_kernel(Geom g, Seqs q, c
   const int len = q.len[b];
   const int n = q.n[b];
   if (n <= 0) return;
-  const int count = len + (with_chunk ? n : 0);
+  // fp8: the call's own rows are stored before the attention, so every row
+  // comes from the cache
+  const int stored = g.kv_fp8 ? len + n : len;
+  const int count = g.kv_fp8 ? len + n : len + (with_chunk ? n : 0);
   const int kvh = kv_head_of_unit(g, idx);
   const int c = threadIdx.x % CH;
   const int64_t base = ((int64_t)b * g.nR + idx) * rows;
@@ -136,12 +141,17 @@ __global__ __launch_bounds__(kAppendThreads) void stage_kernel(Geom g, Seqs q, c
   const uint8_t* rv8 = reinterpret_cast<const uint8_t*>(g.rv);
   for (int p = x * kRowsPerBlock + threadIdx.x / CH; p < min(count, (x + 1) * kRowsPerBlock); p += ROWS_PER_PASS) {
     uint4 kx, vx;
-    if (p < len) {
+    if (p < stored) {
       const int64_t rrow = retrieval_row0(g, b, idx, p) + p;
       const uint2 kc = reinterpret_cast<const uint2*>(rk8 + rrow * D)[c];
       const uint2 vc = reinterpret_cast<const uint2*>(rv8 + rrow * D)[c];
-      kx = int8_dequant8(kc.x, kc.y, g.rks[rrow]);
-      vx = int8_dequant8(vc.x, vc.y, g.rvs[rrow]);
+      if (g.kv_fp8) {  // code * scale: exact in bf16 (4 significant bits, a power-of-two scale)
+        kx = fp8_to_bf16x8(kc.x, kc.y, g.fp8_scale_k);
+        vx = fp8_to_bf16x8(vc.x, vc.y, g.fp8_scale_v);
+      } else {
+        kx = int8_dequant8(kc.x, kc.y, g.rks[rrow]);
+        vx = int8_dequant8(vc.x, vc.y, g.rvs[rrow]);
+      }
     } else {
       const int64_t src = (((int64_t)q.off[b] + (p - len)) * g.Hkv + kvh) * D;
       kx = reinterpret_cast<const uint4*>(k + src)[c];

@@ -132,6 +132,17 @@ __device__ __forceinline__ float2 fp8_unpack2(uint32_t w) {
   return make_float2(f.x, f.y);
 }
 
+// Eight e4m3 codes (bytes of w0, w1) times a power-of-two scale as bf16
+// pairs: exact (an e4m3 value has 4 significant bits; decoded at unit scale,
+// then scaled in fp32).
+__device__ __forceinline__ uint4 fp8_to_bf16x8(uint32_t w0, uint32_t w1, float scale) {
+  auto scaled = [scale](uint32_t x) { return pack_bf16x2(bf16_lo(x) * scale, bf16_hi(x) * scale); };
+  return make_uint4(scaled(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false))),
+                    scaled(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true))),
+                    scaled(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false))),
+                    scaled(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true))));
+}
+
 // The 8 bf16 values x as an fp8 cache stores them: code * scale, which
 // bf16 holds exactly (e4m3 values have 4 significant bits).
 __device__ __forceinline__ uint4 fp8_roundtrip8(const uint4& x, float inv_scale, float scale) {

@@ -114,7 +114,7 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   g->kv_fp8 = c->kv_format == DUO_KV_FP8;
   g->fp8_mfma = g->kv_fp8 && c->fp8_prefill == DUO_FP8_PREFILL_MFMA;
   g->decode_dynamic = c->decode_split == DUO_DECODE_DYNAMIC;
-  if ((g->kv_int8 || c->rope_base > 0.f) && c->prefill_staging != nullptr) {
+  if ((g->kv_int8 || g->kv_fp8 || c->rope_base > 0.f) && c->prefill_staging != nullptr) {
     g->prefill_staging = static_cast<uint16_t*>(c->prefill_staging);
     g->prefill_staging_bytes = c->prefill_staging_bytes;
   }
@@ -191,7 +191,8 @@ void plan_layout(const duo_config* c, duo::Geom* g, duo_layout* L) {
   // the staging workspace of a prefill that reads rows up to max_len: int8
   // rows as bf16 K and V, and with rotary embedding the streaming heads'
   // turned chunk K rows
-  L->prefill_staging_bytes = (g->kv_int8 ? 4 * (int64_t)g->B * nr * g->D * g->max_len : 0) +
+  L->prefill_staging_bytes = ((g->kv_int8 || (g->kv_fp8 && !g->fp8_mfma)) ? 4 * (int64_t)g->B * nr * g->D * g->max_len
+                                                                           : 0) +
                              (c->rope_base > 0.f ? 2 * (int64_t)g->B * ns * g->D * g->max_len : 0);
   L->n_retrieval = nr;
   L->n_streaming = ns;
@@ -435,9 +436,12 @@ duo_status prefill_call(duo_cache* h, const duo::Seqs& sq, int32_t max_n, const 
   // retrieval rows are stored (rotated) first and the attention reads every
   // retrieval key from the cache; streaming heads rotate their chunk rows
   // as they load them.
-  // An fp8 cache stores the retrieval rows first as well: its prefill reads
-  // every retrieval key and value as stored.
-  const bool store_first = h->geom.rope || h->geom.kv_fp8;
+  // A bf16 or fp8 cache stores the retrieval rows first as well: its
+  // prefill reads every retrieval key and value as stored (contiguous rows
+  // of one head, rather than rows strided by the input's heads).  An int8
+  // cache without rotary embedding attends its chunk's own rows at input
+  // precision, read from the input.
+  const bool store_first = h->geom.rope || !h->geom.kv_int8;
   if (store_first) e = duo::launch_append(h->geom, sq, kk, vv, max_n, s, duo::kAppendRetrieval);
   if (e == hipSuccess)
     e = duo::launch_prefill(h->geom, sq, static_cast<const uint16_t*>(q), kk, vv, max_n, static_cast<uint16_t*>(out),

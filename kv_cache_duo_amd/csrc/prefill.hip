@@ -134,6 +134,9 @@ __device__ __forceinline__ uint32_t scaled_pair(uint32_t w, float s) {
 // cache with rotary embedding, prefix or not) every retrieval tile is
 // staged: stored rows dequantized, the chunk's rows turned to their
 // positions.
+// ROPE 3: no rotation, and every retrieval key and value row comes from the
+// cache, the call's own rows too (they were stored first): a bf16 cache, and
+// the exact fp8 prefill over rows staged as bf16 in the caller's workspace.
 // F8: the retrieval cache holds e4m3 rows (DUO_KV_FP8, exact prefill); the
 // call's own rows are stored first, so every retrieval tile is staged from
 // the cache: codes through registers, decoded at unit scale -- exactly, an
@@ -241,7 +244,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     const bool ok = my_i <= i_hi;
     const uint4* src = reinterpret_cast<const uint4*>(a.q + (((int64_t)sq.off[b] + (ok ? my_i : i_lo)) * g.Hq + h) * D);
     const float s = ok ? c2 : 0.f;
-    if constexpr (ROPE) {
+    if constexpr (ROPE == 1 || ROPE == 2) {
       // k-step c holds dims 16c + 8 half + 0..7 (chunk 2c + half of the
       // row): interleaved pairs lie inside it; half-split pairs join k-step c
       // with c + QC/2 (dims d and d + D/2), in this same lane.
@@ -396,7 +399,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     if constexpr (ROPE != 0 && !Q8) {
       if (retrieval) {
         // every key row is in the cache (this chunk's rows were stored,
-        // rotated, before the kernel); rows past qmax read row 0 instead
+        // rotated or as fp8 values, before the kernel); rows past qmax read
+        // row k0 instead
         if (k0 + kBN - 1 <= qmax) {
           const uint16_t* kb = ckr + (int64_t)k0 * D + koff_c;
           const uint16_t* vb = cvr + (int64_t)k0 * D + voff_c;
@@ -768,12 +772,13 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
   // streaming heads' turned chunk K rows, each only if the rest has room.
   uint16_t* ws = g.prefill_staging;
   const int64_t ws_bytes = ws != nullptr ? g.prefill_staging_bytes : 0;
-  int64_t int8_elems = 0;  // per tensor, when the int8 rows are staged
+  int64_t int8_elems = 0;  // per tensor, when the 8-bit rows are staged
   int64_t int8_rows = 0;
-  if (g.kv_int8 && g.nR > 0 && (prefix || g.rope) && ws != nullptr) {
-    for (int i = 0; i < q.nact; ++i) {
+  const bool fp8_exact = g.kv_fp8 && !g.fp8_mfma;
+  if (((g.kv_int8 && (prefix || g.rope)) || fp8_exact) && g.nR > 0 && ws != nullptr) {
+    for (int i = 0; i < q.nact; ++i) {  // fp8: every row, the call's own stored first
       const int b = q.act[i];
-      const int64_t r = (int64_t)q.len[b] + (g.rope ? q.n[b] : 0);
+      const int64_t r = (int64_t)q.len[b] + ((g.rope || fp8_exact) ? q.n[b] : 0);
       int8_rows = r > int8_rows ? r : int8_rows;
     }
     const int64_t elems = (int64_t)g.B * g.nR * int8_rows * g.D;
@@ -792,8 +797,12 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
     }
   }
   // rotary mode of the kernels: 1 when every turned key comes from memory
-  // (no streaming heads, or their turned copy), 2 when tiles turn them
-  const int rope = !g.rope ? 0 : (g.nS == 0 || a.rot_k != nullptr) ? 1 : 2;
+  // (no streaming heads, or their turned copy), 2 when tiles turn them; 3
+  // (no rotation): every retrieval row from memory, the call's own among
+  // them (a bf16 cache, or fp8 rows staged as bf16)
+  const bool stored_bf16 = !g.kv_int8 && !g.kv_fp8;
+  const int rope = !g.rope ? ((stored_bf16 || (fp8_exact && int8_elems > 0)) ? 3 : 0)
+                           : (g.nS == 0 || a.rot_k != nullptr) ? 1 : 2;
   // launch_t for the cache format's flags and the rotary mode
   auto run = [&](const Geom& gg, auto q8_c, auto f8_c, bool streaming_only = false) -> hipError_t {
     constexpr bool Q8 = decltype(q8_c)::value, F8 = decltype(f8_c)::value;
@@ -801,20 +810,26 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
       if (rope == 0) return launch_t<128, Q8, 0, F8>(gg, q, a, max_n, s, streaming_only);
       if constexpr (!Q8) {
         if (rope == 1) return launch_t<128, Q8, 1, F8>(gg, q, a, max_n, s, streaming_only);
+        if constexpr (!F8) {
+          if (rope == 3) return launch_t<128, Q8, 3, F8>(gg, q, a, max_n, s, streaming_only);
+        }
       }
       return launch_t<128, Q8, 2, F8>(gg, q, a, max_n, s, streaming_only);
     }
     if (rope == 0) return launch_t<64, Q8, 0, F8>(gg, q, a, max_n, s, streaming_only);
     if constexpr (!Q8) {
       if (rope == 1) return launch_t<64, Q8, 1, F8>(gg, q, a, max_n, s, streaming_only);
+      if constexpr (!F8) {
+        if (rope == 3) return launch_t<64, Q8, 3, F8>(gg, q, a, max_n, s, streaming_only);
+      }
     }
     return launch_t<64, Q8, 2, F8>(gg, q, a, max_n, s, streaming_only);
   };
   using T = std::true_type;
   using F = std::false_type;
-  if (g.kv_fp8 && !g.fp8_mfma)  // stored e4m3 rows decoded exactly, bf16 matrix cores, one launch
+  if (fp8_exact && int8_elems == 0)  // stored e4m3 rows decoded exactly in the tiles, bf16 matrix cores
     return run(g, F(), T());
-  if (g.kv_fp8) {  // retrieval heads on fp8 matrix cores, streaming heads here
+  if (g.kv_fp8 && !fp8_exact) {  // retrieval heads on fp8 matrix cores, streaming heads here
     const hipError_t e = launch_prefill_fp8(g, q, qin, max_n, out, s);
     if (e != hipSuccess) return e;
     return run(g, F(), F(), true);
@@ -823,9 +838,12 @@ hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, con
     // Stage the rows the call reads as bf16 in the caller's workspace (once
     // per call, instead of once per work-group and tile), then attend as
     // over a bf16 cache laid out [B][nR][rows][D]; with rotary embedding the
-    // chunk's rows are staged turned, as a bf16 cache would hold them.
+    // int8 chunk's rows are staged turned, as a bf16 cache would hold them
+    // (fp8 values are staged times their power-of-two scales, exactly, so
+    // the bf16 kernel attends the same values as the fp8 tiles would).
     Geom gs = g;
     gs.kv_int8 = 0;
+    gs.kv_fp8 = 0;
     gs.rk = ws;
     gs.rv = ws + int8_elems;
     gs.rks = gs.rvs = nullptr;

@@ -34,7 +34,7 @@ def new_cache(batch, hq, hkv, d, max_len, sink, recent, mask, poison=True):
 
 
 def staging_workspace(cfg, nbytes=None):
-    """Attach an int8 prefill staging workspace to cfg (all of
+    """Attach a prefill staging workspace to cfg (all of
     prefill_staging_bytes(cfg) by default), filled with 0xFF bytes: a staged row
     read before it is written would be a bf16 NaN and poison the output."""
     n = duo.prefill_staging_bytes(cfg) if nbytes is None else nbytes

@@ -176,14 +176,15 @@ def test_int8_layout():
 
 def test_prefill_staging_workspace_size_and_checks():
     """The layout reports the staging workspace that serves every prefill:
-    4 B nR D max_len bytes for an int8 cache, plus 2 B nS D max_len with
-    rotary embedding (0 otherwise); the configuration's workspace must be
-    16-byte aligned with a size >= 0."""
-    cfg = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], kv_format=duo.DUO_KV_INT8)
-    lay = _attach(cfg, [5, 7]).layout()
-    assert lay.prefill_staging_bytes == duo.prefill_staging_bytes(cfg) == 4 * 2 * 2 * 128 * 1000
-    for fmt in (duo.DUO_KV_BF16, duo.DUO_KV_FP8):
-        other = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], kv_format=fmt)
+    4 B nR D max_len bytes for an int8 cache and an fp8 one with exact
+    prefill, plus 2 B nS D max_len with rotary embedding (0 otherwise); the
+    configuration's workspace must be 16-byte aligned with a size >= 0."""
+    for kw in (dict(kv_format=duo.DUO_KV_INT8), dict(kv_format=duo.DUO_KV_FP8)):
+        cfg = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], **kw)
+        lay = _attach(cfg, [5, 7]).layout()
+        assert lay.prefill_staging_bytes == duo.prefill_staging_bytes(cfg) == 4 * 2 * 2 * 128 * 1000
+    for kw in (dict(kv_format=duo.DUO_KV_BF16), dict(kv_format=duo.DUO_KV_FP8, fp8_prefill=duo.DUO_FP8_PREFILL_MFMA)):
+        other = _cfg(kv_head_is_retrieval=[0, 1, 1, 0], **kw)
         assert _attach(other, [5, 7]).layout().prefill_staging_bytes == 0 == duo.prefill_staging_bytes(other)
     # rotary embedding adds the streaming heads' turned chunk K rows (any format)
     for fmt, extra in ((duo.DUO_KV_BF16, 0), (duo.DUO_KV_INT8, 4 * 2 * 2 * 128 * 1000)):

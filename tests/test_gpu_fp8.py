@@ -31,7 +31,7 @@ import kv_cache_duo_amd as duo
 from fp8_model import assert_fp8_mfma_close, mfma_sigma
 from oracle import attend_rows, streaming_slot_positions
 from oracle.fp8_cache import quantize_rows_fp8, seen_rows_fp8
-from parity_util import assert_close, require_gpu, run_sequence, to_np32
+from parity_util import assert_close, require_gpu, run_sequence, staging_workspace, to_np32
 from workloads import qkv
 
 pytestmark = pytest.mark.gpu
@@ -350,3 +350,51 @@ def test_fp8_exact_prefill_is_bf16_engine_on_stored_values(paged):
         outb, _, _ = run_sequence(bf, q, ks, vs, chunks, 0)
         assert torch.equal(out8.view(torch.int16), outb.view(torch.int16)), \
             (len(chunks), (out8.float() - outb.float()).abs().max().item())
+
+
+@pytest.mark.parametrize("variant", ["contiguous", "paged", "rope", "rope_paged"])
+def test_fp8_staged_exact_prefill_equals_tiled(variant):
+    """Exact prefill with the staging workspace (every retrieval row the call
+    reads decoded once, exactly, to bf16 code * scale, then the bf16 tile
+    engine) and without it (e4m3 tiles decoded in every work-group, scales
+    folded into q and the normalisation): outputs and caches equal bit for
+    bit, with tensor scales 2 and 1/4, also when a workspace too small for
+    the later calls makes them fall back to the tiles.  The chunk plan mixes
+    sequences with and without new rows, prefixes that end inside a tile,
+    and chunks of one row."""
+    require_gpu()
+    _say(f"fp8 staged == tiled, {variant}")
+    mask = [1, 0, 1, 1]
+    b_n, hq, hkv, d, t = 3, 8, 4, 128, 1500
+    sk, sv = 2.0, 0.25
+    kw = {}
+    if "paged" in variant:
+        kw.update(page_tokens=512, num_pages=b_n * 3)
+    if "rope" in variant:
+        kw.update(rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF)
+    q, k, v = qkv(b_n, t, hq, hkv, d, 46, "cuda")
+    k, v = (k.float() * sk).to(torch.bfloat16), (v.float() * sv).to(torch.bfloat16)
+    plan = [[300, 0, 130], [1, 700, 64], [500, 1, 0], [0, 300, 900], [699, 499, 1]]
+    cfg0 = duo.Config(b_n, hq, hkv, d, t, 8, 64, mask, kv_format=duo.DUO_KV_FP8, kv_scale_k=sk, kv_scale_v=sv,
+                      **kw)
+    n_r = sum(mask)
+    # enough for rows up to 830 (the first three calls), not for the last two
+    small = 4 * b_n * n_r * d * 830
+    outs, caches = {}, {}
+    for mode, nbytes in (("tiled", None), ("staged", duo.prefill_staging_bytes(cfg0)), ("small", small)):
+        cfg = duo.Config(**{**cfg0.__dict__})
+        if nbytes is not None:
+            staging_workspace(cfg, nbytes)
+        cache = duo.duo_cache_init(cfg, torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8,
+                                                   device="cuda"))
+        outs[mode], _, _ = run_sequence(cache, q, k, v, plan, 0)
+        caches[mode] = cache
+        torch.cuda.synchronize()
+        assert torch.isfinite(outs[mode].float()).all(), mode
+    for mode in ("staged", "small"):
+        assert torch.equal(outs["tiled"].view(torch.int16), outs[mode].view(torch.int16)), \
+            (mode, (outs["tiled"].float() - outs[mode].float()).abs().max().item())
+        for name in ("rk", "rv", "sk", "sv"):
+            va = duo.cache_views(caches["tiled"])[name]
+            vb = duo.cache_views(caches[mode])[name]
+            assert torch.equal(va.view(torch.uint8), vb.view(torch.uint8)), f"{mode} {name}"

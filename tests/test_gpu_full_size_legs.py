@@ -11,8 +11,9 @@ as the benchmark launches it, with
   * the dynamic decode split,
   * an int8 retrieval cache with rotary embedding,
 
-the rotary legs with the prefill staging workspace (the chunk's K rows
-turned once per call), as the benchmark runs them.
+the rotary and fp8 legs with the prefill staging workspace (the chunk's K
+rows turned, the fp8 rows decoded, once per call), as the benchmark runs
+them.
 
 Sequences 0 and 7 are compared at sampled prefill rows and decode steps, in
 every query head, with the oracle of each format at the bar its own tests
@@ -73,7 +74,7 @@ def _cache(leg, mask, t):
         kw = dict(kv_format=duo.DUO_KV_INT8, rope_base=10000.0, rope_style=duo.DUO_ROPE_HALF)
     cfg = duo.Config(W.batch, W.num_q_heads, W.num_kv_heads, W.head_dim, t, W.sink, W.recent,
                      [int(x) for x in mask], **kw)
-    if leg in ("int8rope", "rope"):  # as the benchmark runs these legs
+    if leg in ("int8rope", "rope", "fp8"):  # as the benchmark runs these legs
         staging_workspace(cfg)
     buf = torch.full((duo.required_bytes(cfg),), 0xFF, dtype=torch.uint8, device="cuda")
     return duo.duo_cache_init(cfg, buf)

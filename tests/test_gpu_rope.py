@@ -294,11 +294,13 @@ def test_rope_chunked_equals_one_shot_bitwise(d, style, fmt):
 @pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged"])
 def test_rope_staged_prefill_equals_tiled(paged, fmt):
     """With the prefill staging workspace a call turns its streaming heads'
-    chunk K rows once (and an int8 cache's rows are staged); without it every
-    tile turns them.  Both turn a key the one way, so outputs and caches are
-    equal bit for bit -- also when the workspace is too small for the later
-    calls (which then fall back).  Chunks mix sequences with and without new
-    rows and windows that straddle the chunk boundary."""
+    chunk K rows once (and an 8-bit cache's retrieval rows are staged as
+    bf16); without it every tile turns them.  Both turn a key the one way, so
+    outputs and caches are equal bit for bit -- also when the workspace is
+    too small for some calls or parts (which then fall back: for fp8 the
+    first call stages its rows but not the turned chunk, the later ones at
+    most the turned chunk).  Chunks mix sequences with and without new rows and
+    windows that straddle the chunk boundary."""
     require_gpu()
     _say(f"rope staged == tiled, {fmt} paged={paged}")
     mask = [1, 0, 0, 1]
