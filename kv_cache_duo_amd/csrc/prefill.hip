@@ -175,11 +175,13 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   // new tokens (longest stored prefix first).  Work-groups go to the 8 XCDs
   // round-robin (blockIdx mod 8).  When every unit (sequence, KV head, head
   // chunk) does the same work and the units of a kind split evenly over the
-  // XCDs, every unit stays on one XCD and that XCD runs its query tiles in
-  // order, so the resident work-groups of a unit stream the same K/V tiles
-  // nearly together and share them in the XCD's L2.  Otherwise (sequences of
-  // different lengths: pinned units would load some XCDs far more than
-  // others) t-major, unit-minor, which spreads every unit over all XCDs.
+  // XCDs, every unit stays on one XCD, and each XCD runs its units one after
+  // another, a unit's query tiles longest first: the XCD's resident
+  // work-groups then belong to one unit, start nearly together and take
+  // nearly the same time, so they stream the same K/V tiles nearly together
+  // and share them in the XCD's L2.  Otherwise (sequences of different
+  // lengths: pinned units would load some XCDs far more than others)
+  // t-major, unit-minor, which spreads every unit over all XCDs.
   int id = blockIdx.x;
   const bool retrieval = id < a.items_r;
   if (!retrieval) id -= a.items_r;
@@ -187,9 +189,9 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
   const int per_t = sq.nact * nkind * a.n_hc;
   int t, rest;
   if (sq.uniform && per_t % kXcds == 0 && (retrieval || a.items_r % kXcds == 0)) {
-    const int x = id % kXcds, k = id / kXcds, per_x = per_t / kXcds;
-    t = a.tiles_max - 1 - k / per_x;
-    rest = x + kXcds * (k % per_x);
+    const int x = id % kXcds, k = id / kXcds;
+    t = a.tiles_max - 1 - k % a.tiles_max;
+    rest = x + kXcds * (k / a.tiles_max);
   } else {
     t = a.tiles_max - 1 - id / per_t;
     rest = id % per_t;
