@@ -74,6 +74,7 @@ struct PrefillArgs {
   int32_t tq;         // tokens per query tile
   int32_t n_hc;       // G / gh
   int32_t items_r;    // work-groups of retrieval heads
+  int32_t xcd_plan;   // 1: retrieval units dealt to the XCDs in snake order (sequences of different lengths)
   // rotary embedding with the staging workspace: the chunk's K rows of every
   // streaming head, turned once per call, [B][nS][rot_n][D] (null: turned
   // in every tile that holds them)
@@ -192,6 +193,28 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     const int x = id % kXcds, k = id / kXcds;
     t = a.tiles_max - 1 - k % a.tiles_max;
     rest = x + kXcds * (k / a.tiles_max);
+  } else if (retrieval && a.xcd_plan) {
+    // Sequences of different lengths: the retrieval units (longest stored
+    // prefix first) are dealt to the XCDs in snake order -- round j deals
+    // units 8j .. 8j+7, every other round in reverse -- and each XCD runs its
+    // units one after another, a unit's query tiles longest first, so that
+    // its resident work-groups again share one unit's K/V tiles in its L2.
+    const int x = id % kXcds;
+    int k = id / kXcds;
+    t = -1;
+    rest = 0;
+    for (int j = 0;; ++j) {
+      const int u = kXcds * j + ((j & 1) ? kXcds - 1 - x : x);
+      if (u >= per_t) break;
+      const int tiles = (sq.n[active_seq(sq, u / (a.n_hc * nkind))] + a.tq - 1) / a.tq;
+      if (k < tiles) {
+        t = tiles - 1 - k;
+        rest = u;
+        break;
+      }
+      k -= tiles;
+    }
+    if (t < 0) return;  // past the end of this XCD's units
   } else {
     t = a.tiles_max - 1 - id / per_t;
     rest = id % per_t;
@@ -747,6 +770,32 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
   a.tq = kWaves * 32 / a.gh;
   a.tiles_max = (max_n + a.tq - 1) / a.tq;
   a.items_r = streaming_only ? 0 : a.tiles_max * q.nact * g.nR * a.n_hc;
+  a.xcd_plan = 0;
+  const int units_r = q.nact * g.nR * a.n_hc;
+  if (!streaming_only && !(q.uniform && units_r % kXcds == 0) && units_r >= 2 * kXcds) {
+    // the kernel's snake deal of the retrieval units, when it balances the
+    // XCDs' work (keys summed over query tiles) within 10%
+    int64_t slots[kXcds] = {}, work[kXcds] = {};
+    for (int j = 0; kXcds * j < units_r; ++j)
+      for (int x = 0; x < kXcds; ++x) {
+        const int u = kXcds * j + ((j & 1) ? kXcds - 1 - x : x);
+        if (u >= units_r) continue;
+        const int b = q.act[u / (a.n_hc * g.nR)];
+        const int64_t tiles = (q.n[b] + a.tq - 1) / a.tq;
+        slots[x] += tiles;
+        work[x] += tiles * (2 * (int64_t)q.len[b] + q.n[b]);
+      }
+    int64_t max_slots = 0, max_work = 0, sum_work = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      max_slots = slots[x] > max_slots ? slots[x] : max_slots;
+      max_work = work[x] > max_work ? work[x] : max_work;
+      sum_work += work[x];
+    }
+    if (10 * kXcds * max_work <= 11 * sum_work) {
+      a.xcd_plan = 1;
+      a.items_r = (int32_t)(kXcds * max_slots);
+    }
+  }
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * q.nact * g.nS * a.n_hc;
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL((prefill_kernel<D, Q8, ROPE, F8>), dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
