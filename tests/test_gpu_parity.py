@@ -83,6 +83,25 @@ def test_gqa_mixed_lengths_and_empty_rows():
     _full_check(cache, q, k, v, mask, sink, recent, chunks, steps, "gqa-mixed")
 
 
+def test_many_units_mixed_lengths():
+    """16 sequences of different lengths, 2 retrieval KV heads each (32
+    retrieval units, G = 4): the first two calls are balanced enough for the
+    prefill's snake deal of units to the 8 XCDs (one-shot rows of 120..600
+    tokens, then 48 rows over those prefixes), the last two are not (skipped
+    sequences, ragged rows) and take the t-major order."""
+    require_gpu()
+    _say("many units, mixed lengths")
+    b_n, mask = 16, [1, 0, 1, 0]
+    sink, recent = 16, 64
+    chunks = [[120 + 32 * i for i in range(b_n)], [48] * b_n,
+              [0 if i % 3 == 0 else 60 + 19 * i for i in range(b_n)], [180 - 10 * i for i in range(b_n)]]
+    steps = 2
+    t = max(sum(c[b] for c in chunks) for b in range(b_n)) + steps
+    q, k, v = qkv(b_n, t, 16, 4, 128, 77, "cuda")
+    cache = new_cache(b_n, 16, 4, 128, t, sink, recent, mask)
+    _full_check(cache, q, k, v, mask, sink, recent, chunks, steps, "many-units")
+
+
 @pytest.mark.parametrize("hq,hkv,mask", [(24, 3, [0, 1, 0]), (6, 2, [1, 0]), (16, 8, [1, 0, 0, 1, 1, 0, 1, 0])])
 def test_group_sizes(hq, hkv, mask):
     """G = 8, 3 and 2: head chunking in prefill and decode."""
