@@ -125,6 +125,40 @@ void finish_seqs(Seqs& q, int32_t batch);
 // Sequence of active slot i (i work-group uniform).
 __device__ __forceinline__ int active_seq(const Seqs& q, int i) { return q.act[i]; }
 
+// Prefill work over sequences of different lengths, dealt to the 8 XCDs of
+// an MI355X (work-group i runs on XCD i mod 8).  Units u = 0 .. units-1
+// (units_per_seq per active sequence, active slot u / units_per_seq, so the
+// longest stored prefix first) go to the XCDs in snake order: round j deals
+// units 8j .. 8j+7, every other round in reverse.  Each XCD runs its units
+// one after another, a unit's query tiles (tq rows) longest first, so its
+// resident work-groups share one unit's K/V tiles in its L2.
+constexpr int kPrefillXcds = 8;
+__host__ __device__ __forceinline__ int snake_unit(int j, int x) {
+  return kPrefillXcds * j + ((j & 1) ? kPrefillXcds - 1 - x : x);
+}
+// Work-group count of the deal (8 x the largest XCD's tile count), or 0 when
+// it would leave the XCDs' work (keys summed over query tiles) more than 10%
+// from even, or there are fewer than 16 units.
+int64_t snake_deal_items(const Seqs& q, int units_per_seq, int tq);
+// Work item `id` of the deal: query tile t of unit u; false past the end of
+// its XCD's units.
+__device__ __forceinline__ bool snake_deal_item(const Seqs& sq, int id, int units, int units_per_seq, int tq, int& t,
+                                                int& u) {
+  const int x = id % kPrefillXcds;
+  int k = id / kPrefillXcds;
+  for (int j = 0;; ++j) {
+    const int v = snake_unit(j, x);
+    if (v >= units) return false;
+    const int tiles = (sq.n[active_seq(sq, v / units_per_seq)] + tq - 1) / tq;
+    if (k < tiles) {
+      t = tiles - 1 - k;
+      u = v;
+      return true;
+    }
+    k -= tiles;
+  }
+}
+
 // Writes of int32 words of the cache buffer (page-table entries, device
 // lengths), carried in the kernel arguments.
 constexpr int kWordWritesPerLaunch = 448;

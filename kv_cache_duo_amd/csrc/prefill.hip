@@ -194,27 +194,8 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     t = a.tiles_max - 1 - k % a.tiles_max;
     rest = x + kXcds * (k / a.tiles_max);
   } else if (retrieval && a.xcd_plan) {
-    // Sequences of different lengths: the retrieval units (longest stored
-    // prefix first) are dealt to the XCDs in snake order -- round j deals
-    // units 8j .. 8j+7, every other round in reverse -- and each XCD runs its
-    // units one after another, a unit's query tiles longest first, so that
-    // its resident work-groups again share one unit's K/V tiles in its L2.
-    const int x = id % kXcds;
-    int k = id / kXcds;
-    t = -1;
-    rest = 0;
-    for (int j = 0;; ++j) {
-      const int u = kXcds * j + ((j & 1) ? kXcds - 1 - x : x);
-      if (u >= per_t) break;
-      const int tiles = (sq.n[active_seq(sq, u / (a.n_hc * nkind))] + a.tq - 1) / a.tq;
-      if (k < tiles) {
-        t = tiles - 1 - k;
-        rest = u;
-        break;
-      }
-      k -= tiles;
-    }
-    if (t < 0) return;  // past the end of this XCD's units
+    // sequences of different lengths: the snake deal of the retrieval units
+    if (!snake_deal_item(sq, id, per_t, nkind * a.n_hc, a.tq, t, rest)) return;
   } else {
     t = a.tiles_max - 1 - id / per_t;
     rest = id % per_t;
@@ -772,28 +753,11 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
   a.items_r = streaming_only ? 0 : a.tiles_max * q.nact * g.nR * a.n_hc;
   a.xcd_plan = 0;
   const int units_r = q.nact * g.nR * a.n_hc;
-  if (!streaming_only && !(q.uniform && units_r % kXcds == 0) && units_r >= 2 * kXcds) {
-    // the kernel's snake deal of the retrieval units, when it balances the
-    // XCDs' work (keys summed over query tiles) within 10%
-    int64_t slots[kXcds] = {}, work[kXcds] = {};
-    for (int j = 0; kXcds * j < units_r; ++j)
-      for (int x = 0; x < kXcds; ++x) {
-        const int u = kXcds * j + ((j & 1) ? kXcds - 1 - x : x);
-        if (u >= units_r) continue;
-        const int b = q.act[u / (a.n_hc * g.nR)];
-        const int64_t tiles = (q.n[b] + a.tq - 1) / a.tq;
-        slots[x] += tiles;
-        work[x] += tiles * (2 * (int64_t)q.len[b] + q.n[b]);
-      }
-    int64_t max_slots = 0, max_work = 0, sum_work = 0;
-    for (int x = 0; x < kXcds; ++x) {
-      max_slots = slots[x] > max_slots ? slots[x] : max_slots;
-      max_work = work[x] > max_work ? work[x] : max_work;
-      sum_work += work[x];
-    }
-    if (10 * kXcds * max_work <= 11 * sum_work) {
+  if (!streaming_only && !(q.uniform && units_r % kXcds == 0)) {
+    const int64_t items = snake_deal_items(q, g.nR * a.n_hc, a.tq);
+    if (items > 0) {
       a.xcd_plan = 1;
-      a.items_r = (int32_t)(kXcds * max_slots);
+      a.items_r = (int32_t)items;
     }
   }
   const int64_t blocks = (int64_t)a.items_r + (int64_t)a.tiles_max * q.nact * g.nS * a.n_hc;
@@ -803,6 +767,28 @@ hipError_t launch_t(const Geom& g, const Seqs& q, PrefillArgs a, int32_t max_n, 
 }
 
 }  // namespace
+
+int64_t snake_deal_items(const Seqs& q, int units_per_seq, int tq) {
+  const int units = q.nact * units_per_seq;
+  if (units < 2 * kPrefillXcds) return 0;
+  int64_t slots[kPrefillXcds] = {}, work[kPrefillXcds] = {};
+  for (int j = 0; kPrefillXcds * j < units; ++j)
+    for (int x = 0; x < kPrefillXcds; ++x) {
+      const int u = snake_unit(j, x);
+      if (u >= units) continue;
+      const int b = q.act[u / units_per_seq];
+      const int64_t tiles = (q.n[b] + tq - 1) / tq;
+      slots[x] += tiles;
+      work[x] += tiles * (2 * (int64_t)q.len[b] + q.n[b]);
+    }
+  int64_t max_slots = 0, max_work = 0, sum_work = 0;
+  for (int x = 0; x < kPrefillXcds; ++x) {
+    max_slots = slots[x] > max_slots ? slots[x] : max_slots;
+    max_work = work[x] > max_work ? work[x] : max_work;
+    sum_work += work[x];
+  }
+  return 10 * kPrefillXcds * max_work <= 11 * sum_work ? kPrefillXcds * max_slots : 0;
+}
 
 hipError_t launch_prefill(const Geom& g, const Seqs& q, const uint16_t* qin, const uint16_t* kin,
                           const uint16_t* vin, int32_t max_n, uint16_t* out, hipStream_t s) {

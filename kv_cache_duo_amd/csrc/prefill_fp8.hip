@@ -68,6 +68,7 @@ struct Fp8Args {
   const uint16_t* q;  // [rows][Hq][D] bf16
   uint16_t* out;      // [rows][Hq][D] bf16
   int32_t tiles_max, gh, tq, n_hc;
+  int32_t xcd_plan;  // 1: the snake deal of units to XCDs (sequences of different lengths)
 };
 
 // 16-byte granule swizzles (by row) of the K and V tiles in LDS.
@@ -112,16 +113,20 @@ __global__ __launch_bounds__(kThreads, 3) void prefill_fp8_kernel(Geom g, Seqs s
   const int half = lane >> 5;
 
   // ---- work item: retrieval units of the sequences with new tokens
-  // (longest stored prefix first), longest query tiles first; a unit stays on
-  // one XCD (blockIdx mod 8) when every unit does the same work and the units
-  // split evenly over the XCDs, else t-major, unit-minor over all XCDs
+  // (longest stored prefix first), longest query tiles first.  When every
+  // unit does the same work and the units split evenly over the XCDs
+  // (blockIdx mod 8), each unit stays on one XCD and each XCD runs its units
+  // one after another; with sequences of different lengths the snake deal of
+  // units to XCDs when it balances, else t-major, unit-minor over all XCDs
   const int id = blockIdx.x;
   const int per_t = sq.nact * g.nR * a.n_hc;
   int t, rest;
   if (sq.uniform && per_t % kXcds == 0) {
-    const int x = id % kXcds, k = id / kXcds, per_x = per_t / kXcds;
-    t = a.tiles_max - 1 - k / per_x;
-    rest = x + kXcds * (k % per_x);
+    const int x = id % kXcds, k = id / kXcds;
+    t = a.tiles_max - 1 - k % a.tiles_max;
+    rest = x + kXcds * (k / a.tiles_max);
+  } else if (a.xcd_plan) {
+    if (!snake_deal_item(sq, id, per_t, g.nR * a.n_hc, a.tq, t, rest)) return;
   } else {
     t = a.tiles_max - 1 - id / per_t;
     rest = id % per_t;
@@ -425,7 +430,15 @@ hipError_t launch_prefill_fp8(const Geom& g, const Seqs& q, const uint16_t* qin,
   a.n_hc = g.G / a.gh;
   a.tq = kWaves * 32 / a.gh;
   a.tiles_max = (max_n + a.tq - 1) / a.tq;
-  const int64_t blocks = (int64_t)a.tiles_max * q.nact * g.nR * a.n_hc;
+  int64_t blocks = (int64_t)a.tiles_max * q.nact * g.nR * a.n_hc;
+  a.xcd_plan = 0;
+  if (!(q.uniform && (q.nact * g.nR * a.n_hc) % kXcds == 0)) {
+    const int64_t items = snake_deal_items(q, g.nR * a.n_hc, a.tq);
+    if (items > 0) {
+      a.xcd_plan = 1;
+      blocks = items;
+    }
+  }
   if (blocks <= 0) return hipSuccess;
   if (g.D == 128)
     hipLaunchKernelGGL(prefill_fp8_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, s, g, q, a);
