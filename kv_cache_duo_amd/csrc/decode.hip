@@ -427,29 +427,72 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Geom g, Seqs sq, Decod
         s[j][gg] = valid ? acc * g.scale_log2 : -INFINITY;
       }
     }
+    // With several query heads per KV head (GC >= 4) the V products
+    // dominate the loop's vector work: dim d of rows 2t and 2t + 1 then goes
+    // as one bf16 pair (v_perm of their words) into one v_dot2 per dim and
+    // head.  (For one head per KV head the plain FMAs measured faster.)
+    constexpr bool kPairV = GC >= 4;
+    uint32_t vpair[kPairV ? kInFlight / 2 : 1][8];
+#pragma unroll
+    for (int t = 0; t < (kPairV ? kInFlight / 2 : 0); ++t) {
+      const uint32_t w0[4] = {vr[2 * t].x, vr[2 * t].y, vr[2 * t].z, vr[2 * t].w};
+      const uint32_t w1[4] = {vr[2 * t + 1].x, vr[2 * t + 1].y, vr[2 * t + 1].z, vr[2 * t + 1].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vpair[t][2 * e] = __builtin_amdgcn_perm(w1[e], w0[e], 0x05040100u);      // low halves
+        vpair[t][2 * e + 1] = __builtin_amdgcn_perm(w1[e], w0[e], 0x07060302u);  // high halves
+      }
+    }
+    // the batch's max per head; rescale only when some lane's max moved (one
+    // wave vote for all heads): elsewhere the factor is exactly 1 (or l and
+    // o are still 0), so skipping it changes nothing, and past the first
+    // rows the max rarely moves
+    float mn[GC], mu[GC];
+    bool moved = false;
 #pragma unroll
     for (int gg = 0; gg < GC; ++gg) {
       float mx = s[0][gg];
 #pragma unroll
       for (int j = 1; j < kInFlight; ++j) mx = fmaxf(mx, s[j][gg]);
-      const float mn = fmaxf(m[gg], mx);
-      const float mu = max_or_zero(mn);
-      const float alpha = exp2_fast(m[gg] - mu);
-      l[gg] *= alpha;
+      mn[gg] = fmaxf(m[gg], mx);
+      mu[gg] = max_or_zero(mn[gg]);
+      moved = moved || mn[gg] > m[gg];
+    }
+    if (__any(moved)) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[gg][e] *= alpha;
+      for (int gg = 0; gg < GC; ++gg) {
+        const float alpha = exp2_fast(m[gg] - mu[gg]);
+        l[gg] *= alpha;
 #pragma unroll
-      for (int j = 0; j < kInFlight; ++j) {
-        const float p = exp2_fast(s[j][gg] - mu);
-        l[gg] += p;
-        const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+        for (int e = 0; e < 8; ++e) o[gg][e] *= alpha;
+      }
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o[gg][2 * e] = fmaf(p, bf16_lo(w[e]), o[gg][2 * e]);
-          o[gg][2 * e + 1] = fmaf(p, bf16_hi(w[e]), o[gg][2 * e + 1]);
+    for (int gg = 0; gg < GC; ++gg) {
+      if constexpr (kPairV) {
+        // rows in pairs: the two weights as one bf16 pair (l sums those same
+        // values), one v_dot2 per dim with the two rows' values of that dim
+#pragma unroll
+        for (int t = 0; t < kInFlight / 2; ++t) {
+          const uint32_t pw = pack_bf16x2(exp2_fast(s[2 * t][gg] - mu[gg]), exp2_fast(s[2 * t + 1][gg] - mu[gg]));
+          l[gg] = dot2_bf16(pw, 0x3f803f80u, l[gg]);  // (1, 1)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[gg][e] = dot2_bf16(vpair[t][e], pw, o[gg][e]);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kInFlight; ++j) {
+          const float p = exp2_fast(s[j][gg] - mu[gg]);
+          l[gg] += p;
+          const uint32_t w[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[gg][2 * e] = fmaf(p, bf16_lo(w[e]), o[gg][2 * e]);
+            o[gg][2 * e + 1] = fmaf(p, bf16_hi(w[e]), o[gg][2 * e + 1]);
+          }
         }
       }
-      m[gg] = mn;
+      m[gg] = mn[gg];
     }
   };
 
