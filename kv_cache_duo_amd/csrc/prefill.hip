@@ -625,6 +625,10 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
     const bool need_mask = k0 + kBN - 1 > blo || (!retrieval && k0 + kBN - 1 >= g.S && k0 < bhi - g.W + 1);
     if (live) {
       f32x16_t sacc[2];
+      // wave priority: raised while this wave issues its matrix-core work
+      // (S^T, then higher for the P V block) and back to 0 for the softmax,
+      // so that the SIMD's other wave takes the vector ALU in between
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int c = 0; c < QC; ++c)
 #pragma unroll
@@ -632,6 +636,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           const bf16x8_t ka = *reinterpret_cast<const bf16x8_t*>(kcur + k_addr(kb2, c));
           sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[c], c == 0 ? negm : sacc[kb2], 0, 0, 0);
         }
+      __builtin_amdgcn_s_setprio(0);
       // masks: causal on the diagonal, band for streaming heads (branch-free)
       if (need_mask) {
         const int lo_win = retrieval ? -1 : max(my_q - g.W, g.S - 1);  // keep kp > lo_win ...
@@ -674,6 +679,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) negm[r] = -mu;
       }
+      __builtin_amdgcn_s_setprio(2);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -694,6 +700,7 @@ void prefill_kernel(Geom g, Seqs sq, PrefillArgs a) {
           }
         }
     }
+    __builtin_amdgcn_s_setprio(0);
     if constexpr (Q8 || ROPE == 2 || F8) {
       if (staged) store_tile(knext, vnext);
     }
