@@ -123,7 +123,7 @@ struct Seqs {
 void finish_seqs(Seqs& q, int32_t batch);
 
 // Sequence of active slot i (i work-group uniform).
-__device__ __forceinline__ int active_seq(const Seqs& q, int i) { return q.act[i]; }
+__host__ __device__ __forceinline__ int active_seq(const Seqs& q, int i) { return q.act[i]; }
 
 // Prefill work over sequences of different lengths, dealt to the 8 XCDs of
 // an MI355X (work-group i runs on XCD i mod 8).  Units u = 0 .. units-1
@@ -142,8 +142,8 @@ __host__ __device__ __forceinline__ int snake_unit(int j, int x) {
 int64_t snake_deal_items(const Seqs& q, int units_per_seq, int tq);
 // Work item `id` of the deal: query tile t of unit u; false past the end of
 // its XCD's units.
-__device__ __forceinline__ bool snake_deal_item(const Seqs& sq, int id, int units, int units_per_seq, int tq, int& t,
-                                                int& u) {
+__host__ __device__ __forceinline__ bool snake_deal_item(const Seqs& sq, int id, int units, int units_per_seq, int tq,
+                                                         int& t, int& u) {
   const int x = id % kPrefillXcds;
   int k = id / kPrefillXcds;
   for (int j = 0;; ++j) {
