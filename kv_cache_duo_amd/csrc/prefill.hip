@@ -7,8 +7,11 @@
 //   retrieval: keys 0..p;   streaming: keys j <= p with j < sink or j > p-recent.
 // Earlier positions come from the cache (retrieval rows, or the sink / ring
 // slots of streaming heads), positions of this chunk from the inputs, so a
-// sequence may be prefilled in chunks.  The append of the chunk runs after
-// this kernel (streaming ring slots read here may be overwritten by it).
+// sequence may be prefilled in chunks.  The streaming heads' rows of the
+// chunk are appended after this kernel (ring slots read here may be
+// overwritten by it); the retrieval rows of a bf16 or fp8 cache, and of any
+// cache with rotary embedding, are stored before it, and the retrieval tiles
+// then read every row from the cache (contiguous rows of one head).
 //
 // Tile engine (flash-style online softmax, fp32 accumulation):
 //   * work-group = 4 waves; each wave owns 32 query rows of one query head;
@@ -35,13 +38,17 @@
 //     exceeds it by more than 2^8; the result is exact because l and O always
 //     share the same reference;
 //   * l sums the bf16 P that the MFMA consumes (v_dot2 with ones);
-//   * work-groups run longest query tile first, t-major and unit-minor.
+//   * work-groups run longest query tile first; on each XCD one unit (head
+//     group of one sequence) at a time where the work allows it (see the
+//     work-item mapping), so the resident work-groups share its K/V in L2;
+//   * the wave priority is raised over the matrix-core blocks and lowered
+//     for the softmax.
 // With rotary position embedding (RoFormer, cited in the pith.science review
 // page's reference list) q is turned to its position in the prologue; the
 // chunk's retrieval rows are stored (rotated) before this kernel, so every
-// retrieval key comes from the cache; streaming tiles holding chunk rows are
-// staged through registers and their chunk K rows turned before the LDS
-// write.
+// retrieval key comes from the cache; the streaming heads' chunk K rows come
+// turned from the call's staging workspace, or are staged through registers
+// and turned in the tiles that hold them.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
