@@ -285,8 +285,9 @@ duo_status duo_cache_release(duo_cache* h, int32_t b, void* stream);
  * (older ones would be overwritten at once).  Lengths advance by n_new.
  * n_new: HOST int32 [B], each in [0, chunk].
  * Errors: INVALID_ARG (null handle/k/v/n_new, misaligned, chunk < 1,
- * n_new out of range), CAPACITY (len_b + n_new[b] > max_len, or a paged
- * cache without enough free pages), HIP. */
+ * n_new out of range), UNSUPPORTED (B * chunk > 2^31 - 1 input rows),
+ * CAPACITY (len_b + n_new[b] > max_len, or a paged cache without enough
+ * free pages), HIP. */
 duo_status duo_cache_append(duo_cache* h, const void* k, const void* v,
                             const int32_t* n_new, int32_t chunk, void* stream);
 

@@ -296,6 +296,7 @@ namespace {
 duo_status check_chunk(const duo_cache* h, const int32_t* n_new, int32_t chunk, duo::Seqs* sq, int32_t* max_n) {
   if (chunk < 1) return DUO_ERR_INVALID_ARG;
   if (n_new == nullptr) return DUO_ERR_INVALID_ARG;
+  if ((int64_t)h->cfg.batch * chunk > INT32_MAX) return DUO_ERR_UNSUPPORTED;  // row offsets b * chunk are int32
   int32_t mx = 0;
   for (int b = 0; b < h->cfg.batch; ++b) {
     if (n_new[b] < 0 || n_new[b] > chunk) return DUO_ERR_INVALID_ARG;

@@ -264,6 +264,10 @@ def test_call_validation_leaves_state_unchanged():
     assert lib.duo_prefill(h, A, A, A, n_ok, 0, A, None) == duo.DUO_ERR_INVALID_ARG
     assert lib.duo_prefill(h, A, A, A, (ctypes.c_int32 * 2)(5, 1), 4, A, None) == duo.DUO_ERR_INVALID_ARG
     assert lib.duo_cache_append(h, A, A, (ctypes.c_int32 * 2)(-1, 0), 4, None) == duo.DUO_ERR_INVALID_ARG
+    # row offsets b * chunk are int32: B * chunk past 2^31 - 1 is refused before any work
+    big = 2**30 + 1
+    assert lib.duo_cache_append(h, A, A, n_ok, big, None) == duo.DUO_ERR_UNSUPPORTED
+    assert lib.duo_prefill(h, A, A, A, n_ok, big, A, None) == duo.DUO_ERR_UNSUPPORTED
     # capacity: sequence 1 holds 990 of 1000 tokens
     assert lib.duo_prefill(h, A, A, A, (ctypes.c_int32 * 2)(0, 11), 16, A, None) == duo.DUO_ERR_CAPACITY
     assert lib.duo_cache_append(h, A, A, (ctypes.c_int32 * 2)(0, 11), 16, None) == duo.DUO_ERR_CAPACITY
