@@ -94,7 +94,7 @@ def measured_ceilings(decode_mib: int, extra_mib=()):
     out = {}
     sizes = [decode_mib] + [m for m in extra_mib if m != decode_mib]
     for args in ([["stream_read_rotating", str(m), "8"] for m in sizes] +
-                 [["stream_read", "4096"], ["mfma"], ["mfma_random"], ["mfma_fp8_random"]]):
+                 [["stream_read", "4096"], ["mfma"], ["mfma_random"], ["mfma_fp8_random"], ["lds_read"]]):
         r = subprocess.run([exe, *args], capture_output=True, text=True, timeout=120)
         if r.returncode != 0:
             raise RuntimeError(f"{exe} {' '.join(args)} failed: {r.stderr}")

@@ -9,6 +9,9 @@
 //   ceiling mfma_random        -- the same with changing pseudo-random operands
 //   ceiling mfma_fp8_random    -- v_mfma_scale_f32_32x32x64_f8f6f4 (e4m3, unit
 //                                 scales) with changing pseudo-random operands
+//   ceiling lds_read           -- conflict-free 16-byte LDS reads (ds_read_b128),
+//                                 8 in flight per wave, 8 work-groups per CU;
+//                                 bytes per CU per shader clock
 // Standalone executable (not part of the C ABI); prints one JSON line.
 #include <hip/hip_runtime.h>
 
@@ -241,6 +244,36 @@ int run_stream_read_rotating(size_t mib, int nbuf) {
   return 0;
 }
 
+// Each wave reads 1 KB rows of a 16 KB LDS buffer (64 lanes x 16 contiguous
+// bytes: no bank conflicts), 8 reads per round. The row offset passes through
+// an empty asm statement every round, so the compiler can neither hoist nor
+// merge the reads. Block 0 stamps the shader clock and the 100 MHz real-time
+// counter around its loop: their ratio is the clock the reads ran at. (Its
+// own loop ends early -- the oldest waves of a CU are served first -- so the
+// rate itself comes from the launch's event time.)
+__global__ __launch_bounds__(256) void lds_read(unsigned* out, int iters) {
+  __shared__ u32x4 buf[1024];
+  for (unsigned i = threadIdx.x; i < 1024; i += 256) buf[i] = u32x4{i, 3 * i + 1, 5 * i + 2, 7 * i + 3};
+  __syncthreads();
+  const unsigned lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned off = wave * 256 + lane;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  const unsigned long long t0 = __builtin_readcyclecounter();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc ^= buf[(off + 128 * j) & 1023];
+    asm volatile("" : "+v"(off));
+  }
+  const unsigned long long t1 = __builtin_readcyclecounter();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  if ((acc.x ^ acc.y ^ acc.z ^ acc.w) == 0x9e3779b9u) out[4 + blockIdx.x] = acc.x;
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    out[0] = (unsigned)(t1 - t0);
+    out[1] = (unsigned)(r1 - r0);
+  }
+}
+
 // mode 0: bf16 constant operands, 1: bf16 random operands, 2: fp8 random
 int run_mfma(int mode) {
   int dev = 0, cus = 0;
@@ -270,6 +303,36 @@ int run_mfma(int mode) {
   return 0;
 }
 
+// LDS read rate: bytes per CU per shader clock, and in TB/s over the chip.
+int run_lds_read() {
+  int dev = 0, cus = 0;
+  if (!ok(hipGetDevice(&dev), "device") ||
+      !ok(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev), "attr"))
+    return 1;
+  const unsigned blocks = (unsigned)cus * 8;  // 8 work-groups of 4 waves per CU, all resident
+  const int iters = 1 << 14;
+  unsigned* out = nullptr;
+  if (!ok(hipMalloc(&out, (4 + blocks) * sizeof(unsigned)), "hipMalloc")) return 1;
+  hipEvent_t a, b;
+  if (!ok(hipEventCreate(&a), "event") || !ok(hipEventCreate(&b), "event")) return 1;
+  hipLaunchKernelGGL(lds_read, dim3(blocks), dim3(256), 0, 0, out, iters);
+  (void)hipEventRecord(a, 0);
+  hipLaunchKernelGGL(lds_read, dim3(blocks), dim3(256), 0, 0, out, iters);
+  (void)hipEventRecord(b, 0);
+  if (!ok(hipEventSynchronize(b), "sync")) return 1;
+  float ms = 0.f;
+  (void)hipEventElapsedTime(&ms, a, b);
+  unsigned stamps[2] = {0, 0};
+  if (!ok(hipMemcpy(stamps, out, sizeof(stamps), hipMemcpyDeviceToHost), "copy")) return 1;
+  const double bytes_per_cu = 8.0 * 256 * iters * 8 * 16;  // per CU: 8 blocks x 256 lanes x reads x 16 B
+  const double clock_ghz = stamps[1] ? (double)stamps[0] / stamps[1] * 0.1 : 0.0;  // real-time counter: 100 MHz
+  const double seconds = ms * 1e-3;
+  printf("{\"ceiling\": \"lds_read_b128\", \"cus\": %d, \"bytes_per_cu_per_clock\": %.1f, \"clock_ghz\": %.3f, "
+         "\"tbs\": %.1f}\n", cus, clock_ghz > 0 ? bytes_per_cu / (seconds * clock_ghz * 1e9) : 0.0, clock_ghz,
+         bytes_per_cu * cus / seconds / 1e12);
+  return 0;
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -281,8 +344,9 @@ int main(int argc, char** argv) {
   if (argc >= 2 && std::strcmp(argv[1], "mfma") == 0) return run_mfma(0);
   if (argc >= 2 && std::strcmp(argv[1], "mfma_random") == 0) return run_mfma(1);
   if (argc >= 2 && std::strcmp(argv[1], "mfma_fp8_random") == 0) return run_mfma(2);
+  if (argc >= 2 && std::strcmp(argv[1], "lds_read") == 0) return run_lds_read();
   fprintf(stderr, "usage: ceiling stream_read <MiB> | ceiling stream_read_rotating <MiB> <buffers> | ceiling copy <MiB>"
                   " | ceiling mfma"
-                  " | ceiling mfma_random | ceiling mfma_fp8_random\n");
+                  " | ceiling mfma_random | ceiling mfma_fp8_random | ceiling lds_read\n");
   return 2;
 }
